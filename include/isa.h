@@ -1,0 +1,202 @@
+/*
+ * isa.h -- C ABI of the IndexPool sparse-attention path for AMD Instinct MI355X
+ * (gfx950): IndexPool -> 32-head lightning indexer with top-512-group selection
+ * -> NoPE MLA softmax attention over the selected latent rows.
+ *
+ * Sources (web pages; cited by title and section):
+ *  [WIKI]  "GLM-5.3-Flash: 하이브리드 희소·선형 어텐션과 IndexPool·EPD로 1M 컨텍스트를
+ *          오픈 소스로 서빙하는 방법" (llm-wiki.hwlabs.dev): sections "희소 어텐션:
+ *          인덱서로 필요한 토큰만" (an indexer keeps one key per position and picks
+ *          the positions softmax attention runs over), "IndexPool: 인덱서 KV 캐시를
+ *          4배 압축" (pooling equation k_pool = sum_i w_i k_i over 4 consecutive
+ *          keys, weights summing to 1, learned; a quarter of the storage), "양자화:
+ *          W8A8와 혼합 캐시" (the distant compressed cache is INT8).
+ *  [REMIO] "GLM-5.3 Sparse Attention은 연산량을 줄이지만 HBM 수요는 지속된다"
+ *          (remio.ai), section "GLM-5.3 Sparse Attention이 실제로 바꾸는 것": the
+ *          indexer scores earlier positions and keeps the top-k (2048); MLA
+ *          attends over compressed latent rows; below 2048 positions attention
+ *          stays dense; the indexer still has to see the whole history.
+ *  [TREND] "GLM-5.3-Flash vs Qwen3.8-Flash-Next: 두 중국 AI 연구소가 독립적으로 같은
+ *          모델 설계로 수렴한 이유" (alltoptrend.co.kr): section "수렴점 2 — 4배 압축
+ *          후 2,048 토큰만 유지" (32-head lightning indexer, pooling before scoring,
+ *          4-token blocks x top 512 = 2048 tokens) and section "의견이 갈리는 지점 —
+ *          위치 인코딩" (qk_rope_head_dim = 0: NoPE).
+ * The pages give no score formula, dtypes, tie rule or interface; the choices
+ * made here are stated at each declaration.
+ *
+ * Conventions for every call
+ *  - Fixed dimensions: indexer keys 128-d, 32 indexer heads, groups of 4 tokens,
+ *    64 attention heads over a 512-d latent, k <= 512 groups.
+ *  - Memory is owned by the caller.  Pointers marked [dev] are device pointers,
+ *    [host] are host pointers read during the call only.  All [dev] pointers
+ *    must be 16-byte aligned.  Tensors are dense row-major.
+ *  - Paging: a page holds 256 tokens of indexer keys ([256,128] bf16, 64 KiB) or
+ *    of latent rows ([256,512] bf16, 256 KiB), which is 64 pooled groups
+ *    ([64,128] int8, 8 KiB).  Logical page j of a sequence is tokens
+ *    256j..256j+255 = groups 64j..64j+63; one block table maps it to the same
+ *    physical page id in the key, latent and pooled pools.
+ *  - Work is enqueued on `stream`; no call synchronises or reads device memory
+ *    on the host.  Outputs are valid once the stream reaches the call.
+ *  - Workspace: `ws` [dev] of at least isa_workspace_size(...) bytes, zero-
+ *    filled once before its first use (isa_workspace_init or any zero fill).
+ *    Calls keep the parts they use zeroed between calls.  Calls that share a
+ *    workspace must be ordered on one stream.
+ *  - Errors: argument errors are reported synchronously by the return code
+ *    before anything is enqueued.  Errors that depend on device data (a page
+ *    id outside the pool, a head weight outside [0,64], a score above
+ *    INT32_MAX, a row position outside its sequence) set bits in the sticky
+ *    error word at the start of the workspace; read it with isa_device_error.
+ *    Nothing aborts or throws across this boundary.
+ */
+#ifndef ISA_H
+#define ISA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* isa_stream_t; /* a hipStream_t (0 = the null stream) */
+
+typedef enum {
+  ISA_OK = 0,
+  ISA_ERR_INVALID_ARG = 1,  /* NULL / misaligned pointer, bad size, bad flag */
+  ISA_ERR_UNSUPPORTED = 2,  /* a size beyond what the library supports */
+  ISA_ERR_WORKSPACE = 3,    /* workspace smaller than isa_workspace_size() */
+  ISA_ERR_HIP = 4           /* the HIP runtime rejected a launch */
+} isa_status;
+
+/* bits of the device error word */
+#define ISA_DERR_PAGE_OOB 0x1u       /* block-table entry outside [0, num_pages) */
+#define ISA_DERR_HEADW_RANGE 0x2u    /* indexer head weight outside [0, 64] */
+#define ISA_DERR_SCORE_OVERFLOW 0x4u /* an indexer score above INT32_MAX */
+#define ISA_DERR_ROW_RANGE 0x8u      /* row sequence / position or a group id outside its sequence */
+#define ISA_DERR_NONFINITE 0x10u     /* non-finite pooled amax (NaN / Inf indexer keys) */
+
+#define ISA_MAX_BATCH 256          /* sequences per call */
+#define ISA_MAX_SEQ_LEN (1 << 22)  /* tokens per sequence */
+#define ISA_MAX_K 512              /* groups selected per row */
+
+/* One batch of sequences that share page pools. */
+typedef struct {
+  int32_t batch;                /* B, 1..ISA_MAX_BATCH */
+  int32_t max_pages;            /* columns of block_table; >= ceil(L_b/256) for every b */
+  int32_t num_pages;            /* physical pages in each pool (bounds for block_table) */
+  int32_t reserved;             /* must be 0 */
+  const int32_t* seq_lens_host; /* [host] [B] tokens per sequence, 1..ISA_MAX_SEQ_LEN */
+  const int32_t* block_table;   /* [dev]  [B, max_pages] physical page ids */
+} isa_seqs;
+
+enum { ISA_OP_INDEXPOOL = 1, ISA_OP_INDEXER_TOPK = 2, ISA_OP_SPARSE_MLA = 3, ISA_OP_PREFILL_SCORES = 4 };
+
+/* Workspace bytes (a multiple of 256) that `op` needs for these sequences.
+ * rows: query rows (attention and top-k from precomputed scores; ignored
+ * otherwise); cols: score columns per row for top-k from precomputed scores.
+ * Returns 0 for invalid arguments. */
+size_t isa_workspace_size(int op, const isa_seqs* s, int32_t rows, int32_t cols);
+
+/* Zero-fill a workspace on `stream` (needed once, before its first use). */
+isa_status isa_workspace_init(void* ws, size_t ws_bytes, isa_stream_t stream);
+
+/* Copy the sticky device error word to *err_word [host] (synchronises
+ * `stream`), and clear it when `clear` is nonzero. */
+isa_status isa_device_error(void* ws, isa_stream_t stream, uint32_t* err_word, int clear);
+
+const char* isa_status_string(isa_status status);
+const char* isa_version(void);
+
+#define ISA_SCALE_DYNAMIC 0u /* scales[b] := max|pooled| / 127 of sequence b (1 if all zero) */
+#define ISA_SCALE_GIVEN 1u   /* use scales[b] as given (> 0), single pass, clamp to +-127 */
+
+/*
+ * (1) IndexPool + int8 quantisation of the indexer key cache ([WIKI] IndexPool
+ * and quantisation sections; [TREND] convergence 2: pooling precedes scoring).
+ *   keys    [dev] bf16 bits [num_pages, 256, 128], token-paged
+ *   w4      [host] the 4 learned pooling weights (fp32, sum 1), shared by all
+ *           groups and channels
+ *   s       sequences and block table
+ *   scales  [dev] fp32 [B]: written (DYNAMIC) or read (GIVEN)
+ *   pooled  [dev] int8 [num_pages, 64, 128], group-paged; group g of sequence b is
+ *           row g%64 of page block_table[b][g/64]
+ * Group g pools tokens 4g..4g+3: sum_i w_i k_{4g+i} in fp32.  A last group of
+ * r < 4 tokens uses w_0..w_{r-1} divided by their sum.  The pooled value x is
+ * stored as clamp(round_half_even(x / scale), -127, 127).  Rows of a sequence's
+ * last page beyond its last group are left untouched.
+ */
+isa_status isa_indexpool(const uint16_t* keys, const float* w4, const isa_seqs* s, float* scales,
+                         int8_t* pooled, uint32_t flags, void* ws, size_t ws_bytes, isa_stream_t stream);
+
+/*
+ * (2) Lightning-indexer scoring and top-k group selection ([REMIO] section on
+ * what sparse attention changes: score earlier positions, keep the top-k,
+ * dense below the budget; [TREND] convergence 2: 32 heads, 512 groups of 4).
+ *
+ * Decode mode (scores_in == NULL): one row per sequence, rows == s->batch.
+ *   q       [dev] int8 [B, 32, 128] indexer query of each sequence
+ *   head_w  [dev] int8 [B, 32] head weights, each in [0, 64]
+ *   pooled  [dev] int8 [num_pages, 64, 128] (from isa_indexpool)
+ *   score of group g:  S = sum_h head_w[h] * max(0, sum_d q[h][d] * pooled[g][d]),
+ *   exact integer arithmetic; every group 0..ceil(L_b/4)-1 is a candidate.
+ *   scores_out [dev] optional int32 [B, ld_scores] (ld_scores >= max_b ceil(L_b/4)):
+ *           the scores of every group, for checking; NULL to skip.
+ * Precomputed mode (scores_in != NULL, e.g. from isa_indexer_prefill_scores):
+ *   scores_in [dev] int32 [rows, ld_scores]; entry < 0 means "not a candidate";
+ *   q, head_w, pooled, scores_out are ignored and s may be NULL.
+ *
+ * Selection (both modes): the candidates of a row are ranked by higher score,
+ * then lower group id; the first k are selected, or all candidates when there
+ * are at most k (the dense fallback: fewer than 4k = 2048 tokens).
+ *   out_idx   [dev] int32 [rows, k]: selected group ids in ascending order, then -1
+ *   out_count [dev] int32 [rows]: number selected
+ * k: 1..512 (512 = 2048 tokens).
+ */
+isa_status isa_indexer_topk(const int8_t* q, const int8_t* head_w, const int8_t* pooled, const isa_seqs* s,
+                            const int32_t* scores_in, int32_t rows, int32_t ld_scores, int32_t k,
+                            int32_t* out_idx, int32_t* out_count, int32_t* scores_out, void* ws,
+                            size_t ws_bytes, isa_stream_t stream);
+
+/*
+ * (3) Sparse MLA attention over the selected groups ([WIKI] sparse attention
+ * section: softmax only over the selected positions; [REMIO]: MLA keeps one
+ * compressed latent per token; [TREND] positional encoding section: NoPE).
+ * Absorbed form: keys = values = the 512-d latent row; no rotary part.
+ *   q        [dev] bf16 bits [rows, 64, 512]
+ *   latent   [dev] bf16 bits [num_pages, 256, 512], token-paged; values must be
+ *            finite with magnitude below 65504
+ *   row_seq  [dev] int32 [rows] sequence of each row, or NULL: row r is sequence r
+ *   row_pos  [dev] int32 [rows] last visible token, or NULL: L_seq - 1
+ *   idx, count [dev] from isa_indexer_topk ([rows, k], [rows])
+ *   sm_scale softmax scale (1/sqrt(512) for this model)
+ *   out      [dev] fp32 [rows, 64, 512]: softmax(q_h . c_t * sm_scale) weighted sum of
+ *            c_t over tokens t of the selected groups with t <= pos and t < L
+ *   lse      [dev] fp32 [rows, 64] natural log-sum-exp of the scaled scores, or NULL
+ * A row with no visible token gets out = 0 and lse = -inf.
+ * Arithmetic: bf16 products with fp32 accumulation for q.c; fp32 softmax;
+ * probabilities rounded to fp16 and latents converted exactly to fp16 for the
+ * weighted sum, fp32 accumulation.
+ */
+isa_status isa_sparse_mla_decode(const uint16_t* q, const uint16_t* latent, const isa_seqs* s,
+                                 const int32_t* row_seq, const int32_t* row_pos, int32_t rows,
+                                 const int32_t* idx, const int32_t* count, int32_t k, float sm_scale,
+                                 float* out, float* lse, void* ws, size_t ws_bytes, isa_stream_t stream);
+
+/*
+ * (4) Prefill indexer scores of Q queries of one sequence (s->batch == 1)
+ * against all its pooled groups -- a dense int8 contraction ([REMIO]: the
+ * indexer scores the whole retained history).
+ *   q       [dev] int8 [Q, 32, 128]; head_w [dev] int8 [Q, 32] in [0, 64]
+ *   q_pos   [dev] int32 [Q] absolute token position of each query, < L
+ *   scores  [dev] int32 [Q, ld_scores], ld_scores >= ceil(L/4): the decode score
+ *           formula for groups g <= q_pos/4 (the query's own group included) and
+ *           -1 for later groups; columns >= ceil(L/4) are left untouched.
+ */
+isa_status isa_indexer_prefill_scores(const int8_t* q, const int8_t* head_w, const int32_t* q_pos, int32_t Q,
+                                      const int8_t* pooled, const isa_seqs* s, int32_t* scores,
+                                      int32_t ld_scores, void* ws, size_t ws_bytes, isa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ISA_H */

@@ -1,0 +1,183 @@
+"""IndexPool sparse attention on AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libisa.so`` (the HIP kernels and the C ABI of
+``include/isa.h``).  Functions keep the C names; they only marshal torch tensors
+(device memory and streams) into pointers, sizes and the caller's HIP stream.
+Every step of the path runs in the library's kernels; there is no fallback: if
+the library is not built, importing the binding raises.
+
+Build the library with ``python -m long_context_sparse_indexpool_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libisa.so")
+
+IDX_DIM, IDX_HEADS, GROUP, ATT_HEADS, LAT_DIM = 128, 32, 4, 64, 512
+PAGE_TOKENS, PAGE_GROUPS = 256, 64
+MAX_BATCH, MAX_SEQ_LEN, MAX_K = 256, 1 << 22, 512
+
+ISA_OK, ISA_ERR_INVALID_ARG, ISA_ERR_UNSUPPORTED, ISA_ERR_WORKSPACE, ISA_ERR_HIP = range(5)
+ISA_OP_INDEXPOOL, ISA_OP_INDEXER_TOPK, ISA_OP_SPARSE_MLA, ISA_OP_PREFILL_SCORES = 1, 2, 3, 4
+ISA_SCALE_DYNAMIC, ISA_SCALE_GIVEN = 0, 1
+DERR_PAGE_OOB, DERR_HEADW_RANGE, DERR_SCORE_OVERFLOW, DERR_ROW_RANGE, DERR_NONFINITE = 1, 2, 4, 8, 16
+
+EXPORTS = ("isa_workspace_size", "isa_workspace_init", "isa_device_error", "isa_status_string", "isa_version",
+           "isa_indexpool", "isa_indexer_topk", "isa_sparse_mla_decode", "isa_indexer_prefill_scores")
+
+
+class IsaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class isa_seqs(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("seq_lens_host", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run: python -m long_context_sparse_indexpool_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_uint32
+    sp = ctypes.POINTER(isa_seqs)
+    lib.isa_workspace_size.argtypes = [ctypes.c_int, sp, i32, i32]
+    lib.isa_workspace_size.restype = sz
+    lib.isa_workspace_init.argtypes = [vp, sz, vp]
+    lib.isa_device_error.argtypes = [vp, vp, ctypes.POINTER(u32), ctypes.c_int]
+    lib.isa_status_string.argtypes = [ctypes.c_int]
+    lib.isa_status_string.restype = ctypes.c_char_p
+    lib.isa_version.restype = ctypes.c_char_p
+    lib.isa_indexpool.argtypes = [vp, vp, sp, vp, vp, u32, vp, sz, vp]
+    lib.isa_indexer_topk.argtypes = [vp, vp, vp, sp, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.isa_sparse_mla_decode.argtypes = [vp, vp, sp, vp, vp, i32, vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp]
+    lib.isa_indexer_prefill_scores.argtypes = [vp, vp, vp, i32, vp, sp, vp, i32, vp, sz, vp]
+    for f in ("isa_workspace_init", "isa_device_error", "isa_indexpool", "isa_indexer_topk",
+              "isa_sparse_mla_decode", "isa_indexer_prefill_scores"):
+        getattr(lib, f).restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.isa_status_string(status).decode()
+
+
+def version() -> str:
+    return lib.isa_version().decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != ISA_OK:
+        raise IsaError(fn, status)
+
+
+def _stream(stream: Optional[torch.cuda.Stream]) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor], dtype: torch.dtype, name: str) -> Optional[int]:
+    if t is None:
+        return None
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    return t.data_ptr()
+
+
+@dataclass
+class Seqs:
+    """A batch of sequences sharing page pools (marshalled into ``isa_seqs``)."""
+    lens: Sequence[int]
+    block_table: torch.Tensor  # int32 [B, max_pages] on the device
+    num_pages: int
+
+    def __post_init__(self):
+        self._lens = (ctypes.c_int32 * len(self.lens))(*[int(x) for x in self.lens])
+        bt = self.block_table
+        self._c = isa_seqs(len(self.lens), bt.shape[1] if bt.dim() == 2 else 0, int(self.num_pages), 0,
+                           ctypes.cast(self._lens, ctypes.c_void_p), _ptr(bt, torch.int32, "block_table"))
+
+    @property
+    def c(self) -> ctypes.POINTER(isa_seqs):
+        return ctypes.byref(self._c)
+
+
+def workspace_size(op: int, seqs: Optional[Seqs], rows: int = 0, cols: int = 0) -> int:
+    return int(lib.isa_workspace_size(op, seqs.c if seqs is not None else None, rows, cols))
+
+
+def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace (zero fill is the only initialisation the library needs)."""
+    return torch.zeros(max(256, (nbytes + 255) // 256 * 256), dtype=torch.uint8, device=device)
+
+
+def isa_workspace_init(ws: torch.Tensor, stream=None) -> None:
+    _check("isa_workspace_init", lib.isa_workspace_init(_ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
+
+
+def isa_device_error(ws: torch.Tensor, clear: bool = False, stream=None) -> int:
+    word = ctypes.c_uint32(0)
+    _check("isa_device_error", lib.isa_device_error(_ptr(ws, torch.uint8, "ws"), _stream(stream),
+                                                    ctypes.byref(word), int(clear)))
+    return int(word.value)
+
+
+def isa_indexpool(keys: torch.Tensor, w4: Sequence[float], seqs: Seqs, scales: torch.Tensor,
+                  pooled: torch.Tensor, flags: int, ws: torch.Tensor, stream=None) -> None:
+    """IndexPool + int8 quantisation.  keys: bf16 bits (int16/uint16 view) [pages,256,128];
+    pooled: int8 [pages,64,128]; scales: fp32 [B]."""
+    w = (ctypes.c_float * 4)(*[float(x) for x in w4])
+    k = keys if keys.dtype == torch.int16 else keys.view(torch.int16)
+    _check("isa_indexpool", lib.isa_indexpool(_ptr(k, torch.int16, "keys"), ctypes.cast(w, ctypes.c_void_p), seqs.c,
+                                              _ptr(scales, torch.float32, "scales"), _ptr(pooled, torch.int8, "pooled"),
+                                              flags, _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
+
+
+def isa_indexer_topk(q: Optional[torch.Tensor], head_w: Optional[torch.Tensor], pooled: Optional[torch.Tensor],
+                     seqs: Optional[Seqs], scores_in: Optional[torch.Tensor], rows: int, ld_scores: int, k: int,
+                     out_idx: torch.Tensor, out_count: torch.Tensor, scores_out: Optional[torch.Tensor],
+                     ws: torch.Tensor, stream=None) -> None:
+    _check("isa_indexer_topk", lib.isa_indexer_topk(
+        _ptr(q, torch.int8, "q"), _ptr(head_w, torch.int8, "head_w"), _ptr(pooled, torch.int8, "pooled"),
+        seqs.c if seqs is not None else None, _ptr(scores_in, torch.int32, "scores_in"), rows, ld_scores, k,
+        _ptr(out_idx, torch.int32, "out_idx"), _ptr(out_count, torch.int32, "out_count"),
+        _ptr(scores_out, torch.int32, "scores_out"), _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
+
+
+def isa_sparse_mla_decode(q: torch.Tensor, latent: torch.Tensor, seqs: Seqs, row_seq: Optional[torch.Tensor],
+                          row_pos: Optional[torch.Tensor], rows: int, idx: torch.Tensor, count: torch.Tensor, k: int,
+                          sm_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor], ws: torch.Tensor,
+                          stream=None) -> None:
+    qq = q if q.dtype == torch.int16 else q.view(torch.int16)
+    lat = latent if latent.dtype == torch.int16 else latent.view(torch.int16)
+    _check("isa_sparse_mla_decode", lib.isa_sparse_mla_decode(
+        _ptr(qq, torch.int16, "q"), _ptr(lat, torch.int16, "latent"), seqs.c, _ptr(row_seq, torch.int32, "row_seq"),
+        _ptr(row_pos, torch.int32, "row_pos"), rows, _ptr(idx, torch.int32, "idx"),
+        _ptr(count, torch.int32, "count"), k, float(sm_scale), _ptr(out, torch.float32, "out"),
+        _ptr(lse, torch.float32, "lse"), _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
+
+
+def isa_indexer_prefill_scores(q: torch.Tensor, head_w: torch.Tensor, q_pos: torch.Tensor, Q: int,
+                               pooled: torch.Tensor, seqs: Seqs, scores: torch.Tensor, ld_scores: int,
+                               ws: torch.Tensor, stream=None) -> None:
+    _check("isa_indexer_prefill_scores", lib.isa_indexer_prefill_scores(
+        _ptr(q, torch.int8, "q"), _ptr(head_w, torch.int8, "head_w"), _ptr(q_pos, torch.int32, "q_pos"), Q,
+        _ptr(pooled, torch.int8, "pooled"), seqs.c, _ptr(scores, torch.int32, "scores"), ld_scores,
+        _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))

@@ -1,0 +1,238 @@
+// api.hip -- the C ABI of libisa (see include/isa.h): argument validation on
+// the host, workspace layout, work plans passed by value to the kernels, and
+// launches on the caller's stream.  Nothing here allocates or synchronises
+// except isa_device_error, which reads the error word on request.
+#include <string.h>
+
+#include "isa_launch.hpp"
+
+namespace isa {
+namespace {
+
+constexpr size_t HDR = 256;
+
+inline size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline int64_t groups_of(int32_t L) { return ((int64_t)L + GROUP - 1) / GROUP; }
+
+// Host validation of a batch description.
+bool valid_seqs(const isa_seqs* s) {
+  if (!s || s->batch < 1 || s->batch > ISA_MAX_BATCH || s->max_pages < 1 || s->num_pages < 1 || s->reserved != 0 ||
+      !s->seq_lens_host || !s->block_table || !aligned16(s->block_table))
+    return false;
+  for (int b = 0; b < s->batch; ++b) {
+    int32_t L = s->seq_lens_host[b];
+    if (L < 1 || L > ISA_MAX_SEQ_LEN) return false;
+    if ((L + PAGE_TOK - 1) / PAGE_TOK > s->max_pages) return false;
+  }
+  return true;
+}
+
+void fill_batch(const isa_seqs* s, BatchArgs* a, int32_t k) {
+  memset(a, 0, sizeof(*a));
+  a->batch = s->batch;
+  a->max_pages = s->max_pages;
+  a->num_pages = s->num_pages;
+  a->k = k;
+  for (int b = 0; b < s->batch; ++b) a->lens[b] = s->seq_lens_host[b];
+}
+
+int decode_tiles(int32_t L, int32_t k) {
+  int64_t G = groups_of(L);
+  return G <= k ? 1 : (int)((G + TILE_G - 1) / TILE_G);
+}
+
+int pool_tiles(int32_t L) { return (int)((groups_of(L) + POOL_TILE_G - 1) / POOL_TILE_G); }
+
+struct DecodeLayout {
+  size_t ghist, tickets, tile_cnt, tile_list, total;
+};
+DecodeLayout decode_layout(const isa_seqs* s, int32_t k) {
+  DecodeLayout d;
+  int nt = 0;
+  for (int b = 0; b < s->batch; ++b) nt += decode_tiles(s->seq_lens_host[b], k);
+  d.ghist = HDR;
+  d.tickets = d.ghist + up256((size_t)s->batch * NBINS * 4);
+  d.tile_cnt = d.tickets + up256((size_t)s->batch * 4);
+  d.tile_list = d.tile_cnt + up256((size_t)nt * 4);
+  d.total = d.tile_list + up256((size_t)nt * TILE_G * 8);
+  return d;
+}
+
+size_t pool_ws(const isa_seqs* s) {
+  int nt = 0;
+  for (int b = 0; b < s->batch; ++b) nt += pool_tiles(s->seq_lens_host[b]);
+  return HDR + up256((size_t)nt * 4 + (size_t)s->batch * 4);
+}
+
+size_t mla_ws(int32_t rows, int32_t k) {
+  MlaPlan p = plan_mla(rows, k);
+  if (p.splits <= 1) return HDR;
+  return HDR + up256((size_t)rows * p.splits * ATT_HEADS * LAT_DIM * 4) +
+         up256((size_t)rows * p.splits * ATT_HEADS * 2 * 4);
+}
+
+__global__ void k_fill_zero(uint4* p, size_t n16) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (; i < n16; i += stride) p[i] = make_uint4(0, 0, 0, 0);
+}
+
+}  // namespace
+
+isa_status launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
+  size_t n16 = bytes / 16;
+  if (n16 == 0) return ISA_OK;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, stream, (uint4*)p, n16);
+  return hipGetLastError() == hipSuccess ? ISA_OK : ISA_ERR_HIP;
+}
+
+}  // namespace isa
+
+using namespace isa;
+
+extern "C" {
+
+const char* isa_version(void) { return "isa 0.1 (gfx950)"; }
+
+const char* isa_status_string(isa_status st) {
+  switch (st) {
+    case ISA_OK: return "ok";
+    case ISA_ERR_INVALID_ARG: return "invalid argument";
+    case ISA_ERR_UNSUPPORTED: return "unsupported size";
+    case ISA_ERR_WORKSPACE: return "workspace too small";
+    case ISA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+size_t isa_workspace_size(int op, const isa_seqs* s, int32_t rows, int32_t cols) {
+  (void)cols;
+  switch (op) {
+    case ISA_OP_INDEXPOOL:
+      return valid_seqs(s) ? pool_ws(s) : 0;
+    case ISA_OP_INDEXER_TOPK:
+      if (s == nullptr) return HDR;
+      return valid_seqs(s) ? decode_layout(s, MAX_K).total : 0;
+    case ISA_OP_SPARSE_MLA:
+      return rows >= 1 ? mla_ws(rows, MAX_K) : 0;
+    case ISA_OP_PREFILL_SCORES:
+      return HDR;
+  }
+  return 0;
+}
+
+isa_status isa_workspace_init(void* ws, size_t ws_bytes, isa_stream_t stream) {
+  if (!ws || !aligned16(ws) || ws_bytes < HDR || (ws_bytes & 15)) return ISA_ERR_INVALID_ARG;
+  return launch_fill_zero(ws, ws_bytes, (hipStream_t)stream);
+}
+
+isa_status isa_device_error(void* ws, isa_stream_t stream, uint32_t* err_word, int clear) {
+  if (!ws || !err_word) return ISA_ERR_INVALID_ARG;
+  if (hipMemcpyAsync(err_word, ws, 4, hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess) return ISA_ERR_HIP;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return ISA_ERR_HIP;
+  if (clear && *err_word) return launch_fill_zero(ws, 16, (hipStream_t)stream);
+  return ISA_OK;
+}
+
+isa_status isa_indexpool(const uint16_t* keys, const float* w4, const isa_seqs* s, float* scales, int8_t* pooled,
+                         uint32_t flags, void* ws, size_t ws_bytes, isa_stream_t stream) {
+  if (!keys || !w4 || !scales || !pooled || !ws) return ISA_ERR_INVALID_ARG;
+  if (!aligned16(keys) || !aligned16(pooled) || !aligned16(ws) || ((uintptr_t)scales & 3)) return ISA_ERR_INVALID_ARG;
+  if (flags != ISA_SCALE_DYNAMIC && flags != ISA_SCALE_GIVEN) return ISA_ERR_INVALID_ARG;
+  if (!valid_seqs(s)) return ISA_ERR_INVALID_ARG;
+  for (int i = 0; i < 4; ++i)
+    if (!(w4[i] == w4[i])) return ISA_ERR_INVALID_ARG;
+  if (ws_bytes < pool_ws(s)) return ISA_ERR_WORKSPACE;
+  BatchArgs a;
+  fill_batch(s, &a, MAX_K);
+  int t = 0;
+  for (int b = 0; b < s->batch; ++b) {
+    a.tile_start[b] = t;
+    t += pool_tiles(s->seq_lens_host[b]);
+  }
+  a.tile_start[s->batch] = t;
+  float* amax_part = reinterpret_cast<float*>((char*)ws + HDR);
+  return launch_indexpool(a, keys, w4, s->block_table, scales, pooled, flags == ISA_SCALE_DYNAMIC, amax_part,
+                          (uint32_t*)ws, (hipStream_t)stream);
+}
+
+isa_status isa_indexer_topk(const int8_t* q, const int8_t* head_w, const int8_t* pooled, const isa_seqs* s,
+                            const int32_t* scores_in, int32_t rows, int32_t ld_scores, int32_t k, int32_t* out_idx,
+                            int32_t* out_count, int32_t* scores_out, void* ws, size_t ws_bytes,
+                            isa_stream_t stream) {
+  if (k < 1 || k > MAX_K || !out_idx || !out_count || !ws) return ISA_ERR_INVALID_ARG;
+  if (!aligned16(out_idx) || !aligned16(out_count) || !aligned16(ws)) return ISA_ERR_INVALID_ARG;
+  if (scores_in) {
+    if (!aligned16(scores_in) || rows < 1 || ld_scores < 1) return ISA_ERR_INVALID_ARG;
+    if (ws_bytes < HDR) return ISA_ERR_WORKSPACE;
+    return launch_topk_rows(scores_in, rows, ld_scores, ld_scores, k, out_idx, out_count, (hipStream_t)stream);
+  }
+  if (!q || !head_w || !pooled || !aligned16(q) || !aligned16(head_w) || !aligned16(pooled))
+    return ISA_ERR_INVALID_ARG;
+  if (!valid_seqs(s) || rows != s->batch) return ISA_ERR_INVALID_ARG;
+  if (scores_out) {
+    if (!aligned16(scores_out)) return ISA_ERR_INVALID_ARG;
+    for (int b = 0; b < s->batch; ++b)
+      if (groups_of(s->seq_lens_host[b]) > ld_scores) return ISA_ERR_INVALID_ARG;
+  }
+  DecodeLayout d = decode_layout(s, k);
+  if (ws_bytes < d.total) return ISA_ERR_WORKSPACE;
+  BatchArgs a;
+  fill_batch(s, &a, k);
+  int t = 0;
+  for (int b = 0; b < s->batch; ++b) {
+    a.tile_start[b] = t;
+    t += decode_tiles(s->seq_lens_host[b], k);
+  }
+  a.tile_start[s->batch] = t;
+  char* base = (char*)ws;
+  DecodeWs w{(uint32_t*)base, (uint32_t*)(base + d.ghist), (uint32_t*)(base + d.tickets),
+             (uint32_t*)(base + d.tile_cnt), (uint64_t*)(base + d.tile_list)};
+  return launch_indexer_decode(a, q, head_w, pooled, s->block_table, w, out_idx, out_count, scores_out, ld_scores,
+                               (hipStream_t)stream);
+}
+
+isa_status isa_sparse_mla_decode(const uint16_t* q, const uint16_t* latent, const isa_seqs* s,
+                                 const int32_t* row_seq, const int32_t* row_pos, int32_t rows, const int32_t* idx,
+                                 const int32_t* count, int32_t k, float sm_scale, float* out, float* lse, void* ws,
+                                 size_t ws_bytes, isa_stream_t stream) {
+  if (!q || !latent || !idx || !count || !out || !ws) return ISA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(latent) || !aligned16(idx) || !aligned16(count) || !aligned16(out) ||
+      !aligned16(ws) || (lse && !aligned16(lse)) || (row_seq && !aligned16(row_seq)) ||
+      (row_pos && !aligned16(row_pos)))
+    return ISA_ERR_INVALID_ARG;
+  if (k < 1 || k > MAX_K || rows < 1 || !(sm_scale > 0.f) || sm_scale != sm_scale) return ISA_ERR_INVALID_ARG;
+  if (!valid_seqs(s)) return ISA_ERR_INVALID_ARG;
+  if (!row_seq && rows > s->batch) return ISA_ERR_INVALID_ARG;
+  MlaPlan p = plan_mla(rows, k);
+  if ((long long)rows * p.splits > 0x7FFFFFFF) return ISA_ERR_UNSUPPORTED;
+  if (ws_bytes < mla_ws(rows, k)) return ISA_ERR_WORKSPACE;
+  BatchArgs a;
+  fill_batch(s, &a, k);
+  char* base = (char*)ws;
+  MlaWs w{(uint32_t*)base, (float*)(base + HDR),
+          (float*)(base + HDR + up256((size_t)rows * p.splits * ATT_HEADS * LAT_DIM * 4))};
+  return launch_sparse_mla(a, p, q, latent, s->block_table, row_seq, row_pos, idx, count, k, sm_scale, out, lse, w,
+                           (hipStream_t)stream);
+}
+
+isa_status isa_indexer_prefill_scores(const int8_t* q, const int8_t* head_w, const int32_t* q_pos, int32_t Q,
+                                      const int8_t* pooled, const isa_seqs* s, int32_t* scores, int32_t ld_scores,
+                                      void* ws, size_t ws_bytes, isa_stream_t stream) {
+  if (!q || !head_w || !q_pos || !pooled || !scores || !ws) return ISA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(head_w) || !aligned16(q_pos) || !aligned16(pooled) || !aligned16(scores) ||
+      !aligned16(ws))
+    return ISA_ERR_INVALID_ARG;
+  if (Q < 1 || !valid_seqs(s) || s->batch != 1) return ISA_ERR_INVALID_ARG;
+  if (groups_of(s->seq_lens_host[0]) > ld_scores) return ISA_ERR_INVALID_ARG;
+  if (ws_bytes < HDR) return ISA_ERR_WORKSPACE;
+  BatchArgs a;
+  fill_batch(s, &a, MAX_K);
+  return launch_prefill_scores(a, q, head_w, q_pos, Q, pooled, s->block_table, scores, ld_scores, (uint32_t*)ws,
+                               (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// isa_common.hpp -- constants, launch arguments and device helpers shared by the
+// gfx950 kernels of the IndexPool sparse-attention library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/isa.h"
+
+namespace isa {
+
+// Fixed dimensions of the path (see isa.h).
+constexpr int IDX_DIM = 128;     // indexer key / query channels
+constexpr int IDX_HEADS = 32;    // lightning-indexer heads
+constexpr int GROUP = 4;         // tokens pooled into one indexer key
+constexpr int ATT_HEADS = 64;    // MLA query heads
+constexpr int LAT_DIM = 512;     // MLA latent width (keys = values)
+constexpr int PAGE_TOK = 256;    // tokens per page
+constexpr int PAGE_GRP = PAGE_TOK / GROUP;  // pooled groups per page
+constexpr int MAX_K = ISA_MAX_K;
+
+// Score histogram: a monotone 11-bit key of a 32-bit score (exact below 128,
+// then 64 sub-bins per octave).  Used by every top-k kernel.
+constexpr int NBINS = 2048;
+constexpr uint32_t INVALID_SCORE = 0xFFFFFFFFu;  // never a valid score (max valid < 2^32 - 1)
+
+__device__ __forceinline__ int score_bin(uint32_t s) {
+  if (s < 64u) return (int)s;
+  int e = 31 - __clz(s);  // 6..31
+  return ((e - 5) << 6) | (int)((s >> (e - 6)) & 63u);
+}
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+// Per-call description of the batch, passed by value in the kernel arguments so
+// that no host-to-device copy is needed: lengths and a tile prefix per sequence.
+struct BatchArgs {
+  int32_t batch;
+  int32_t max_pages;
+  int32_t num_pages;
+  int32_t k;
+  int32_t lens[ISA_MAX_BATCH];
+  int32_t tile_start[ISA_MAX_BATCH + 1];  // first work tile of each sequence
+};
+
+// Sticky device error word (first word of every workspace).
+__device__ __forceinline__ void report(uint32_t* err, uint32_t bits) {
+  if (err) atomicOr(err, bits);
+}
+
+// Physical page of logical page j of sequence b, or -1 (and an error bit) when
+// the block table points outside the pool.
+__device__ __forceinline__ int phys_page(const int32_t* __restrict__ bt, int max_pages, int num_pages, int b,
+                                         int j, uint32_t* err) {
+  int p = bt[(size_t)b * max_pages + j];
+  if (p < 0 || p >= num_pages) {
+    report(err, ISA_DERR_PAGE_OOB);
+    return -1;
+  }
+  return p;
+}
+
+// Sequence owning work tile `t` (binary search over the per-sequence prefix).
+__device__ __forceinline__ int tile_owner(const BatchArgs& a, int t) {
+  int lo = 0, hi = a.batch - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (a.tile_start[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Block-wide exclusive prefix sum of one value per thread (blockDim.x <= 1024,
+// a multiple of 64).  `tmp` holds >= blockDim.x/64 + 1 words of LDS.  Returns
+// the exclusive prefix; *total receives the block sum.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) tmp[wid] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t run = 0;
+    for (int w = 0; w < nw; ++w) {
+      uint32_t t = tmp[w];
+      tmp[w] = run;
+      run += t;
+    }
+    tmp[nw] = run;
+  }
+  __syncthreads();
+  uint32_t r = tmp[wid] + x - v;
+  *total = tmp[nw];
+  __syncthreads();
+  return r;
+}
+
+}  // namespace isa

@@ -1,0 +1,55 @@
+// isa_launch.hpp -- host-side launchers of the gfx950 kernels (internal to libisa).
+#pragma once
+
+#include "isa_common.hpp"
+
+namespace isa {
+
+constexpr int TILE_G = 2048;  // pooled groups per decode work tile (32 pages)
+constexpr int TILE_MAX_PER_SEQ = (ISA_MAX_SEQ_LEN / GROUP + TILE_G - 1) / TILE_G;
+
+// Decode indexer workspace (pointers into the caller's workspace).
+struct DecodeWs {
+  uint32_t* err;
+  uint32_t* ghist;
+  uint32_t* tickets;
+  uint32_t* tile_cnt;
+  uint64_t* tile_list;
+};
+
+isa_status launch_indexer_decode(const BatchArgs& a, const int8_t* q, const int8_t* hw, const int8_t* pooled,
+                                 const int32_t* bt, const DecodeWs& w, int32_t* out_idx, int32_t* out_count,
+                                 int32_t* scores_out, int32_t ld_scores, hipStream_t stream);
+
+isa_status launch_topk_rows(const int32_t* scores, int32_t rows, int32_t cols, int32_t ld, int32_t k,
+                            int32_t* out_idx, int32_t* out_count, hipStream_t stream);
+
+isa_status launch_indexpool(const BatchArgs& a, const uint16_t* keys, const float w4[4], const int32_t* bt,
+                            float* scales, int8_t* pooled, bool dynamic, float* amax_part, uint32_t* err,
+                            hipStream_t stream);
+constexpr int POOL_TILE_G = 256;  // groups per pooling work tile (4 pages)
+
+// Sparse MLA attention: split plan chosen on the host.
+struct MlaPlan {
+  int32_t rows;
+  int32_t splits;         // token splits per row
+  int32_t groups_per_split;
+};
+struct MlaWs {
+  uint32_t* err;
+  float* o_part;    // [rows][splits][64][512]
+  float* ml_part;   // [rows][splits][64][2]  (running max in log2 units, sum)
+};
+MlaPlan plan_mla(int32_t rows, int32_t k);
+isa_status launch_sparse_mla(const BatchArgs& a, const MlaPlan& p, const uint16_t* q, const uint16_t* latent,
+                             const int32_t* bt, const int32_t* row_seq, const int32_t* row_pos,
+                             const int32_t* idx, const int32_t* count, int32_t k, float sm_scale, float* out,
+                             float* lse, const MlaWs& w, hipStream_t stream);
+
+isa_status launch_prefill_scores(const BatchArgs& a, const int8_t* q, const int8_t* hw, const int32_t* q_pos,
+                                 int32_t Q, const int8_t* pooled, const int32_t* bt, int32_t* scores,
+                                 int32_t ld, uint32_t* err, hipStream_t stream);
+
+isa_status launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+
+}  // namespace isa

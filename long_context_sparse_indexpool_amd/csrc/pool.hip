@@ -1,0 +1,170 @@
+// pool.hip -- IndexPool and int8 quantisation of the indexer key cache, gfx950.
+//
+// Method (pages cited by title): "GLM-5.3-Flash: 하이브리드 희소·선형 어텐션과
+// IndexPool·EPD로 1M 컨텍스트를 오픈 소스로 서빙하는 방법" (llm-wiki.hwlabs.dev),
+// section "IndexPool: 인덱서 KV 캐시를 4배 압축": four consecutive indexer keys merge
+// into one, k_pool = sum_i w_i k_i with learned weights summing to 1, which
+// quarters the cache; section "양자화: W8A8와 혼합 캐시": the distant compressed
+// cache is kept in INT8.  The quantiser (not on the pages): one symmetric
+// scale per sequence, amax/127, round half to even, clamp to +-127.  A last
+// group of r < 4 tokens renormalises its r weights.
+//
+// HBM-bound stream: 1 KiB of bf16 keys in, 128 B of int8 out per group.  A
+// workgroup handles 256 groups (4 key pages) of one sequence; 16 threads per
+// group, 8 channels each, 16-byte loads and 8-byte stores.  The dynamic scale
+// needs the sequence's amax first: a first launch reduces per-tile maxima and
+// the last tile of each sequence (atomic ticket) publishes the scale; the
+// second launch pools again and quantises.  A given scale skips the first pass.
+#include "isa_launch.hpp"
+
+namespace isa {
+
+constexpr int POOL_THREADS = 256;
+constexpr int POOL_ITERS = POOL_TILE_G / (POOL_THREADS / 16);
+
+struct PoolPtrs {
+  const uint16_t* keys;
+  const int32_t* bt;
+  float* scales;
+  int8_t* pooled;
+  float* amax_part;   // [ntiles]
+  uint32_t* tickets;  // [B], zero between calls
+  uint32_t* err;
+  float w[4];
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// Pooled fp32 values of channels 8c..8c+7 of group g (r tokens present).
+__device__ __forceinline__ void pool8(const PoolPtrs& P, const uint16_t* grp, int r, int c, float (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = 0.f;
+  float wsum = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (t < r) {
+      v4i v = *reinterpret_cast<const v4i*>(grp + t * IDX_DIM + c * 8);
+      const float w = P.w[t];
+      wsum += w;
+      x[0] = fmaf(w, bf16_lo(v.x), x[0]);
+      x[1] = fmaf(w, bf16_hi(v.x), x[1]);
+      x[2] = fmaf(w, bf16_lo(v.y), x[2]);
+      x[3] = fmaf(w, bf16_hi(v.y), x[3]);
+      x[4] = fmaf(w, bf16_lo(v.z), x[4]);
+      x[5] = fmaf(w, bf16_hi(v.z), x[5]);
+      x[6] = fmaf(w, bf16_lo(v.w), x[6]);
+      x[7] = fmaf(w, bf16_hi(v.w), x[7]);
+    }
+  }
+  if (r < 4) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = x[i] / wsum;
+  }
+}
+
+template <bool QUANT>
+__global__ __launch_bounds__(POOL_THREADS) void k_pool(const BatchArgs a, const PoolPtrs P) {
+  __shared__ int32_t pages[POOL_TILE_G / PAGE_GRP];
+  __shared__ float red[POOL_THREADS / 64];
+  __shared__ uint32_t ticket;
+  const int tid = threadIdx.x;
+  const int tile = blockIdx.x;
+  const int b = tile_owner(a, tile);
+  const int t0 = a.tile_start[b];
+  const int L = a.lens[b];
+  const int G = (L + GROUP - 1) / GROUP;
+  const int g0 = (tile - t0) * POOL_TILE_G;
+  if (tid < POOL_TILE_G / PAGE_GRP) {
+    int j = g0 / PAGE_GRP + tid;
+    pages[tid] = (g0 + tid * PAGE_GRP < G) ? phys_page(P.bt, a.max_pages, a.num_pages, b, j, P.err) : -1;
+  }
+  __syncthreads();
+  const int c = tid & 15;  // channel block
+  float inv = 1.f, scale = 1.f;
+  if (QUANT) {
+    scale = P.scales[b];
+    if (!(scale > 0.f) || !isfinite(scale)) {
+      if (tid == 0) report(P.err, ISA_DERR_NONFINITE);
+      scale = 1.f;
+    }
+  }
+  float amax = 0.f;
+  bool nonfinite = false;
+  for (int it = 0; it < POOL_ITERS; ++it) {
+    const int gl = it * (POOL_THREADS / 16) + (tid >> 4);
+    const int g = g0 + gl;
+    if (g >= G) break;
+    const int pg = pages[gl / PAGE_GRP];
+    if (pg < 0) continue;
+    const int r = min(4, L - 4 * g);
+    const uint16_t* grp = P.keys + ((size_t)pg * PAGE_TOK + (size_t)(4 * g) % PAGE_TOK) * IDX_DIM;
+    float x[8];
+    pool8(P, grp, r, c, x);
+    if (QUANT) {
+      uint32_t packed[2] = {0, 0};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float qv = __builtin_rintf(x[i] / scale);  // round half to even
+        qv = fminf(fmaxf(qv, -127.f), 127.f);
+        packed[i >> 2] |= ((uint32_t)((int32_t)qv) & 0xFFu) << (8 * (i & 3));
+      }
+      int8_t* dst = P.pooled + ((size_t)pg * PAGE_GRP + g % PAGE_GRP) * IDX_DIM + c * 8;
+      *reinterpret_cast<uint2*>(dst) = make_uint2(packed[0], packed[1]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        nonfinite |= !isfinite(x[i]);
+        amax = fmaxf(amax, fabsf(x[i]));
+      }
+    }
+  }
+  if (QUANT) return;
+
+  // ---- per-tile amax; the last tile of the sequence publishes the scale ----
+  if (__any(nonfinite) && (tid & 63) == 0) report(P.err, ISA_DERR_NONFINITE);
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  if (tid == 0) {
+    float m = red[0];
+    for (int i = 1; i < POOL_THREADS / 64; ++i) m = fmaxf(m, red[i]);
+    P.amax_part[tile] = m;
+    __threadfence();
+    ticket = atomicAdd(&P.tickets[b], 1u);
+  }
+  __syncthreads();
+  const int ntiles = a.tile_start[b + 1] - t0;
+  if ((int)ticket != ntiles - 1) return;
+  __threadfence();
+  float m = 0.f;
+  for (int i = tid; i < ntiles; i += POOL_THREADS)
+    m = fmaxf(m, __hip_atomic_load(&P.amax_part[t0 + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  __syncthreads();
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) {
+    float mm = red[0];
+    for (int i = 1; i < POOL_THREADS / 64; ++i) mm = fmaxf(mm, red[i]);
+    P.scales[b] = mm > 0.f ? mm / 127.f : 1.f;
+    __hip_atomic_store(&P.tickets[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+isa_status launch_indexpool(const BatchArgs& a, const uint16_t* keys, const float w4[4], const int32_t* bt,
+                            float* scales, int8_t* pooled, bool dynamic, float* amax_part, uint32_t* err,
+                            hipStream_t stream) {
+  const int ntiles = a.tile_start[a.batch];
+  // per-tile maxima, then one ticket counter per sequence
+  PoolPtrs P{keys, bt, scales, pooled, amax_part, reinterpret_cast<uint32_t*>(amax_part + ntiles), err,
+             {w4[0], w4[1], w4[2], w4[3]}};
+  if (dynamic) {
+    hipLaunchKernelGGL(k_pool<false>, dim3(ntiles), dim3(POOL_THREADS), 0, stream, a, P);
+    if (hipGetLastError() != hipSuccess) return ISA_ERR_HIP;
+  }
+  hipLaunchKernelGGL(k_pool<true>, dim3(ntiles), dim3(POOL_THREADS), 0, stream, a, P);
+  return hipGetLastError() == hipSuccess ? ISA_OK : ISA_ERR_HIP;
+}
+
+}  // namespace isa

@@ -1,0 +1,154 @@
+// score_prefill.hip -- prefill lightning-indexer scores, a dense int8 MFMA
+// contraction with a fused ReLU / head-weight epilogue, gfx950.
+//
+// Method (pages cited by title): "GLM-5.3 Sparse Attention은 연산량을 줄이지만 HBM
+// 수요는 지속된다" (remio.ai), section "GLM-5.3 Sparse Attention이 실제로 바꾸는 것":
+// the indexer scores the whole retained history.  "GLM-5.3-Flash vs
+// Qwen3.8-Flash-Next" (alltoptrend), section "수렴점 2 — 4배 압축 후 2,048 토큰만
+// 유지": 32 heads, keys pooled 4 -> 1 before scoring.  Prefill masking (not on
+// the pages; this library's contract): a query at position p sees groups
+// g <= floor(p/4), its own group included; later groups get -1.
+//
+// Scores of Q queries x G groups: [Q*32, 128] x [128, G] int8 -> int32, then
+// S[q][g] = sum_h w[q][h] * max(0, acc[q,h][g]).  v_mfma_i32_32x32x32_i8 with a
+// query's 32 heads as M and 32 groups as N; four MFMAs cover the 128 channels.
+// Each wave keeps 4 queries' operands and head weights in registers and
+// streams 32-group key blocks through them; the epilogue is two VALU ops per
+// element (max, 24-bit multiply-add) plus one cross-half add, which costs about
+// as much issue time as the MFMAs, so waves interleave the two.  A workgroup
+// covers 16 queries x 1024 groups.  Workgroups are numbered so that every
+// query block of one group range lands on the same XCD (dispatch is
+// round-robin over the 8 XCDs): the range's 128 KiB of keys is then fetched
+// into that XCD's L2 once and reused by all query blocks.
+#include "isa_launch.hpp"
+
+namespace isa {
+
+constexpr int PF_THREADS = 256;
+constexpr int PF_QW = 4;                      // queries per wave
+constexpr int PF_QB = PF_QW * (PF_THREADS / 64);  // queries per workgroup
+constexpr int PF_GT = 1024;                   // groups per workgroup
+constexpr int N_XCD = 8;
+
+struct PrefillPtrs {
+  const int8_t* q;
+  const int8_t* hw;
+  const int32_t* q_pos;
+  const int8_t* pooled;
+  const int32_t* bt;
+  int32_t* scores;
+  int32_t ld;
+  int32_t Q;
+  int32_t n_qb;
+  int32_t n_gr;
+  uint32_t* err;
+};
+
+__global__ __launch_bounds__(PF_THREADS) void k_prefill_scores(const BatchArgs a, const PrefillPtrs P) {
+  __shared__ int32_t pages[PF_GT / PAGE_GRP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int xcd = blockIdx.x % N_XCD;
+  const int i = blockIdx.x / N_XCD;
+  const int qb = i % P.n_qb;
+  const int gr = (i / P.n_qb) * N_XCD + xcd;
+  if (gr >= P.n_gr) return;
+  const int L = a.lens[0];
+  const int G = (L + GROUP - 1) / GROUP;
+  const int g0 = gr * PF_GT;
+  const int gN = min(G - g0, PF_GT);
+  if (tid < PF_GT / PAGE_GRP) {
+    pages[tid] = tid * PAGE_GRP < gN ? phys_page(P.bt, a.max_pages, a.num_pages, 0, g0 / PAGE_GRP + tid, P.err)
+                                     : -1;
+  }
+
+  // this wave's queries: operands, head weights of the accumulator rows, visible range
+  v4i qa[PF_QW][4];
+  uint32_t wv[PF_QW][16];
+  int lastg[PF_QW];
+  bool bad = false;
+#pragma unroll
+  for (int qq = 0; qq < PF_QW; ++qq) {
+    int qi = qb * PF_QB + wave * PF_QW + qq;
+    bool live = qi < P.Q;
+    int qc = live ? qi : 0;
+    const v4i* qp = reinterpret_cast<const v4i*>(P.q + (size_t)qc * IDX_HEADS * IDX_DIM + (lane & 31) * IDX_DIM +
+                                                 (lane >> 5) * 64);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qa[qq][c] = qp[c];
+    const int8_t* hp = P.hw + (size_t)qc * IDX_HEADS;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      int w = hp[(r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)];
+      bad |= (w < 0) | (w > 64);
+      wv[qq][r] = (uint32_t)w;
+    }
+    int p = P.q_pos[qc];
+    if (live && (p < 0 || p >= L)) {
+      bad = true;
+      p = -4;
+    }
+    lastg[qq] = live ? p / GROUP : -2;  // -2: query beyond Q, nothing stored
+  }
+  if (__any(bad) && lane == 0) report(P.err, ISA_DERR_HEADW_RANGE | ISA_DERR_ROW_RANGE);
+  __syncthreads();
+
+  const int8_t* kbase = P.pooled + (lane >> 5) * 64;
+  auto load_blk = [&](int blk, v4i (&kb)[4]) {
+    int gl = blk * 32 + (lane & 31);
+    int pg = gl < gN ? pages[gl / PAGE_GRP] : -1;
+    if (pg >= 0) {
+      const v4i* p = reinterpret_cast<const v4i*>(kbase + ((size_t)pg * PAGE_GRP + gl % PAGE_GRP) * IDX_DIM);
+      kb[0] = p[0];
+      kb[1] = p[1];
+      kb[2] = p[2];
+      kb[3] = p[3];
+    } else {
+      kb[0] = kb[1] = kb[2] = kb[3] = v4i{0, 0, 0, 0};
+    }
+  };
+  const int nblk = (gN + 31) / 32;
+  v4i cur[4], nxt[4];
+  load_blk(0, cur);
+  bool overflow = false;
+  for (int blk = 0; blk < nblk; ++blk) {
+    if (blk + 1 < nblk) load_blk(blk + 1, nxt);
+    const int g = g0 + blk * 32 + (lane & 31);
+#pragma unroll
+    for (int qq = 0; qq < PF_QW; ++qq) {
+      v16i acc = {0};
+      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[qq][0], cur[0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[qq][1], cur[1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[qq][2], cur[2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[qq][3], cur[3], acc, 0, 0, 0);
+      uint32_t s = 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s += wv[qq][r] * (uint32_t)max(acc[r], 0);
+      s += __shfl_xor(s, 32, 64);
+      if (lane < 32 && g < g0 + gN && lastg[qq] != -2) {
+        int qi = qb * PF_QB + wave * PF_QW + qq;
+        bool vis = g <= lastg[qq];
+        overflow |= vis && s > 0x7FFFFFFFu;
+        __builtin_nontemporal_store(vis ? (int32_t)s : -1, P.scores + (size_t)qi * P.ld + g);
+      }
+    }
+    cur[0] = nxt[0];
+    cur[1] = nxt[1];
+    cur[2] = nxt[2];
+    cur[3] = nxt[3];
+  }
+  if (__any(overflow) && lane == 0) report(P.err, ISA_DERR_SCORE_OVERFLOW);
+}
+
+isa_status launch_prefill_scores(const BatchArgs& a, const int8_t* q, const int8_t* hw, const int32_t* q_pos,
+                                 int32_t Q, const int8_t* pooled, const int32_t* bt, int32_t* scores,
+                                 int32_t ld, uint32_t* err, hipStream_t stream) {
+  const int G = (a.lens[0] + GROUP - 1) / GROUP;
+  PrefillPtrs P{q, hw, q_pos, pooled, bt, scores, ld, Q, (Q + PF_QB - 1) / PF_QB, (G + PF_GT - 1) / PF_GT, err};
+  const int gr_rounds = (P.n_gr + N_XCD - 1) / N_XCD;
+  const long long nwg = (long long)gr_rounds * N_XCD * P.n_qb;
+  if (nwg > 0x7FFFFFFF) return ISA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(k_prefill_scores, dim3((unsigned)nwg), dim3(PF_THREADS), 0, stream, a, P);
+  return hipGetLastError() == hipSuccess ? ISA_OK : ISA_ERR_HIP;
+}
+
+}  // namespace isa

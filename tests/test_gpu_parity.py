@@ -1,0 +1,281 @@
+"""GPU parity of the HIP path against the CPU oracle on small seeded inputs that
+still span several work tiles, ragged tails, the dense fallback and ties.
+
+Bars: pooled keys within 1 int8 LSB and scales within 1e-6 relative; indexer
+scores and selected ids bit-exact; attention max-abs <= 2e-2, relative L2 <=
+1e-3, |d lse| <= 1e-3.  Every case runs through the C ABI.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth.configs import IDX_DIM, LAT_DIM, SM_SCALE, custom
+
+import harness as H
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = [1, 2, 3, 4, 5, 255, 256, 257, 1001, 2047, 2048, 2049, 2052, 4099, 8192, 8195, 9000, 20003]
+
+
+@pytest.fixture(scope="module")
+def ragged_batch():
+    H.log("ragged batch: pool")
+    wl = custom("ragged", 11, RAGGED, paged_random=True)
+    db = H.make_batch(wl)
+    H.run_pool(db)
+    return db
+
+
+def test_library_loads_on_gpu():
+    m = H.isa()
+    assert "gfx950" in m.version()
+
+
+def test_pool_parity_ragged(ragged_batch):
+    res = H.check_pool(ragged_batch)
+    assert len(res) == len(RAGGED)
+
+
+def test_pool_given_scale(ragged_batch):
+    db = ragged_batch
+    wl = db.wl
+    given = db.scales.cpu().numpy() * np.float32(0.5)  # half the dynamic scale: values clamp at +-127
+    db2 = H.DeviceBatch(wl, db.seqs, db.bt, keys=db.keys, host=db.host)
+    H.run_pool(db2, flags=1, scales_in=given)
+    to = wl.token_offsets
+    w4 = wl.pool_weights()
+    for b in range(wl.batch):
+        ref = oracle.pool_given_scale(db.host["keys"][to[b]: to[b + 1]], w4, float(given[b]))
+        got = H.pooled_logical(db2, b)
+        assert np.max(np.abs(got.astype(int) - ref.astype(int))) <= 1
+        assert got.max() <= 127 and got.min() >= -127
+
+
+@pytest.mark.parametrize("k", [512, 1, 13])
+def test_topk_decode_parity_ragged(ragged_batch, k):
+    db = ragged_batch
+    H.log(f"topk decode k={k}")
+    idx, cnt, sc, _ = H.run_topk(db, k=k)
+    wl = db.wl
+
+    def one(b):
+        S = H.oracle_scores_for(db, b)
+        G = wl.groups(b)
+        assert np.array_equal(sc[b, :G].astype(np.int64), S), f"seq {b} (L={wl.lens[b]}): scores differ"
+        H.check_topk_row(S, k, idx[b], int(cnt[b]))
+        return True
+
+    assert all(oracle.map_rows(one, range(wl.batch)))
+
+
+def test_topk_decode_without_score_output_matches(ragged_batch):
+    db = ragged_batch
+    idx1, cnt1, _, _ = H.run_topk(db, with_scores=True)
+    idx2, cnt2, _, _ = H.run_topk(db, with_scores=False)
+    assert np.array_equal(idx1, idx2) and np.array_equal(cnt1, cnt2)
+
+
+def _batch_with_keys(name, lens, keys_logical, seed=5, paged=True):
+    wl = custom(name, seed, lens, paged_random=paged)
+    db = H.make_batch(wl, with_keys=False, with_latent=False)
+    db.host["keys"] = keys_logical
+    db.keys = H.pool_from_logical(wl, keys_logical, 256, H.NAN_BF16)
+    H.run_pool(db)
+    return db
+
+
+def test_topk_ties_from_repeated_keys():
+    """Pooled rows drawn from 3 distinct rows: every score is one of 3 values, so
+    thousands of candidates tie at the boundary (exercises the exact resolve
+    both in LDS and from the global lists)."""
+    lens = [40000, 9000, 3000]
+    base = synth.normal_bf16(21, 1, (3, IDX_DIM))
+    pick = synth.uniform_i8(21, 2, (sum(lens) // 4 + 4,), 0, 2).astype(np.int64)
+    keys = np.repeat(base[pick], 4, axis=0)[: sum(lens)]
+    db = _batch_with_keys("ties", lens, keys)
+    for k in (512, 100):
+        idx, cnt, sc, _ = H.run_topk(db, k=k)
+        for b in range(len(lens)):
+            S = H.oracle_scores_for(db, b)
+            assert len(np.unique(S)) <= 3
+            assert np.array_equal(sc[b, : db.wl.groups(b)].astype(np.int64), S)
+            H.check_topk_row(S, k, idx[b], int(cnt[b]))
+
+
+def test_topk_all_scores_equal():
+    lens = [30000, 5000]
+    keys = np.zeros((sum(lens), IDX_DIM), np.uint16)
+    db = _batch_with_keys("zero", lens, keys)
+    idx, cnt, sc, _ = H.run_topk(db)
+    assert not np.any(sc[0, :7500]) and not np.any(sc[1, :1250])
+    for b in range(2):
+        assert cnt[b] == 512 and np.array_equal(idx[b], np.arange(512))
+
+
+def test_topk_rows_from_scores_in():
+    m = H.isa()
+    rng = np.random.default_rng(3)
+    rows = []
+    rows.append(rng.integers(0, 2**31 - 1, size=70000))
+    rows.append(rng.integers(0, 50, size=70000))                   # heavy ties
+    r = rng.integers(0, 10**7, size=70000); r[rng.random(70000) < 0.7] = -1
+    rows.append(r)                                                  # masked entries
+    r = np.full(70000, -1); r[[5, 77, 69999]] = [3, 3, 0]
+    rows.append(r)                                                  # fewer than k valid
+    rows.append(np.full(70000, 12345))                              # all equal, > ROW_CAND in the boundary
+    r = rng.integers(0, 1000, size=70000); r[60000:] = -1
+    rows.append(r)
+    S = np.stack(rows).astype(np.int32)
+    for k in (512, 7):
+        sd = torch.from_numpy(S).cuda()
+        idx = torch.full((S.shape[0], k), -7, dtype=torch.int32, device="cuda")
+        cnt = torch.zeros(S.shape[0], dtype=torch.int32, device="cuda")
+        ws = m.alloc_workspace(m.workspace_size(m.ISA_OP_INDEXER_TOPK, None))
+        m.isa_indexer_topk(None, None, None, None, sd, S.shape[0], S.shape[1], k, idx, cnt, None, ws)
+        torch.cuda.synchronize()
+        idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+        for i in range(S.shape[0]):
+            H.check_topk_row(S[i].astype(np.int64), k, idx[i], int(cnt[i]))
+
+
+def test_attention_parity_ragged(ragged_batch):
+    db = ragged_batch
+    wl = db.wl
+    H.log("attention ragged")
+    idx, cnt, _, _ = H.run_topk(db, with_scores=False)
+    out, lse = H.run_attention(db, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), 512)
+    lat = db.host["latent"]
+    to = wl.token_offsets
+    q = db.host["q_attn"]
+
+    def one(b):
+        L = wl.lens[b]
+        ref, ref_lse = oracle.attention(q[b], lat[to[b]: to[b + 1]], L, L - 1, idx[b], int(cnt[b]), SM_SCALE)
+        return H.attention_tolerance(out[b], ref, lse[b], ref_lse)
+
+    res = oracle.map_rows(one, range(wl.batch))
+    H.log(f"attention worst max-abs {max(r[0] for r in res):.2e} rel {max(r[1] for r in res):.2e}")
+
+
+def test_attention_rows_with_positions(ragged_batch):
+    """Rows that map to sequences with an earlier last-visible position (prefill rows)."""
+    db = ragged_batch
+    wl = db.wl
+    rng = np.random.default_rng(9)
+    row_seq = np.array([17, 17, 17, 16, 12, 9, 0, 13, 15, 14], np.int32)
+    row_pos = np.array([rng.integers(0, wl.lens[s]) for s in row_seq], np.int32)
+    row_pos[0] = 0
+    row_pos[1] = wl.lens[17] - 1
+    rows = len(row_seq)
+    # selections: random groups (sorted, unique) of each row's sequence, k=512
+    k = 512
+    idx = np.full((rows, k), -1, np.int32)
+    cnt = np.zeros(rows, np.int32)
+    for r, s in enumerate(row_seq):
+        G = wl.groups(s)
+        n = min(G, k if r % 2 == 0 else 37)
+        idx[r, :n] = np.sort(rng.choice(G, n, replace=False))
+        cnt[r] = n
+    q = synth.normal_bf16(4, 6, (rows, 64, LAT_DIM))
+    out, lse = H.run_attention(db, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), k, q=q,
+                               row_seq=row_seq, row_pos=row_pos, rows=rows)
+    lat = db.host["latent"]
+    to = wl.token_offsets
+    for r, s in enumerate(row_seq):
+        ref, ref_lse = oracle.attention(q[r], lat[to[s]: to[s + 1]], wl.lens[s], int(row_pos[r]), idx[r],
+                                        int(cnt[r]), SM_SCALE)
+        H.attention_tolerance(out[r], ref, lse[r], ref_lse)
+
+
+def test_prefill_scores_topk_attention():
+    m = H.isa()
+    L = 20003
+    wl = custom("prefill_small", 31, [L], kind="prefill",
+                q_pos=[0, 1, 3, 4, 5, 100, 2047, 2048, 2049, 4095, 5000, 9999, 15000, 19999, 20000, 20002] +
+                list(range(18000, 18024)))
+    db = H.make_batch(wl)
+    H.run_pool(db)
+    Q = wl.rows
+    G = wl.groups(0)
+    ld = (G + 3) // 4 * 4
+    qh, hwh = wl.q_idx(), wl.head_w()
+    qpos = wl.row_pos()
+    sc = torch.full((Q, ld), -7, dtype=torch.int32, device="cuda")
+    ws = m.alloc_workspace(256)
+    m.isa_indexer_prefill_scores(torch.from_numpy(qh).cuda(), torch.from_numpy(hwh).cuda(),
+                                 torch.from_numpy(qpos).cuda(), Q, db.pooled, db.seqs, sc, ld, ws)
+    torch.cuda.synchronize()
+    assert m.isa_device_error(ws) == 0
+    S = sc.cpu().numpy()
+    k8 = H.pooled_logical(db, 0)
+    refs = oracle.map_rows(lambda i: oracle.prefill_scores(qh[i], hwh[i], int(qpos[i]), k8), range(Q))
+    for i in range(Q):
+        assert np.array_equal(S[i, :G].astype(np.int64), refs[i]), f"query {i} (pos {qpos[i]})"
+        assert np.all(S[i, G:] == -7), "columns beyond the sequence were written"
+    # selection from the precomputed rows
+    idx = torch.full((Q, 512), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(Q, dtype=torch.int32, device="cuda")
+    m.isa_indexer_topk(None, None, None, None, sc, Q, ld, 512, idx, cnt, None, ws)
+    torch.cuda.synchronize()
+    idxh, cnth = idx.cpu().numpy(), cnt.cpu().numpy()
+    for i in range(Q):
+        H.check_topk_row(refs[i], 512, idxh[i], int(cnth[i]))
+    out, lse = H.run_attention(db, idx, cnt, 512, row_seq=np.zeros(Q, np.int32), row_pos=qpos, rows=Q)
+    q = db.host["q_attn"]
+    lat = db.host["latent"]
+    for i in range(Q):
+        ref, ref_lse = oracle.attention(q[i], lat, L, int(qpos[i]), idxh[i], int(cnth[i]), SM_SCALE)
+        H.attention_tolerance(out[i], ref, lse[i], ref_lse)
+
+
+def test_paging_is_invisible():
+    """The same logical data at two physical placements gives bit-identical outputs."""
+    lens = [9000, 3001, 20000]
+    outs = []
+    for paged in (False, True):
+        wl = custom("perm", 13, lens, paged_random=paged)
+        db = H.make_batch(wl)
+        H.run_pool(db)
+        idx, cnt, sc, _ = H.run_topk(db)
+        out, lse = H.run_attention(db, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), 512)
+        outs.append((np.concatenate([H.pooled_logical(db, b).ravel() for b in range(3)]), idx, cnt, sc, out, lse))
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+
+
+def test_repeat_runs_are_bitwise_identical(ragged_batch):
+    db = ragged_batch
+    r1 = H.run_topk(db)
+    r2 = H.run_topk(db)
+    for a, b in zip(r1[:3], r2[:3]):
+        assert np.array_equal(a, b)
+    i, c = torch.from_numpy(r1[0]).cuda(), torch.from_numpy(r1[1]).cuda()
+    o1 = H.run_attention(db, i, c, 512)
+    o2 = H.run_attention(db, i, c, 512)
+    assert np.array_equal(o1[0], o2[0]) and np.array_equal(o1[1], o2[1])
+
+
+def test_device_errors_are_reported_not_faulted():
+    """A block table entry outside the pool and a head weight outside [0,64] set
+    error bits; the kernels skip the bad accesses."""
+    m = H.isa()
+    wl = custom("err", 17, [3000, 700])
+    db = H.make_batch(wl, with_latent=False)
+    H.run_pool(db)
+    bad_bt = db.bt.clone()
+    bad_bt[0, 3] = wl.num_pages + 5
+    seqs = m.Seqs(wl.lens, bad_bt, wl.num_pages)
+    hw = wl.head_w()
+    hw[0, 0] = 65  # sequence 0 is scored (sequence 1 takes the dense fallback and reads no weights)
+    idx = torch.zeros((2, 512), dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(2, dtype=torch.int32, device="cuda")
+    ws = m.alloc_workspace(m.workspace_size(m.ISA_OP_INDEXER_TOPK, seqs))
+    m.isa_indexer_topk(torch.from_numpy(wl.q_idx()).cuda(), torch.from_numpy(hw).cuda(), db.pooled, seqs, None, 2,
+                       0, 512, idx, cnt, None, ws)
+    torch.cuda.synchronize()
+    err = m.isa_device_error(ws, clear=True)
+    assert err & m.DERR_PAGE_OOB and err & m.DERR_HEADW_RANGE
+    assert m.isa_device_error(ws) == 0
