@@ -1,5 +1,5 @@
-// indexer_decode.hip -- decode-time lightning-indexer scoring fused with exact
-// top-k group selection, for gfx950.
+// indexer_decode.hip -- decode-time lightning-indexer scoring and exact top-k
+// group selection, for gfx950.
 //
 // Method (pages cited by title): "GLM-5.3 Sparse Attention은 연산량을 줄이지만 HBM
 // 수요는 지속된다" (remio.ai), section "GLM-5.3 Sparse Attention이 실제로 바꾸는 것":
@@ -9,41 +9,46 @@
 // 4 -> 1, top 512 blocks of 4 tokens.  Score of a pooled group (the pages print
 // no formula; this library's contract): S = sum_h w_h * max(0, q_h . k).
 //
-// Design.  One launch.  The grid is a list of work tiles of 2048 pooled groups
-// (32 pages) per sequence.  Each 256-thread workgroup streams its tile's int8
-// keys straight from HBM into MFMA operands: v_mfma_i32_32x32x32_i8 with the 32
-// indexer heads as M (query in registers, loaded once) and 32 groups as N, four
-// MFMAs over the 128 channels; each lane loads 64 contiguous bytes of one key.
-// The epilogue applies ReLU and the head weights exactly (u32 multiply-add;
-// every partial stays below 2^32) and reduces the heads across the two lane
-// halves.  Scores go to LDS (and, optionally, to a checking buffer).
-// The workgroup then emits the candidates that can still be in the global
-// top-k: it histograms its scores by an 11-bit monotone key, finds the bin
-// holding its own k-th best, and writes every candidate from that bin up to a
-// per-tile list ordered by bin (descending), and adds those bins to a global
-// per-sequence histogram.  The last workgroup of a sequence (atomic ticket)
-// finds the global boundary bin, takes the candidates above it, resolves the
-// boundary bin exactly by radix select on (score, -id) keys, sorts the k ids
-// ascending and writes them; it then clears the histogram and ticket for the
-// next call.
+// Two launches, no cross-workgroup synchronisation inside either (on this
+// 8-XCD part a device-scope fence writes back the whole L2, which cost more
+// than the streaming itself; the kernel boundary gives coherence for free).
+//
+// k_indexer_score: one workgroup per work tile of 2048 pooled groups (32
+// pages) of one sequence.  Its four waves stream the tile's int8 keys straight
+// from HBM into v_mfma_i32_32x32x32_i8 operands -- the 32 indexer heads are M
+// (the query stays in registers), 32 groups are N, four MFMAs span the 128
+// channels, each lane loading 64 contiguous bytes of one key, two steps of
+// loads kept in flight.  The epilogue applies ReLU and the head weights exactly
+// in u32 (every partial stays below 2^32) and adds the two lane halves.  The
+// workgroup then keeps only candidates that can still reach the global top-k:
+// it histograms its scores by an 11-bit monotone key, finds the bin of its own
+// k-th best, and writes every candidate from that bin up into a per-tile list
+// ordered by descending bin, plus the (bin, count) pairs of those bins.
+//
+// k_indexer_select: one workgroup per sequence.  It sums the tiles' pairs into
+// an LDS histogram, finds the global boundary bin, takes every candidate above
+// it, resolves the boundary bin exactly by radix select on (score, -id) keys,
+// sorts the k ids ascending and writes them.
 #include "isa_launch.hpp"
 #include "select_device.hpp"
 
 namespace isa {
 
 constexpr int DEC_THREADS = 256;
-constexpr int DEC_STEPS = TILE_G / 128;        // 4 waves x 32 groups per step
-constexpr int CAND_LDS = 1024;                 // boundary candidates resolved in LDS
+constexpr int DEC_STEPS = TILE_G / 128;  // 4 waves x 32 groups per step
+constexpr int DEC_PF = 2;                // steps of key loads in flight per wave
+constexpr int SEL_THREADS = 512;
+constexpr int SEL_CAND = 2048;           // boundary candidates resolved in LDS
+constexpr int SEL_LDS_PAIRS = 16384;     // (bin, count) pairs fetched into LDS in the first round
 
 struct DecodePtrs {
   const int8_t* q;
   const int8_t* hw;
   const int8_t* pooled;
   const int32_t* bt;
-  uint32_t* ghist;      // [B][NBINS], zero between calls
-  uint32_t* tickets;    // [B], zero between calls
-  uint32_t* tile_cnt;   // [ntiles]
-  uint64_t* tile_list;  // [ntiles][TILE_G]
+  uint2* tile_meta;     // [ntiles] (candidates, pairs)
+  uint32_t* tile_pairs; // [ntiles][PAIR_CAP] (bin << 16 | count), descending bins
+  uint64_t* tile_list;  // [ntiles][TILE_G] (score << 32 | group), descending bins
   int32_t* out_idx;     // [B][k]
   int32_t* out_count;   // [B]
   int32_t* scores_out;  // [B][ld] or null
@@ -51,36 +56,23 @@ struct DecodePtrs {
   uint32_t* err;
 };
 
-__device__ __forceinline__ void load_key_operand(v4i (&kb)[4], const int8_t* __restrict__ p) {
-  const v4i* v = reinterpret_cast<const v4i*>(p);
-  kb[0] = __builtin_nontemporal_load(v + 0);
-  kb[1] = __builtin_nontemporal_load(v + 1);
-  kb[2] = __builtin_nontemporal_load(v + 2);
-  kb[3] = __builtin_nontemporal_load(v + 3);
-}
-
-__global__ __launch_bounds__(DEC_THREADS) void k_indexer_decode(const BatchArgs a, const DecodePtrs P) {
-  __shared__ uint32_t sc[TILE_G];          // tile scores; later: boundary candidates (as u64)
-  __shared__ uint32_t hist[NBINS];         // tile histogram -> emission cursors -> global histogram
-  __shared__ uint32_t sel[MAX_K];          // final selection
-  __shared__ uint32_t toff[2 * (TILE_MAX_PER_SEQ + 1)];  // per-tile prefix of sure / boundary counts
-  __shared__ uint32_t h256[256];
+__global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a, const DecodePtrs P) {
+  __shared__ uint32_t sc[TILE_G];   // tile scores
+  __shared__ uint32_t hist[NBINS];  // tile histogram -> emission cursors
   __shared__ uint32_t scr[SCR_WORDS];
   __shared__ int32_t pages[TILE_G / PAGE_GRP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile = blockIdx.x;
   const int b = tile_owner(a, tile);
-  const int t0 = a.tile_start[b];
-  const int ntiles = a.tile_start[b + 1] - t0;
   const int L = a.lens[b];
   const int G = (L + GROUP - 1) / GROUP;
   const uint32_t K = (uint32_t)a.k;
-  const int g0 = (tile - t0) * TILE_G;
+  const int g0 = (tile - a.tile_start[b]) * TILE_G;
   const int gN = min(G - g0, TILE_G);
   const bool dense = G <= (int)K;
 
-  if (dense && P.scores_out == nullptr) {  // fewer than k groups: select them all
+  if (dense && P.scores_out == nullptr) {  // at most k groups: select them all
     for (int i = tid; i < (int)K; i += DEC_THREADS) P.out_idx[(size_t)b * K + i] = i < G ? i : -1;
     if (tid == 0) P.out_count[b] = G;
     return;
@@ -119,26 +111,27 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_decode(const BatchArgs 
 
   // ---- stream the tile: 16 steps of 128 groups (32 per wave) ----
   const int8_t* kbase = P.pooled + (lane >> 5) * 64;
-  auto key_ptr = [&](int step) -> const int8_t* {
+  auto load_step = [&](int step, v4i (&kb)[4]) {
     int gl = step * 128 + wave * 32 + (lane & 31);
     int pg = pages[gl / PAGE_GRP];
-    if (gl >= gN || pg < 0) return nullptr;
-    return kbase + ((size_t)pg * PAGE_GRP + (gl % PAGE_GRP)) * IDX_DIM;
-  };
-  v4i cur[4], nxt[4];
-  {
-    const int8_t* p = key_ptr(0);
-    if (p) load_key_operand(cur, p);
-    else cur[0] = cur[1] = cur[2] = cur[3] = v4i{0, 0, 0, 0};
-  }
-  bool overflow = false;
-#pragma unroll 2
-  for (int step = 0; step < DEC_STEPS; ++step) {
-    if (step + 1 < DEC_STEPS) {
-      const int8_t* p = key_ptr(step + 1);
-      if (p) load_key_operand(nxt, p);
-      else nxt[0] = nxt[1] = nxt[2] = nxt[3] = v4i{0, 0, 0, 0};
+    if (gl < gN && pg >= 0) {
+      const v4i* p = reinterpret_cast<const v4i*>(kbase + ((size_t)pg * PAGE_GRP + (gl % PAGE_GRP)) * IDX_DIM);
+      kb[0] = p[0];
+      kb[1] = p[1];
+      kb[2] = p[2];
+      kb[3] = p[3];
+    } else {
+      kb[0] = kb[1] = kb[2] = kb[3] = v4i{0, 0, 0, 0};
     }
+  };
+  v4i buf[DEC_PF + 1][4];
+#pragma unroll
+  for (int s = 0; s < DEC_PF; ++s) load_step(s, buf[s]);
+  bool overflow = false;
+#pragma unroll
+  for (int step = 0; step < DEC_STEPS; ++step) {
+    if (step + DEC_PF < DEC_STEPS) load_step(step + DEC_PF, buf[(step + DEC_PF) % (DEC_PF + 1)]);
+    v4i(&cur)[4] = buf[step % (DEC_PF + 1)];
     v16i acc = {0};
     acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[0], cur[0], acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[1], cur[1], acc, 0, 0, 0);
@@ -155,10 +148,6 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_decode(const BatchArgs 
       overflow |= valid && s > 0x7FFFFFFFu;
       if (P.scores_out && valid) P.scores_out[(size_t)b * P.ld_scores + g0 + gl] = (int32_t)s;
     }
-    cur[0] = nxt[0];
-    cur[1] = nxt[1];
-    cur[2] = nxt[2];
-    cur[3] = nxt[3];
   }
   if (__any(overflow) && lane == 0) report(P.err, ISA_DERR_SCORE_OVERFLOW);
   __syncthreads();
@@ -180,28 +169,32 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_decode(const BatchArgs 
   int bt_local;
   uint32_t n_gt_local, n_valid;
   find_boundary(hist, K, &bt_local, &n_gt_local, &n_valid, scr);
-  const int blo = bt_local < 0 ? 0 : bt_local;  // emit all when at most k are valid
+  const int blo = bt_local < 0 ? 0 : bt_local;  // all valid candidates when at most k
+  uint32_t* pairs = P.tile_pairs + (size_t)tile * PAIR_CAP;
   {
-    // convert counts of bins >= blo into emission cursors (descending bins), and
-    // add them to the sequence's global histogram
-    const int per = NBINS / DEC_THREADS;
+    // bins >= blo, descending: emission cursors and (bin, count) pairs
+    constexpr int per = NBINS / DEC_THREADS;
     const int hi = NBINS - tid * per;
-    uint32_t local = 0;
+    uint32_t local = 0, nz = 0;
     for (int j = 0; j < per; ++j) {
       int bin = hi - 1 - j;
-      if (bin >= blo) local += hist[bin];
+      if (bin >= blo) {
+        local += hist[bin];
+        nz += hist[bin] != 0;
+      }
     }
-    uint32_t tot;
+    uint32_t tot, npairs;
     uint32_t run = block_exclusive_scan(local, scr, &tot);
+    uint32_t po = block_exclusive_scan(nz, scr, &npairs);
     for (int j = 0; j < per; ++j) {
       int bin = hi - 1 - j;
       if (bin < blo) break;
       uint32_t c = hist[bin];
-      if (c) atomicAdd(&P.ghist[(size_t)b * NBINS + bin], c);
+      if (c) pairs[po++] = ((uint32_t)bin << 16) | c;
       hist[bin] = run;
       run += c;
     }
-    if (tid == 0) P.tile_cnt[tile] = tot;
+    if (tid == 0) P.tile_meta[tile] = make_uint2(tot, npairs);
   }
   __syncthreads();
   uint64_t* list = P.tile_list + (size_t)tile * TILE_G;
@@ -215,142 +208,225 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_decode(const BatchArgs 
     uint32_t slot = atomicAdd(&hist[bin], 1u);
     list[slot] = ((uint64_t)s << 32) | (uint32_t)(g0 + e);
   }
+}
 
-  // ---- ticket: the last tile of the sequence finishes the selection ----
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) scr[SCR_RES + 8] = atomicAdd(&P.tickets[b], 1u);
-  __syncthreads();
-  if ((int)scr[SCR_RES + 8] != ntiles - 1) return;
-  __threadfence();
-
-  uint32_t* gh = P.ghist + (size_t)b * NBINS;
-  for (int i = tid; i < NBINS; i += DEC_THREADS) {
-    hist[i] = __hip_atomic_load(&gh[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&gh[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Index j with off[j] <= i < off[j+1] (off ascending, n entries + sentinel).
+__device__ __forceinline__ int owner_of(const uint32_t* off, int n, uint32_t i) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= i) lo = mid; else hi = mid - 1;
   }
-  if (tid == 0) __hip_atomic_store(&P.tickets[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return lo;
+}
+
+// Per sequence: merge the tiles' candidates into the exact top k.
+//  1. one round of loads: every tile's (kept, pairs) and its first SEL_PAIRS_PER
+//     (bin, count) pairs, summed into an LDS histogram (longer pair lists, which
+//     need a tile spanning hundreds of bins, take a second round);
+//  2. the global boundary bin and, per tile, how many candidates lie above it and
+//     in it (pair lists and candidate lists share the descending bin order);
+//  3. one round of loads gathers the candidates above the boundary and those in it;
+//  4. the boundary candidates are ranked by (score, -id) -- all-pairs counting in
+//     LDS, or radix select when there are too many -- and the k ids are placed in
+//     ascending order by counting, straight into the output row.
+__global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs a, const DecodePtrs P) {
+  __shared__ uint32_t hist[NBINS];
+  __shared__ uint32_t lpairs[SEL_LDS_PAIRS];
+  __shared__ uint32_t npr[TILE_MAX_PER_SEQ];
+  __shared__ uint32_t ovf_off[TILE_MAX_PER_SEQ + 1];
+  __shared__ uint32_t sure_off[TILE_MAX_PER_SEQ + 1];
+  __shared__ uint32_t bnd_off[TILE_MAX_PER_SEQ + 1];
+  __shared__ uint32_t ngt[TILE_MAX_PER_SEQ];
+  __shared__ uint32_t nbd[TILE_MAX_PER_SEQ];
+  __shared__ uint64_t cand[SEL_CAND];
+  __shared__ uint32_t sel[MAX_K];
+  __shared__ uint32_t h256[256];
+  __shared__ uint32_t scr[SCR_WORDS];
+
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int G = (a.lens[b] + GROUP - 1) / GROUP;
+  const uint32_t K = (uint32_t)a.k;
+  if (G <= (int)K) return;  // dense row: written by the scoring kernel
+  const int t0 = a.tile_start[b];
+  const int nt = a.tile_start[b + 1] - t0;
+  // pairs of each tile fetched in the first round (a multiple of 4, at most 64)
+  const int per = min(64, (SEL_LDS_PAIRS / nt) & ~3);
+
+  for (int i = tid; i < NBINS; i += SEL_THREADS) hist[i] = 0;
+  __syncthreads();
+  // 1. metadata and the head of every pair list in one round
+  constexpr int CH = 4;  // pairs per load
+  for (int u = tid; u < nt * (per / CH); u += SEL_THREADS) {
+    const int j = u / (per / CH), part = u % (per / CH);
+    const uint32_t np = P.tile_meta[t0 + j].y;
+    const uint4 v = *reinterpret_cast<const uint4*>(P.tile_pairs + (size_t)(t0 + j) * PAIR_CAP + part * CH);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      const uint32_t p = part * CH + e;
+      if (p < np) {
+        lpairs[j * per + p] = w[e];
+        atomicAdd(&hist[w[e] >> 16], w[e] & 0xFFFFu);
+      }
+    }
+    if (part == 0) {
+      npr[j] = np;
+      ngt[j] = nbd[j] = 0;
+    }
+  }
+  __syncthreads();
+  // pairs beyond the LDS slice (tiles spanning many bins): one flat round
+  {
+    constexpr int PT = (TILE_MAX_PER_SEQ + SEL_THREADS - 1) / SEL_THREADS;
+    uint32_t o_[PT], so = 0;
+#pragma unroll
+    for (int r = 0; r < PT; ++r) {
+      int j = tid * PT + r;
+      o_[r] = j < nt && npr[j] > (uint32_t)per ? npr[j] - per : 0u;
+      so += o_[r];
+    }
+    uint32_t tot;
+    uint32_t e = block_exclusive_scan(so, scr, &tot);
+#pragma unroll
+    for (int r = 0; r < PT; ++r) {
+      int j = tid * PT + r;
+      if (j < nt) ovf_off[j] = e;
+      e += o_[r];
+    }
+    if (tid == 0) ovf_off[nt] = tot;
+  }
+  __syncthreads();
+  const uint32_t novf = ovf_off[nt];
+  auto ovf_pair = [&](uint32_t i) -> uint32_t {
+    int j = owner_of(ovf_off, nt, i);
+    return P.tile_pairs[(size_t)(t0 + j) * PAIR_CAP + per + (i - ovf_off[j])];
+  };
+  for (uint32_t i = tid; i < novf; i += SEL_THREADS) {
+    uint32_t w = ovf_pair(i);
+    atomicAdd(&hist[w >> 16], w & 0xFFFFu);
+  }
   __syncthreads();
   int bstar;
   uint32_t n_gt, total;
   find_boundary(hist, K, &bstar, &n_gt, &total, scr);
-  // bstar >= 0 here: the tiles together emitted at least k candidates.
+  // bstar >= 0: the tiles together kept at least k candidates.
   const uint32_t m = K - n_gt;
-
-  // per tile: [0, ngt_j) above bstar, [ngt_j, nge_j) in bstar (lists are bin-descending)
-  uint32_t* sure_off = toff;                          // [ntiles + 1]
-  uint32_t* bnd_off = toff + (TILE_MAX_PER_SEQ + 1);  // [ntiles + 1]
+  // 2. per tile: candidates above the boundary bin and in it
+  for (int u = tid; u < nt * per; u += SEL_THREADS) {
+    const int j = u / per, p = u % per;
+    if ((uint32_t)p >= npr[j]) continue;
+    const uint32_t w = lpairs[u];
+    const int bin = (int)(w >> 16);
+    if (bin > bstar) atomicAdd(&ngt[j], w & 0xFFFFu);
+    else if (bin == bstar) nbd[j] = w & 0xFFFFu;
+  }
+  for (uint32_t i = tid; i < novf; i += SEL_THREADS) {
+    const int j = owner_of(ovf_off, nt, i);
+    const uint32_t w = P.tile_pairs[(size_t)(t0 + j) * PAIR_CAP + per + (i - ovf_off[j])];
+    const int bin = (int)(w >> 16);
+    if (bin > bstar) atomicAdd(&ngt[j], w & 0xFFFFu);
+    else if (bin == bstar) nbd[j] = w & 0xFFFFu;
+  }
+  __syncthreads();
   {
-    constexpr int PT = (TILE_MAX_PER_SEQ + DEC_THREADS - 1) / DEC_THREADS;
-    uint32_t ngt[PT], nbd[PT];
-    uint32_t my_gt = 0, my_bd = 0;
+    constexpr int PT = (TILE_MAX_PER_SEQ + SEL_THREADS - 1) / SEL_THREADS;
+    uint32_t g_[PT], d_[PT], sg = 0, sd = 0;
 #pragma unroll
     for (int r = 0; r < PT; ++r) {
       int j = tid * PT + r;
-      ngt[r] = nbd[r] = 0;
-      if (j < ntiles) {
-        const uint64_t* lj = P.tile_list + (size_t)(t0 + j) * TILE_G;
-        uint32_t cnt = P.tile_cnt[t0 + j];
-        // first position whose bin <= bstar, then first whose bin < bstar
-        uint32_t lo = 0, hi2 = cnt;
-        while (lo < hi2) {
-          uint32_t mid = (lo + hi2) >> 1;
-          if (score_bin(key_score(lj[mid])) > bstar) lo = mid + 1; else hi2 = mid;
-        }
-        uint32_t a0 = lo;
-        hi2 = cnt;
-        while (lo < hi2) {
-          uint32_t mid = (lo + hi2) >> 1;
-          if (score_bin(key_score(lj[mid])) >= bstar) lo = mid + 1; else hi2 = mid;
-        }
-        ngt[r] = a0;
-        nbd[r] = lo - a0;
-      }
-      my_gt += ngt[r];
-      my_bd += nbd[r];
+      g_[r] = j < nt ? ngt[j] : 0u;
+      d_[r] = j < nt ? nbd[j] : 0u;
+      sg += g_[r];
+      sd += d_[r];
     }
     uint32_t tg, tb;
-    uint32_t eg = block_exclusive_scan(my_gt, scr, &tg);
-    uint32_t eb = block_exclusive_scan(my_bd, scr, &tb);
+    uint32_t eg = block_exclusive_scan(sg, scr, &tg);
+    uint32_t eb = block_exclusive_scan(sd, scr, &tb);
 #pragma unroll
     for (int r = 0; r < PT; ++r) {
       int j = tid * PT + r;
-      if (j < ntiles) {
+      if (j < nt) {
         sure_off[j] = eg;
         bnd_off[j] = eb;
       }
-      eg += ngt[r];
-      eb += nbd[r];
+      eg += g_[r];
+      eb += d_[r];
     }
     if (tid == 0) {
-      sure_off[ntiles] = tg;
-      bnd_off[ntiles] = tb;
+      sure_off[nt] = tg;
+      bnd_off[nt] = tb;
     }
   }
   __syncthreads();
-  const uint32_t nsure = sure_off[ntiles];
-  const uint32_t nbnd = bnd_off[ntiles];
-  auto owner = [&](const uint32_t* off, uint32_t i) -> int {  // tile j with off[j] <= i < off[j+1]
-    int lo = 0, hi2 = ntiles - 1;
-    while (lo < hi2) {
-      int mid = (lo + hi2 + 1) >> 1;
-      if (off[mid] <= i) lo = mid; else hi2 = mid - 1;
-    }
-    return lo;
-  };
-  // sure candidates -> sel[0, nsure)
-  for (uint32_t i = tid; i < nsure && i < MAX_K; i += DEC_THREADS) {
-    int j = owner(sure_off, i);
+  // 3. gather
+  const uint32_t nsure = sure_off[nt];
+  const uint32_t nbnd = bnd_off[nt];
+  for (uint32_t i = tid; i < nsure && i < MAX_K; i += SEL_THREADS) {
+    int j = owner_of(sure_off, nt, i);
     sel[i] = (uint32_t)P.tile_list[(size_t)(t0 + j) * TILE_G + (i - sure_off[j])];
   }
-  // boundary candidates
   auto bnd_key = [&](uint32_t i) -> uint64_t {
-    int j = owner(bnd_off, i);
-    // position inside tile j: after its sure part
-    uint32_t ngt_j = sure_off[j + 1] - sure_off[j];
-    uint64_t e = P.tile_list[(size_t)(t0 + j) * TILE_G + ngt_j + (i - bnd_off[j])];
+    int j = owner_of(bnd_off, nt, i);
+    uint64_t e = P.tile_list[(size_t)(t0 + j) * TILE_G + ngt[j] + (i - bnd_off[j])];
     return rank_key(key_score(e), (uint32_t)e);
   };
-  uint64_t* cand = reinterpret_cast<uint64_t*>(sc);  // TILE_G words = CAND_LDS u64
-  const bool in_lds = nbnd <= CAND_LDS;
+  const bool in_lds = nbnd <= SEL_CAND;
   if (in_lds)
-    for (uint32_t i = tid; i < nbnd; i += DEC_THREADS) cand[i] = bnd_key(i);
+    for (uint32_t i = tid; i < nbnd; i += SEL_THREADS) cand[i] = bnd_key(i);
   __syncthreads();
-  uint64_t thr;
+  // 4. the m best boundary candidates
   if (in_lds) {
-    thr = radix_select_threshold(
-        [&](auto f) {
-          for (uint32_t i = tid; i < nbnd; i += DEC_THREADS) f(cand[i]);
-        },
-        m, h256, scr);
+    for (uint32_t i = tid; i < nbnd; i += SEL_THREADS) {
+      const uint64_t ki = cand[i];
+      uint32_t rank = 0;
+      for (uint32_t j = 0; j < nbnd; ++j) rank += cand[j] > ki;
+      if (rank < m) sel[nsure + rank] = key_id(ki);
+    }
   } else {
-    thr = radix_select_threshold(
+    const uint64_t thr = radix_select_threshold(
         [&](auto f) {
-          for (uint32_t i = tid; i < nbnd; i += DEC_THREADS) f(bnd_key(i));
+          for (uint32_t i = tid; i < nbnd; i += SEL_THREADS) f(bnd_key(i));
         },
         m, h256, scr);
-  }
-  if (tid == 0) scr[SCR_RES + 9] = 0;
-  __syncthreads();
-  for (uint32_t i = tid; i < nbnd; i += DEC_THREADS) {
-    uint64_t key = in_lds ? cand[i] : bnd_key(i);
-    if (key >= thr) {
-      uint32_t p = nsure + atomicAdd(&scr[SCR_RES + 9], 1u);
-      if (p < MAX_K) sel[p] = key_id(key);
+    if (tid == 0) scr[SCR_RES + 9] = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < nbnd; i += SEL_THREADS) {
+      uint64_t key = bnd_key(i);
+      if (key >= thr) {
+        uint32_t p = nsure + atomicAdd(&scr[SCR_RES + 9], 1u);
+        if (p < MAX_K) sel[p] = key_id(key);
+      }
     }
   }
   __syncthreads();
-  write_sorted_row(sel, (int)K, (int)K, P.out_idx + (size_t)b * K, P.out_count + b);
+  // ascending order by counting (ids are distinct)
+  int32_t* orow = P.out_idx + (size_t)b * K;
+  for (uint32_t i = tid; i < K; i += SEL_THREADS) {
+    const uint32_t v = sel[i];
+    uint32_t pos = 0;
+    for (uint32_t j = 0; j < K; ++j) pos += sel[j] < v;
+    orow[pos] = (int32_t)v;
+  }
+  if (tid == 0) P.out_count[b] = (int32_t)K;
 }
 
 isa_status launch_indexer_decode(const BatchArgs& a, const int8_t* q, const int8_t* hw, const int8_t* pooled,
                                  const int32_t* bt, const DecodeWs& w, int32_t* out_idx, int32_t* out_count,
                                  int32_t* scores_out, int32_t ld_scores, hipStream_t stream) {
-  DecodePtrs P{q, hw, pooled, bt, w.ghist, w.tickets, w.tile_cnt, w.tile_list, out_idx, out_count,
-               scores_out, ld_scores, w.err};
-  int ntiles = a.tile_start[a.batch];
-  hipLaunchKernelGGL(k_indexer_decode, dim3(ntiles), dim3(DEC_THREADS), 0, stream, a, P);
-  return hipGetLastError() == hipSuccess ? ISA_OK : ISA_ERR_HIP;
+  DecodePtrs P{q, hw, pooled, bt, w.tile_meta, w.tile_pairs, w.tile_list, out_idx, out_count, scores_out,
+               ld_scores, w.err};
+  const int ntiles = a.tile_start[a.batch];
+  hipLaunchKernelGGL(k_indexer_score, dim3(ntiles), dim3(DEC_THREADS), 0, stream, a, P);
+  if (hipGetLastError() != hipSuccess) return ISA_ERR_HIP;
+  bool any_sparse = false;
+  for (int b = 0; b < a.batch; ++b) any_sparse |= (a.lens[b] + GROUP - 1) / GROUP > a.k;
+  if (any_sparse) {
+    hipLaunchKernelGGL(k_indexer_select, dim3(a.batch), dim3(SEL_THREADS), 0, stream, a, P);
+    if (hipGetLastError() != hipSuccess) return ISA_ERR_HIP;
+  }
+  return ISA_OK;
 }
 
 }  // namespace isa

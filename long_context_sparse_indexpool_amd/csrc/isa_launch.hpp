@@ -8,13 +8,14 @@ namespace isa {
 constexpr int TILE_G = 2048;  // pooled groups per decode work tile (32 pages)
 constexpr int TILE_MAX_PER_SEQ = (ISA_MAX_SEQ_LEN / GROUP + TILE_G - 1) / TILE_G;
 
+constexpr int PAIR_CAP = NBINS;  // (bin, count) pairs a decode tile can emit
+
 // Decode indexer workspace (pointers into the caller's workspace).
 struct DecodeWs {
   uint32_t* err;
-  uint32_t* ghist;
-  uint32_t* tickets;
-  uint32_t* tile_cnt;
-  uint64_t* tile_list;
+  uint2* tile_meta;      // [ntiles] (candidates kept, pairs)
+  uint32_t* tile_pairs;  // [ntiles][PAIR_CAP]
+  uint64_t* tile_list;   // [ntiles][TILE_G]
 };
 
 isa_status launch_indexer_decode(const BatchArgs& a, const int8_t* q, const int8_t* hw, const int8_t* pooled,

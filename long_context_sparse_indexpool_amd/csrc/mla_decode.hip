@@ -11,36 +11,44 @@
 // "의견이 갈리는 지점 — 위치 인코딩": qk_rope_head_dim = 0, so no rotary part.  The
 // absorbed form is used: keys = values = the 512-d latent row.
 //
-// Design.  A workgroup is (query row, token split) with four waves; wave w owns
-// heads 16w..16w+15 and the whole split, in tiles of 32 tokens (8 groups).
-// Per tile:
-//  * Scores as S^T = C Q^T with v_mfma_f32_16x16x32_bf16: tokens are M, the
-//    wave's 16 heads are N, the 512 channels the K loop.  Each lane loads 16
-//    contiguous bytes of a latent row per K step straight from HBM (the rows
-//    of a group are contiguous in a page); the query operand stays in
-//    registers.  Computing S^T makes each lane hold 8 probabilities of one
-//    head, which is exactly the A operand layout the PV product needs.
-//  * While loading, wave w converts channels 128w..128w+127 of the tile to fp16
-//    (exact for bf16 values in fp16 range) and stores them transposed into LDS
-//    (V^T, rows padded to 80 B against bank conflicts), in the token order the
-//    probability operand uses.
-//  * Online softmax in fp32 (base 2; the running max per head is reduced across
-//    the four lanes holding it; the output rescale is skipped when no head of
-//    the wave raised its max).
-//  * O += P V with v_mfma_f32_16x16x32_f16: heads as M, 16 channels per N block,
-//    the 32 tokens as K; V^T comes from LDS with one 16-byte read per MFMA.
+// Design.  A workgroup is (query row, token split) with eight waves: wave w owns
+// heads 16(w%4)..+15 and latent channels 256(w/4)..+255, so each wave's output
+// accumulator is 16 heads x 256 channels (64 registers per lane).  The split's
+// selected groups are first turned into a table of physical latent rows (one
+// block-table lookup per group).  Then, per tile of 16 tokens:
+//  * Partial scores S^T = C Q^T over the wave's 256 channels with
+//    v_mfma_f32_16x16x32_bf16: tokens are M, the wave's 16 heads are N.  Each
+//    lane loads 16 contiguous bytes of a latent row per K step straight from
+//    HBM into a ring of register slots; a slot is refilled with the next tile's
+//    K step as soon as it is consumed, so a whole tile of loads is in flight.
+//    The two waves sharing a head block add their halves through LDS (both
+//    then hold identical scores and make identical softmax decisions).
+//  * Each wave also converts one eighth of the tile's channels to fp16 (exact
+//    for bf16 values inside the fp16 range) and stores them transposed in LDS
+//    (V^T).  Computing S^T leaves every lane with four probabilities of one
+//    head in exactly the A-operand layout the P.V product needs.
+//  * Softmax in fp32, base 2.  The exponent reference of a head moves only when
+//    its running max exceeds it by more than 8 (so p <= 256 in fp16), which
+//    makes the rescale of the output accumulator rare.
+//  * O += P V with v_mfma_f32_16x16x16f16: heads are M, 16 channels per N
+//    block, the 16 tokens are K; V^T comes from LDS with one 8-byte read.
 // With one split the workgroup normalises and writes the output; otherwise it
-// writes its unnormalised partial (O, max, sum) and a combine kernel merges
+// writes its unnormalised partial (O, reference, sum) and k_mla_combine merges
 // the splits by log-sum-exp weights.
 #include "isa_launch.hpp"
 
 namespace isa {
 
-constexpr int MLA_THREADS = 256;
-constexpr int TILE_TOK = 32;
+constexpr int MLA_THREADS = 512;  // 8 waves: 4 head blocks x 2 channel halves
+constexpr int HALF_DIM = LAT_DIM / 2;
+constexpr int KSTEPS = HALF_DIM / 32;  // K steps of the score product per wave
+constexpr int NBLK = HALF_DIM / 16;    // 16-channel blocks of the output per wave
+constexpr float RESCALE_LOG2 = 8.f;
+constexpr int TILE_TOK = 16;
 constexpr int TILE_GRP = TILE_TOK / GROUP;
-constexpr int VT_STRIDE = 40;  // halves per V^T row (32 tokens + 8 pad)
+constexpr int VT_STRIDE = 20;  // halves per V^T row (16 tokens + 4 pad)
 constexpr int MAX_GPS = MAX_K; // groups per split held in LDS
+constexpr int MAX_SPLITS = 16;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -63,15 +71,14 @@ struct MlaPtrs {
   int32_t gps;  // groups per split
 };
 
-// token slot inside the 32-token K block, as laid out by the S^T accumulators
-__device__ __forceinline__ int kperm(int t) { return 8 * ((t & 15) >> 2) + (t & 3) + 4 * (t >> 4); }
-
 __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, const MlaPtrs P) {
-  __shared__ _Float16 vt[LAT_DIM * VT_STRIDE];  // 40 KiB
-  __shared__ int32_t sidx[MAX_GPS];
+  __shared__ _Float16 vt[LAT_DIM * VT_STRIDE];  // 20 KiB: V^T of one 16-token tile
+  __shared__ v4f sx[MLA_THREADS];               // 8 KiB: partial scores exchanged between wave pairs
+  __shared__ uint32_t trow[MAX_GPS * GROUP];    // latent row of each token slot, or ~0 if not visible
   __shared__ int32_t rowinfo[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hb = wave & 3, half = wave >> 2;  // heads 16hb.., channels 256half..
   const int r = blockIdx.x / P.splits;
   const int split = blockIdx.x % P.splits;
   const int lq = lane & 15, lg = lane >> 4;  // column / row-group of the 16x16 layouts
@@ -97,131 +104,122 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
   const int jbeg = min(cnt, split * P.gps);
   const int jend = min(cnt, jbeg + P.gps);
   const int ng = jend - jbeg;
+  // token table of the split: one block-table lookup per selected group
   for (int j = tid; j < ng; j += MLA_THREADS) {
     int g = P.idx[(size_t)r * P.k + jbeg + j];
-    if (g < 0 || g >= G) {
-      report(P.err, ISA_DERR_ROW_RANGE);
-      g = -1;
+    int pg = -1;
+    if (g < 0 || g >= G) report(P.err, ISA_DERR_ROW_RANGE);
+    else pg = phys_page(P.bt, a.max_pages, a.num_pages, seq, (g * GROUP) / PAGE_TOK, P.err);
+#pragma unroll
+    for (int i = 0; i < GROUP; ++i) {
+      int tok = g * GROUP + i;
+      bool vis = pg >= 0 && tok < L && tok <= pos;
+      trow[j * GROUP + i] = vis ? (uint32_t)pg * PAGE_TOK + (uint32_t)(tok % PAGE_TOK) : 0xFFFFFFFFu;
     }
-    sidx[j] = g;
   }
 
-  // query operand (B = Q^T): lane -> head 16w + lq, channels 32c + 8lg .. +7
-  v8bf qop[16];
+  // query operand (B = Q^T): lane -> head 16hb + lq, channels 256half + 32c + 8lg .. +7
+  v8bf qop[KSTEPS];
   {
-    const uint16_t* qp = P.q + ((size_t)r * ATT_HEADS + wave * 16 + lq) * LAT_DIM + lg * 8;
+    const uint16_t* qp = P.q + ((size_t)r * ATT_HEADS + hb * 16 + lq) * LAT_DIM + half * HALF_DIM + lg * 8;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
+    for (int c = 0; c < KSTEPS; ++c) {
       v4i v = *reinterpret_cast<const v4i*>(qp + c * 32);
       qop[c] = __builtin_bit_cast(v8bf, v);
     }
   }
-  v4f o[32];
+  v4f o[NBLK];
 #pragma unroll
-  for (int nb = 0; nb < 32; ++nb) o[nb] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int nb = 0; nb < NBLK; ++nb) o[nb] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY, l_run = 0.f;  // exponent reference (log2 units) and partial sum of the head
   __syncthreads();
 
-  const int ntile = (ng + TILE_GRP - 1) / TILE_GRP;
+  const int nslot = ng * GROUP;
+  const int ntile = (nslot + TILE_TOK - 1) / TILE_TOK;
+  // QK operand of a tile: token row lq, channels 256half + 32c + 8lg .. +7.  One
+  // register slot per K step; each slot is refilled with the next tile's K step
+  // as soon as it has been consumed, so a whole tile of loads stays in flight.
+  auto row_of = [&](int tile) -> const v4i* {
+    int slot = tile * TILE_TOK + lq;
+    uint32_t row = (tile < ntile && slot < nslot) ? trow[slot] : 0xFFFFFFFFu;
+    return row != 0xFFFFFFFFu
+               ? reinterpret_cast<const v4i*>(P.latent + (size_t)row * LAT_DIM + half * HALF_DIM + lg * 8)
+               : nullptr;
+  };
+  v4i buf[KSTEPS];
+  {
+    const v4i* src = row_of(0);
+#pragma unroll
+    for (int c = 0; c < KSTEPS; ++c) buf[c] = src ? src[c * 4] : v4i{0, 0, 0, 0};
+  }
   for (int tile = 0; tile < ntile; ++tile) {
-    const int jt = tile * TILE_GRP;
-    // rows this lane loads: tokens t = lq (+16): group slot t/4, token 4g + t%4
-    const uint16_t* src[2];
+    const v4i* nsrc = row_of(tile + 1);
+    v4f sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int bk = 0; bk < 2; ++bk) {
-      int t = bk * 16 + lq;
-      int js = jt + (t >> 2);
-      src[bk] = nullptr;
-      if (js < ng) {
-        int g = sidx[js];
-        int tok = 4 * g + (t & 3);
-        if (g >= 0 && tok < L && tok <= pos) {
-          int pg = phys_page(P.bt, a.max_pages, a.num_pages, seq, tok / PAGE_TOK, P.err);
-          if (pg >= 0) src[bk] = P.latent + ((size_t)pg * PAGE_TOK + (tok % PAGE_TOK)) * LAT_DIM + lg * 8;
-        }
-      }
-    }
-    // S^T = C Q^T over 16 K steps of 32 channels
-    v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      v4i r0 = src[0] ? *reinterpret_cast<const v4i*>(src[0] + c * 32) : v4i{0, 0, 0, 0};
-      v4i r1 = src[1] ? *reinterpret_cast<const v4i*>(src[1] + c * 32) : v4i{0, 0, 0, 0};
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, r0), qop[c], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, r1), qop[c], s1, 0, 0, 0);
-      if ((c >> 2) == wave) {  // this wave's quarter of V^T
-        const int d0 = c * 32 + lg * 8;
-        const int k0 = kperm(lq), k1 = kperm(16 + lq);
-        const uint32_t w0[4] = {(uint32_t)r0.x, (uint32_t)r0.y, (uint32_t)r0.z, (uint32_t)r0.w};
-        const uint32_t w1[4] = {(uint32_t)r1.x, (uint32_t)r1.y, (uint32_t)r1.z, (uint32_t)r1.w};
+    for (int c = 0; c < KSTEPS; ++c) {
+      const v4i rr = buf[c];
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, rr), qop[c], sacc, 0, 0, 0);
+      if ((c >> 1) == hb) {  // this wave's eighth of V^T: token lq, channels 256half + 32c + 8lg .. +7
+        const int d0 = half * HALF_DIM + c * 32 + lg * 8;
+        const uint32_t w[4] = {(uint32_t)rr.x, (uint32_t)rr.y, (uint32_t)rr.z, (uint32_t)rr.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          vt[(d0 + 2 * i) * VT_STRIDE + k0] = (_Float16)__uint_as_float(w0[i] << 16);
-          vt[(d0 + 2 * i + 1) * VT_STRIDE + k0] = (_Float16)__uint_as_float(w0[i] & 0xFFFF0000u);
-          vt[(d0 + 2 * i) * VT_STRIDE + k1] = (_Float16)__uint_as_float(w1[i] << 16);
-          vt[(d0 + 2 * i + 1) * VT_STRIDE + k1] = (_Float16)__uint_as_float(w1[i] & 0xFFFF0000u);
+          vt[(d0 + 2 * i) * VT_STRIDE + lq] = (_Float16)__uint_as_float(w[i] << 16);
+          vt[(d0 + 2 * i + 1) * VT_STRIDE + lq] = (_Float16)__uint_as_float(w[i] & 0xFFFF0000u);
         }
       }
+      buf[c] = nsrc ? nsrc[c * 4] : v4i{0, 0, 0, 0};
     }
-    // visibility of the accumulator tokens: t = 16bk + 4lg + i -> group slot 4bk + lg
-    float x[8];
+    sx[tid] = sacc;
+    __syncthreads();  // V^T and the partial scores complete
+    const v4f other = sx[tid ^ (4 * 64)];  // same heads, the other channel half
+    // the accumulator holds head lq of tokens 4lg + i
+    float x[4];
 #pragma unroll
-    for (int bk = 0; bk < 2; ++bk) {
-      int js = jt + 4 * bk + lg;
-      int g = js < ng ? sidx[js] : -1;
-      v4f s = bk ? s1 : s0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int tok = 4 * g + i;
-        bool vis = g >= 0 && tok < L && tok <= pos;
-        x[bk * 4 + i] = vis ? s[i] * P.c2 : -INFINITY;
-      }
+    for (int i = 0; i < 4; ++i) {
+      int slot = tile * TILE_TOK + 4 * lg + i;
+      bool vis = slot < nslot && trow[slot] != 0xFFFFFFFFu;
+      x[i] = vis ? (sacc[i] + other[i]) * P.c2 : -INFINITY;
     }
-    float mt = x[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mt = fmaxf(mt, x[i]);
+    float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);
-    float alpha = 1.f;
-    v8h pop;
-    if (m_new == -INFINITY) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pop[i] = (_Float16)0.f;
-    } else {
-      alpha = exp2f(m_run - m_new);
-      float ps = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float p = exp2f(x[i] - m_new);
-        ps += p;
-        pop[i] = (_Float16)p;
-      }
-      l_run = l_run * alpha + ps;
-      m_run = m_new;
-    }
-    if (!__all(alpha == 1.f)) {
+    // move the reference only when some head's max got 2^8 above it: p stays <= 256
+    if (__any(mt > m_ref + RESCALE_LOG2)) {
+      const float m_new = fmaxf(m_ref, mt);
+      const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_ref - m_new);
+      l_run *= alpha;
+      m_ref = m_new;
       float al[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * lg + i, 64);
 #pragma unroll
-      for (int nb = 0; nb < 32; ++nb)
+      for (int nb = 0; nb < NBLK; ++nb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[nb][i] *= al[i];
     }
-    __syncthreads();  // V^T complete
+    v4h pop;
+    float ps = 0.f;
 #pragma unroll
-    for (int nb = 0; nb < 32; ++nb) {
-      const v4i v = *reinterpret_cast<const v4i*>(&vt[(nb * 16 + lq) * VT_STRIDE + lg * 8]);
-      o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, __builtin_bit_cast(v8h, v), o[nb], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      float p = m_ref == -INFINITY ? 0.f : exp2f(x[i] - m_ref);
+      ps += p;
+      pop[i] = (_Float16)p;
     }
-    __syncthreads();  // V^T free for the next tile
+    l_run += ps;
+#pragma unroll
+    for (int nb = 0; nb < NBLK; ++nb) {
+      const v2i v = *reinterpret_cast<const v2i*>(&vt[(half * HALF_DIM + nb * 16 + lq) * VT_STRIDE + lg * 4]);
+      o[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pop, __builtin_bit_cast(v4h, v), o[nb], 0, 0, 0);
+    }
+    __syncthreads();  // V^T and sx free for the next tile
   }
 
   // per-head sum over the four lanes holding the head
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
-  const int h0 = wave * 16;
+  const int h0 = hb * 16;
+  const int d_base = half * HALF_DIM;
   if (P.splits == 1) {
     float inv[4];
 #pragma unroll
@@ -231,63 +229,74 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
     }
     float* orow = P.out + (size_t)r * ATT_HEADS * LAT_DIM;
 #pragma unroll
-    for (int nb = 0; nb < 32; ++nb)
+    for (int nb = 0; nb < NBLK; ++nb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) orow[(size_t)(h0 + 4 * lg + i) * LAT_DIM + nb * 16 + lq] = o[nb][i] * inv[i];
-    if (P.lse && lane < 16)
-      P.lse[(size_t)r * ATT_HEADS + h0 + lq] = l_tot > 0.f ? m_run * LN2 + logf(l_tot) : -INFINITY;
+      for (int i = 0; i < 4; ++i)
+        orow[(size_t)(h0 + 4 * lg + i) * LAT_DIM + d_base + nb * 16 + lq] = o[nb][i] * inv[i];
+    if (P.lse && half == 0 && lane < 16)
+      P.lse[(size_t)r * ATT_HEADS + h0 + lq] = l_tot > 0.f ? m_ref * LN2 + logf(l_tot) : -INFINITY;
   } else {
     float* op = P.o_part + ((size_t)r * P.splits + split) * ATT_HEADS * LAT_DIM;
 #pragma unroll
-    for (int nb = 0; nb < 32; ++nb)
+    for (int nb = 0; nb < NBLK; ++nb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) op[(size_t)(h0 + 4 * lg + i) * LAT_DIM + nb * 16 + lq] = o[nb][i];
-    if (lane < 16) {
+      for (int i = 0; i < 4; ++i) op[(size_t)(h0 + 4 * lg + i) * LAT_DIM + d_base + nb * 16 + lq] = o[nb][i];
+    if (half == 0 && lane < 16) {
       float* mp = P.ml_part + (((size_t)r * P.splits + split) * ATT_HEADS + h0 + lq) * 2;
-      mp[0] = m_run;
+      mp[0] = l_tot > 0.f ? m_ref : -INFINITY;
       mp[1] = l_tot;
     }
   }
 }
 
-// Merge the splits of one (row, head): 128 threads x 4 channels.
+// Merge the splits of one (row, head): weights 2^(m_s - M), then a weighted
+// sum of the partial outputs (128 threads x 4 channels, loads unrolled).
 __global__ __launch_bounds__(128) void k_mla_combine(const MlaPtrs P) {
+  __shared__ float wsh[MAX_SPLITS];
+  __shared__ float stat[2];
   const int r = blockIdx.x / ATT_HEADS, h = blockIdx.x % ATT_HEADS;
   const int S = P.splits;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, P.ml_part[(((size_t)r * S + s) * ATT_HEADS + h) * 2]);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float wsum = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const float* mp = P.ml_part + (((size_t)r * S + s) * ATT_HEADS + h) * 2;
-      float f = exp2f(mp[0] - M);
-      wsum += f * mp[1];
-      float4 v = *reinterpret_cast<const float4*>(P.o_part + (((size_t)r * S + s) * ATT_HEADS + h) * LAT_DIM +
-                                                  threadIdx.x * 4);
-      acc.x = fmaf(f, v.x, acc.x);
-      acc.y = fmaf(f, v.y, acc.y);
-      acc.z = fmaf(f, v.z, acc.z);
-      acc.w = fmaf(f, v.w, acc.w);
+  const float* ml = P.ml_part + ((size_t)r * S * ATT_HEADS + h) * 2;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    float m = lane < S ? ml[(size_t)lane * ATT_HEADS * 2] : -INFINITY;
+    float l = lane < S ? ml[(size_t)lane * ATT_HEADS * 2 + 1] : 0.f;
+    float M = m;
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    float w = (M == -INFINITY || m == -INFINITY) ? 0.f : exp2f(m - M);
+    float ws = w * l;
+    for (int o = 32; o > 0; o >>= 1) ws += __shfl_xor(ws, o, 64);
+    if (lane < S) wsh[lane] = ws > 0.f ? w / ws : 0.f;
+    if (lane == 0) {
+      stat[0] = M;
+      stat[1] = ws;
     }
   }
-  float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  acc.x *= inv;
-  acc.y *= inv;
-  acc.z *= inv;
-  acc.w *= inv;
+  __syncthreads();
+  const float* op = P.o_part + ((size_t)r * S * ATT_HEADS + h) * LAT_DIM + threadIdx.x * 4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+  for (int s = 0; s < S; ++s) {
+    float f = wsh[s];
+    float4 v = *reinterpret_cast<const float4*>(op + (size_t)s * ATT_HEADS * LAT_DIM);
+    acc.x = fmaf(f, v.x, acc.x);
+    acc.y = fmaf(f, v.y, acc.y);
+    acc.z = fmaf(f, v.z, acc.z);
+    acc.w = fmaf(f, v.w, acc.w);
+  }
   *reinterpret_cast<float4*>(P.out + ((size_t)r * ATT_HEADS + h) * LAT_DIM + threadIdx.x * 4) = acc;
   if (P.lse && threadIdx.x == 0)
-    P.lse[(size_t)r * ATT_HEADS + h] = wsum > 0.f ? M * LN2 + logf(wsum) : -INFINITY;
+    P.lse[(size_t)r * ATT_HEADS + h] = stat[1] > 0.f ? stat[0] * LN2 + logf(stat[1]) : -INFINITY;
 }
 
 MlaPlan plan_mla(int32_t rows, int32_t k) {
+  // about 256 workgroups in flight, at least 16 groups (64 tokens) per split
   MlaPlan p;
   p.rows = rows;
-  int s = (512 + rows - 1) / rows;
-  int smax = (k + 15) / 16;  // at least 16 groups (64 tokens) per split
+  int s = (256 + rows - 1) / rows;
+  int smax = (k + 15) / 16;
   if (s > smax) s = smax;
-  if (s > 32) s = 32;
+  if (s > MAX_SPLITS) s = MAX_SPLITS;
   if (s < 1) s = 1;
   p.splits = s;
   p.groups_per_split = (k + s - 1) / s;
