@@ -13,8 +13,8 @@
 // 8-XCD part a device-scope fence writes back the whole L2, which cost more
 // than the streaming itself; the kernel boundary gives coherence for free).
 //
-// k_indexer_score: one workgroup per work tile of 2048 pooled groups (32
-// pages) of one sequence.  Its four waves stream the tile's int8 keys straight
+// k_indexer_score: one workgroup per work tile of 4096 pooled groups (64
+// pages) of one sequence.  Its eight waves stream the tile's int8 keys straight
 // from HBM into v_mfma_i32_32x32x32_i8 operands -- the 32 indexer heads are M
 // (the query stays in registers), 32 groups are N, four MFMAs span the 128
 // channels, each lane loading 64 contiguous bytes of one key, two steps of
@@ -34,12 +34,15 @@
 
 namespace isa {
 
-constexpr int DEC_THREADS = 256;
-constexpr int DEC_STEPS = TILE_G / 128;  // 4 waves x 32 groups per step
+constexpr int DEC_THREADS = 512;
+constexpr int DEC_GPS = DEC_THREADS / 2;      // groups per step: 32 per wave
+constexpr int DEC_STEPS = TILE_G / DEC_GPS;
 constexpr int DEC_PF = 2;                // steps of key loads in flight per wave
 constexpr int SEL_THREADS = 512;
 constexpr int SEL_CAND = 2048;           // boundary candidates resolved in LDS
-constexpr int SEL_LDS_PAIRS = 16384;     // (bin, count) pairs fetched into LDS in the first round
+constexpr int SEL_LDS_PAIRS = 8192;      // (bin, count) pairs fetched into LDS in the first round
+constexpr int SEL_LDS_HEAD = 4096;       // candidate-list entries fetched into LDS in the first round
+constexpr int SEL_BUCKETS = 1024;        // id buckets of the final ascending order
 
 struct DecodePtrs {
   const int8_t* q;
@@ -111,8 +114,12 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
 
   // ---- stream the tile: 16 steps of 128 groups (32 per wave) ----
   const int8_t* kbase = P.pooled + (lane >> 5) * 64;
+  // Tiles walk their steps from different starting points, so that the
+  // workgroups streaming at the same moment do not all sit at the same offset
+  // of their (power-of-two spaced) tiles.
+  const int rot = tile % DEC_STEPS;
   auto load_step = [&](int step, v4i (&kb)[4]) {
-    int gl = step * 128 + wave * 32 + (lane & 31);
+    int gl = ((step + rot) % DEC_STEPS) * DEC_GPS + wave * 32 + (lane & 31);
     int pg = pages[gl / PAGE_GRP];
     if (gl < gN && pg >= 0) {
       const v4i* p = reinterpret_cast<const v4i*>(kbase + ((size_t)pg * PAGE_GRP + (gl % PAGE_GRP)) * IDX_DIM);
@@ -141,10 +148,11 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
 #pragma unroll
     for (int i = 0; i < 16; ++i) s += wv[i] * (uint32_t)max(acc[i], 0);  // ReLU <= 2,064,512 < 2^24
     s += __shfl_xor(s, 32, 64);
-    const int gl = step * 128 + wave * 32 + (lane & 31);
+    const int gl = ((step + rot) % DEC_STEPS) * DEC_GPS + wave * 32 + (lane & 31);
     if (lane < 32) {
       bool valid = gl < gN;
       sc[gl] = valid ? s : INVALID_SCORE;
+      if (valid && !dense) atomicAdd(&hist[score_bin(s)], 1u);  // histogram built while streaming
       overflow |= valid && s > 0x7FFFFFFFu;
       if (P.scores_out && valid) P.scores_out[(size_t)b * P.ld_scores + g0 + gl] = (int32_t)s;
     }
@@ -160,12 +168,6 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
 
   // ---- local candidates: every score in a bin >= the bin of this tile's k-th best ----
   constexpr int PER = TILE_G / DEC_THREADS;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    uint32_t s = sc[tid + j * DEC_THREADS];
-    if (s != INVALID_SCORE) atomicAdd(&hist[score_bin(s)], 1u);
-  }
-  __syncthreads();
   int bt_local;
   uint32_t n_gt_local, n_valid;
   find_boundary(hist, K, &bt_local, &n_gt_local, &n_valid, scr);
@@ -221,28 +223,35 @@ __device__ __forceinline__ int owner_of(const uint32_t* off, int n, uint32_t i) 
 }
 
 // Per sequence: merge the tiles' candidates into the exact top k.
-//  1. one round of loads: every tile's (kept, pairs) and its first SEL_PAIRS_PER
-//     (bin, count) pairs, summed into an LDS histogram (longer pair lists, which
-//     need a tile spanning hundreds of bins, take a second round);
-//  2. the global boundary bin and, per tile, how many candidates lie above it and
-//     in it (pair lists and candidate lists share the descending bin order);
-//  3. one round of loads gathers the candidates above the boundary and those in it;
-//  4. the boundary candidates are ranked by (score, -id) -- all-pairs counting in
-//     LDS, or radix select when there are too many -- and the k ids are placed in
-//     ascending order by counting, straight into the output row.
+//  1. one batch of loads, all issued before any is used: every tile's (kept,
+//     pairs), the head of its (bin, count) list and the head of its candidate
+//     list (both lists share the descending bin order); the pairs are summed
+//     into an LDS histogram.  Longer pair lists (a tile spread over many bins)
+//     take one more, flat, round;
+//  2. the global boundary bin and, per tile, how many candidates lie above it
+//     and in it;
+//  3. the candidates come from the LDS list heads (global memory only for a
+//     tile with more candidates than its head holds);
+//  4. the boundary candidates are ranked by (score, -id) -- all-pairs counting
+//     in LDS, or radix select when there are too many -- and the k ids are
+//     placed in ascending order by counting, straight into the output row.
 __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs a, const DecodePtrs P) {
   __shared__ uint32_t hist[NBINS];
   __shared__ uint32_t lpairs[SEL_LDS_PAIRS];
+  __shared__ uint64_t lhead[SEL_LDS_HEAD];
   __shared__ uint32_t npr[TILE_MAX_PER_SEQ];
   __shared__ uint32_t ovf_off[TILE_MAX_PER_SEQ + 1];
   __shared__ uint32_t sure_off[TILE_MAX_PER_SEQ + 1];
   __shared__ uint32_t bnd_off[TILE_MAX_PER_SEQ + 1];
   __shared__ uint32_t ngt[TILE_MAX_PER_SEQ];
   __shared__ uint32_t nbd[TILE_MAX_PER_SEQ];
-  __shared__ uint64_t cand[SEL_CAND];
+  __shared__ __attribute__((aligned(16))) uint64_t cand[SEL_CAND + 2];
   __shared__ uint32_t sel[MAX_K];
   __shared__ uint32_t h256[256];
   __shared__ uint32_t scr[SCR_WORDS];
+  __shared__ uint32_t bcnt[SEL_BUCKETS];
+  __shared__ uint32_t bbase[SEL_BUCKETS];
+  __shared__ uint32_t bstage[MAX_K];
 
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
@@ -251,60 +260,78 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
   if (G <= (int)K) return;  // dense row: written by the scoring kernel
   const int t0 = a.tile_start[b];
   const int nt = a.tile_start[b + 1] - t0;
-  // pairs of each tile fetched in the first round (a multiple of 4, at most 64)
-  const int per = min(64, (SEL_LDS_PAIRS / nt) & ~3);
+  const int per = min(64, (SEL_LDS_PAIRS / nt) & ~3);  // pairs of a tile kept in LDS
+  const int lh = min(64, (SEL_LDS_HEAD / nt) & ~1);    // candidates of a tile kept in LDS
+  const int pu_per_tile = per / 4, hu_per_tile = lh / 2;
 
-  for (int i = tid; i < NBINS; i += SEL_THREADS) hist[i] = 0;
-  __syncthreads();
-  // 1. metadata and the head of every pair list in one round
-  constexpr int CH = 4;  // pairs per load
-  for (int u = tid; u < nt * (per / CH); u += SEL_THREADS) {
-    const int j = u / (per / CH), part = u % (per / CH);
-    const uint32_t np = P.tile_meta[t0 + j].y;
-    const uint4 v = *reinterpret_cast<const uint4*>(P.tile_pairs + (size_t)(t0 + j) * PAIR_CAP + part * CH);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  // 1. one batch of loads
+  constexpr int UP = SEL_LDS_PAIRS / 4 / SEL_THREADS, UH = SEL_LDS_HEAD / 2 / SEL_THREADS;
+  uint4 pv[UP], hv[UH];
+  uint32_t pnp[UP];
 #pragma unroll
-    for (int e = 0; e < CH; ++e) {
-      const uint32_t p = part * CH + e;
-      if (p < np) {
-        lpairs[j * per + p] = w[e];
-        atomicAdd(&hist[w[e] >> 16], w[e] & 0xFFFFu);
-      }
-    }
-    if (part == 0) {
-      npr[j] = np;
-      ngt[j] = nbd[j] = 0;
+  for (int k = 0; k < UP; ++k) {
+    const int u = tid + k * SEL_THREADS;
+    pnp[k] = 0;
+    if (u < nt * pu_per_tile) {
+      const int j = u / pu_per_tile, part = u % pu_per_tile;
+      pnp[k] = P.tile_meta[t0 + j].y;
+      pv[k] = *reinterpret_cast<const uint4*>(P.tile_pairs + (size_t)(t0 + j) * PAIR_CAP + part * 4);
     }
   }
-  __syncthreads();
-  // pairs beyond the LDS slice (tiles spanning many bins): one flat round
-  {
-    constexpr int PT = (TILE_MAX_PER_SEQ + SEL_THREADS - 1) / SEL_THREADS;
-    uint32_t o_[PT], so = 0;
 #pragma unroll
-    for (int r = 0; r < PT; ++r) {
-      int j = tid * PT + r;
-      o_[r] = j < nt && npr[j] > (uint32_t)per ? npr[j] - per : 0u;
-      so += o_[r];
+  for (int k = 0; k < UH; ++k) {
+    const int u = tid + k * SEL_THREADS;
+    if (u < nt * hu_per_tile) {
+      const int j = u / hu_per_tile, part = u % hu_per_tile;
+      hv[k] = *reinterpret_cast<const uint4*>(P.tile_list + (size_t)(t0 + j) * TILE_G + part * 2);
+    }
+  }
+  uint32_t my_np = 0;
+  if (tid < nt) my_np = P.tile_meta[t0 + tid].y;
+  for (int i = tid; i < NBINS; i += SEL_THREADS) hist[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < UP; ++k) {
+    const int u = tid + k * SEL_THREADS;
+    if (u < nt * pu_per_tile) {
+      const int j = u / pu_per_tile, part = u % pu_per_tile;
+      const uint32_t w[4] = {pv[k].x, pv[k].y, pv[k].z, pv[k].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t p = part * 4 + e;
+        if (p < pnp[k]) {
+          lpairs[j * per + p] = w[e];
+          atomicAdd(&hist[w[e] >> 16], w[e] & 0xFFFFu);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < UH; ++k) {
+    const int u = tid + k * SEL_THREADS;
+    if (u < nt * hu_per_tile) {
+      const int j = u / hu_per_tile, part = u % hu_per_tile;
+      lhead[j * lh + part * 2] = ((uint64_t)hv[k].y << 32) | hv[k].x;
+      lhead[j * lh + part * 2 + 1] = ((uint64_t)hv[k].w << 32) | hv[k].z;
+    }
+  }
+  // pairs beyond the LDS slice: prefix over tiles, then one flat round
+  {
+    const uint32_t o = (tid < nt && my_np > (uint32_t)per) ? my_np - per : 0u;
+    if (tid < nt) {
+      npr[tid] = my_np;
+      ngt[tid] = nbd[tid] = 0;
     }
     uint32_t tot;
-    uint32_t e = block_exclusive_scan(so, scr, &tot);
-#pragma unroll
-    for (int r = 0; r < PT; ++r) {
-      int j = tid * PT + r;
-      if (j < nt) ovf_off[j] = e;
-      e += o_[r];
-    }
+    const uint32_t e = block_exclusive_scan(o, scr, &tot);
+    if (tid < nt) ovf_off[tid] = e;
     if (tid == 0) ovf_off[nt] = tot;
   }
   __syncthreads();
   const uint32_t novf = ovf_off[nt];
-  auto ovf_pair = [&](uint32_t i) -> uint32_t {
-    int j = owner_of(ovf_off, nt, i);
-    return P.tile_pairs[(size_t)(t0 + j) * PAIR_CAP + per + (i - ovf_off[j])];
-  };
   for (uint32_t i = tid; i < novf; i += SEL_THREADS) {
-    uint32_t w = ovf_pair(i);
+    const int j = owner_of(ovf_off, nt, i);
+    const uint32_t w = P.tile_pairs[(size_t)(t0 + j) * PAIR_CAP + per + (i - ovf_off[j])];
     atomicAdd(&hist[w >> 16], w & 0xFFFFu);
   }
   __syncthreads();
@@ -313,15 +340,22 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
   find_boundary(hist, K, &bstar, &n_gt, &total, scr);
   // bstar >= 0: the tiles together kept at least k candidates.
   const uint32_t m = K - n_gt;
-  // 2. per tile: candidates above the boundary bin and in it
-  for (int u = tid; u < nt * per; u += SEL_THREADS) {
-    const int j = u / per, p = u % per;
-    if ((uint32_t)p >= npr[j]) continue;
-    const uint32_t w = lpairs[u];
-    const int bin = (int)(w >> 16);
-    if (bin > bstar) atomicAdd(&ngt[j], w & 0xFFFFu);
-    else if (bin == bstar) nbd[j] = w & 0xFFFFu;
+  // 2. per tile: candidates above the boundary bin and in it (one thread walks
+  //    its tile's pairs, highest bin first, and stops below the boundary)
+  if (tid < nt) {
+    const uint32_t np = min(npr[tid], (uint32_t)per);
+    uint32_t g_ = 0, d_ = 0;
+    for (uint32_t p = 0; p < np; ++p) {
+      const uint32_t w = lpairs[tid * per + p];
+      const int bin = (int)(w >> 16);
+      if (bin < bstar) break;
+      if (bin > bstar) g_ += w & 0xFFFFu;
+      else d_ = w & 0xFFFFu;
+    }
+    ngt[tid] = g_;
+    nbd[tid] = d_;
   }
+  __syncthreads();
   for (uint32_t i = tid; i < novf; i += SEL_THREADS) {
     const int j = owner_of(ovf_off, nt, i);
     const uint32_t w = P.tile_pairs[(size_t)(t0 + j) * PAIR_CAP + per + (i - ovf_off[j])];
@@ -331,28 +365,13 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
   }
   __syncthreads();
   {
-    constexpr int PT = (TILE_MAX_PER_SEQ + SEL_THREADS - 1) / SEL_THREADS;
-    uint32_t g_[PT], d_[PT], sg = 0, sd = 0;
-#pragma unroll
-    for (int r = 0; r < PT; ++r) {
-      int j = tid * PT + r;
-      g_[r] = j < nt ? ngt[j] : 0u;
-      d_[r] = j < nt ? nbd[j] : 0u;
-      sg += g_[r];
-      sd += d_[r];
-    }
+    const uint32_t g_ = tid < nt ? ngt[tid] : 0u, d_ = tid < nt ? nbd[tid] : 0u;
     uint32_t tg, tb;
-    uint32_t eg = block_exclusive_scan(sg, scr, &tg);
-    uint32_t eb = block_exclusive_scan(sd, scr, &tb);
-#pragma unroll
-    for (int r = 0; r < PT; ++r) {
-      int j = tid * PT + r;
-      if (j < nt) {
-        sure_off[j] = eg;
-        bnd_off[j] = eb;
-      }
-      eg += g_[r];
-      eb += d_[r];
+    const uint32_t eg = block_exclusive_scan(g_, scr, &tg);
+    const uint32_t eb = block_exclusive_scan(d_, scr, &tb);
+    if (tid < nt) {
+      sure_off[tid] = eg;
+      bnd_off[tid] = eb;
     }
     if (tid == 0) {
       sure_off[nt] = tg;
@@ -360,16 +379,19 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
     }
   }
   __syncthreads();
-  // 3. gather
+  // 3. candidates
   const uint32_t nsure = sure_off[nt];
   const uint32_t nbnd = bnd_off[nt];
+  auto entry = [&](int j, uint32_t e) -> uint64_t {  // e-th candidate of tile j
+    return e < (uint32_t)lh ? lhead[j * lh + e] : P.tile_list[(size_t)(t0 + j) * TILE_G + e];
+  };
   for (uint32_t i = tid; i < nsure && i < MAX_K; i += SEL_THREADS) {
-    int j = owner_of(sure_off, nt, i);
-    sel[i] = (uint32_t)P.tile_list[(size_t)(t0 + j) * TILE_G + (i - sure_off[j])];
+    const int j = owner_of(sure_off, nt, i);
+    sel[i] = (uint32_t)entry(j, i - sure_off[j]);
   }
   auto bnd_key = [&](uint32_t i) -> uint64_t {
-    int j = owner_of(bnd_off, nt, i);
-    uint64_t e = P.tile_list[(size_t)(t0 + j) * TILE_G + ngt[j] + (i - bnd_off[j])];
+    const int j = owner_of(bnd_off, nt, i);
+    const uint64_t e = entry(j, ngt[j] + (i - bnd_off[j]));
     return rank_key(key_score(e), (uint32_t)e);
   };
   const bool in_lds = nbnd <= SEL_CAND;
@@ -378,10 +400,18 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
   __syncthreads();
   // 4. the m best boundary candidates
   if (in_lds) {
+    if (tid == 0 && (nbnd & 1)) cand[nbnd] = 0;  // pad to an even count for paired reads (ranks below all)
+    __syncthreads();
+    const uint32_t npair = (nbnd + 1) / 2;
+    const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(cand);
     for (uint32_t i = tid; i < nbnd; i += SEL_THREADS) {
       const uint64_t ki = cand[i];
       uint32_t rank = 0;
-      for (uint32_t j = 0; j < nbnd; ++j) rank += cand[j] > ki;
+#pragma unroll 8
+      for (uint32_t j = 0; j < npair; ++j) {
+        const ulonglong2 v = c2[j];
+        rank += (v.x > ki) + (v.y > ki);
+      }
       if (rank < m) sel[nsure + rank] = key_id(ki);
     }
   } else {
@@ -393,21 +423,56 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
     if (tid == 0) scr[SCR_RES + 9] = 0;
     __syncthreads();
     for (uint32_t i = tid; i < nbnd; i += SEL_THREADS) {
-      uint64_t key = bnd_key(i);
+      const uint64_t key = bnd_key(i);
       if (key >= thr) {
-        uint32_t p = nsure + atomicAdd(&scr[SCR_RES + 9], 1u);
+        const uint32_t p = nsure + atomicAdd(&scr[SCR_RES + 9], 1u);
         if (p < MAX_K) sel[p] = key_id(key);
       }
     }
   }
   __syncthreads();
-  // ascending order by counting (ids are distinct)
+  // ascending order: counting sort on the high bits of the id (buckets of
+  // 2^sh groups, at most SEL_BUCKETS of them), then a rank inside the bucket
+  int sh = 0;
+  while ((G - 1) >> sh >= SEL_BUCKETS) ++sh;
+  const int nbk = ((G - 1) >> sh) + 1;
+  for (int i = tid; i < nbk; i += SEL_THREADS) bcnt[i] = 0;
+  __syncthreads();
+  const bool mine = tid < (int)K;
+  const uint32_t v = mine ? sel[tid] : 0u;
+  const int bk = (int)(v >> sh);
+  if (mine) atomicAdd(&bcnt[bk], 1u);
+  __syncthreads();
+  {
+    constexpr int PB = SEL_BUCKETS / SEL_THREADS;
+    uint32_t c_[PB], sc_ = 0;
+#pragma unroll
+    for (int r = 0; r < PB; ++r) {
+      const int i = tid * PB + r;
+      c_[r] = i < nbk ? bcnt[i] : 0u;
+      sc_ += c_[r];
+    }
+    uint32_t tot;
+    uint32_t e = block_exclusive_scan(sc_, scr, &tot);
+#pragma unroll
+    for (int r = 0; r < PB; ++r) {
+      const int i = tid * PB + r;
+      if (i < nbk) {
+        bbase[i] = e;
+        bcnt[i] = 0;  // reused as the fill cursor
+      }
+      e += c_[r];
+    }
+  }
+  __syncthreads();
+  if (mine) bstage[bbase[bk] + atomicAdd(&bcnt[bk], 1u)] = v;
+  __syncthreads();
   int32_t* orow = P.out_idx + (size_t)b * K;
-  for (uint32_t i = tid; i < K; i += SEL_THREADS) {
-    const uint32_t v = sel[i];
-    uint32_t pos = 0;
-    for (uint32_t j = 0; j < K; ++j) pos += sel[j] < v;
-    orow[pos] = (int32_t)v;
+  if (mine) {
+    const uint32_t b0 = bbase[bk], n = bcnt[bk];
+    uint32_t rank = 0;
+    for (uint32_t j = 0; j < n; ++j) rank += bstage[b0 + j] < v;
+    orow[b0 + rank] = (int32_t)v;
   }
   if (tid == 0) P.out_count[b] = (int32_t)K;
 }

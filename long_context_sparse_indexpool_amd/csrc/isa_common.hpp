@@ -49,6 +49,16 @@ struct BatchArgs {
   int32_t tile_start[ISA_MAX_BATCH + 1];  // first work tile of each sequence
 };
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
+// (lgkmcnt 0) and meets the other waves, without the workgroup memory fence of
+// __syncthreads(), whose release part also waits for every outstanding global
+// load -- which would drain register prefetches at each barrier.  Use it only
+// where the barrier orders LDS accesses, not global ones.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt/expcnt at maximum (no wait), lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
 // Sticky device error word (first word of every workspace).
 __device__ __forceinline__ void report(uint32_t* err, uint32_t bits) {
   if (err) atomicOr(err, bits);
@@ -66,14 +76,34 @@ __device__ __forceinline__ int phys_page(const int32_t* __restrict__ bt, int max
   return p;
 }
 
-// Sequence owning work tile `t` (binary search over the per-sequence prefix).
+// Sequence owning work tile `t`: the number of sequences whose first tile is
+// <= t, minus one.  Each lane of the wave tests one sequence (one round of
+// loads from the argument block instead of a chain of dependent ones) and a
+// ballot counts them.  The result is uniform across the wave.
 __device__ __forceinline__ int tile_owner(const BatchArgs& a, int t) {
-  int lo = 0, hi = a.batch - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (a.tile_start[mid] <= t) lo = mid; else hi = mid - 1;
+  const int lane = threadIdx.x & 63;
+  int n = 0;
+#pragma unroll
+  for (int base = 0; base < ISA_MAX_BATCH; base += 64) {
+    if (base < a.batch) {
+      const bool le = base + lane < a.batch && a.tile_start[base + lane] <= t;
+      n += __popcll(__ballot(le));
+    }
   }
-  return lo;
+  return n - 1;
+}
+
+// Inclusive prefix sum across a 64-lane wave with DPP moves: shifts of 1, 2, 4
+// and 8 lanes inside each row of 16, then row broadcasts 15 and 31 carry the
+// row totals upward (lanes whose source is outside the range add 0).
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
 }
 
 // Block-wide exclusive prefix sum of one value per thread (blockDim.x <= 1024,
@@ -81,25 +111,17 @@ __device__ __forceinline__ int tile_owner(const BatchArgs& a, int t) {
 // the exclusive prefix; *total receives the block sum.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_inclusive_scan(v);
   if (lane == 63) tmp[wid] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t run = 0;
-    for (int w = 0; w < nw; ++w) {
-      uint32_t t = tmp[w];
-      tmp[w] = run;
-      run += t;
-    }
-    tmp[nw] = run;
+  if (threadIdx.x < 64) {  // scan of the wave totals by the first wave
+    uint32_t t = threadIdx.x < nw ? tmp[threadIdx.x] : 0u;
+    uint32_t it = wave_inclusive_scan(t);
+    if (threadIdx.x < nw) tmp[threadIdx.x] = it - t;
+    if (threadIdx.x == nw - 1) tmp[nw] = it;
   }
   __syncthreads();
-  uint32_t r = tmp[wid] + x - v;
+  const uint32_t r = tmp[wid] + x - v;
   *total = tmp[nw];
   __syncthreads();
   return r;

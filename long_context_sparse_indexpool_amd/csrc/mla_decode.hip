@@ -44,11 +44,15 @@ constexpr int HALF_DIM = LAT_DIM / 2;
 constexpr int KSTEPS = HALF_DIM / 32;  // K steps of the score product per wave
 constexpr int NBLK = HALF_DIM / 16;    // 16-channel blocks of the output per wave
 constexpr float RESCALE_LOG2 = 8.f;
-constexpr int TILE_TOK = 16;
+
+// token slot inside the 32-token K block, in the order the S^T accumulators
+// hand the probabilities to the P.V operand
+__device__ __forceinline__ int kperm(int t) { return 8 * ((t & 15) >> 2) + (t & 3) + 4 * (t >> 4); }
+constexpr int TILE_TOK = 32;
 constexpr int TILE_GRP = TILE_TOK / GROUP;
-constexpr int VT_STRIDE = 20;  // halves per V^T row (16 tokens + 4 pad)
+constexpr int VT_STRIDE = 40;  // halves per V^T row (32 tokens + 8 pad, 80 B)
 constexpr int MAX_GPS = MAX_K; // groups per split held in LDS
-constexpr int MAX_SPLITS = 16;
+constexpr int MAX_SPLITS = 32;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -72,10 +76,9 @@ struct MlaPtrs {
 };
 
 __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, const MlaPtrs P) {
-  __shared__ _Float16 vt[LAT_DIM * VT_STRIDE];  // 20 KiB: V^T of one 16-token tile
-  __shared__ v4f sx[MLA_THREADS];               // 8 KiB: partial scores exchanged between wave pairs
+  __shared__ _Float16 vt[2][LAT_DIM * VT_STRIDE];  // 2 x 40 KiB: V^T of a 32-token tile, double-buffered
+  __shared__ v4f sx[2][2][MLA_THREADS];            // 2 x 16 KiB: partial scores exchanged between wave pairs
   __shared__ uint32_t trow[MAX_GPS * GROUP];    // latent row of each token slot, or ~0 if not visible
-  __shared__ int32_t rowinfo[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hb = wave & 3, half = wave >> 2;  // heads 16hb.., channels 256half..
@@ -83,30 +86,35 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
   const int split = blockIdx.x % P.splits;
   const int lq = lane & 15, lg = lane >> 4;  // column / row-group of the 16x16 layouts
 
-  if (tid == 0) {
-    int seq = P.row_seq ? P.row_seq[r] : r;
-    int ok = seq >= 0 && seq < a.batch;
-    int L = ok ? a.lens[seq] : 0;
-    int pos = ok ? (P.row_pos ? P.row_pos[r] : L - 1) : -1;
-    int cnt = P.count[r];
-    if (!ok || pos < 0 || pos >= L || cnt < 0 || cnt > P.k) {
-      report(P.err, ISA_DERR_ROW_RANGE);
-      cnt = 0;
-    }
-    rowinfo[0] = ok ? seq : 0;
-    rowinfo[1] = L;
-    rowinfo[2] = pos;
-    rowinfo[3] = cnt;
+  // row description, read by every thread (no barrier); the split's group ids
+  // are fetched in the same round, before the count is known
+  int seq = P.row_seq ? P.row_seq[r] : r;
+  const bool seq_ok = seq >= 0 && seq < a.batch;
+  if (!seq_ok) seq = 0;
+  const int L = seq_ok ? a.lens[seq] : 0;
+  const int pos = seq_ok ? (P.row_pos ? P.row_pos[r] : L - 1) : -1;
+  int cnt = P.count[r];
+  const int jbeg0 = split * P.gps;
+  int gid[MAX_GPS / MLA_THREADS + 1];
+#pragma unroll
+  for (int e = 0; e < MAX_GPS / MLA_THREADS + 1; ++e) {
+    const int j = tid + e * MLA_THREADS;
+    gid[e] = (j < P.gps && jbeg0 + j < P.k) ? P.idx[(size_t)r * P.k + jbeg0 + j] : -1;
   }
-  __syncthreads();
-  const int seq = rowinfo[0], L = rowinfo[1], pos = rowinfo[2], cnt = rowinfo[3];
+  if (!seq_ok || pos < 0 || pos >= L || cnt < 0 || cnt > P.k) {
+    if (tid == 0) report(P.err, ISA_DERR_ROW_RANGE);
+    cnt = 0;
+  }
   const int G = (L + GROUP - 1) / GROUP;
-  const int jbeg = min(cnt, split * P.gps);
+  const int jbeg = min(cnt, jbeg0);
   const int jend = min(cnt, jbeg + P.gps);
   const int ng = jend - jbeg;
   // token table of the split: one block-table lookup per selected group
-  for (int j = tid; j < ng; j += MLA_THREADS) {
-    int g = P.idx[(size_t)r * P.k + jbeg + j];
+#pragma unroll
+  for (int e = 0; e < MAX_GPS / MLA_THREADS + 1; ++e) {
+    const int j = tid + e * MLA_THREADS;
+    if (j >= ng) continue;
+    const int g = gid[e];
     int pg = -1;
     if (g < 0 || g >= G) report(P.err, ISA_DERR_ROW_RANGE);
     else pg = phys_page(P.bt, a.max_pages, a.num_pages, seq, (g * GROUP) / PAGE_TOK, P.err);
@@ -136,56 +144,88 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
 
   const int nslot = ng * GROUP;
   const int ntile = (nslot + TILE_TOK - 1) / TILE_TOK;
-  // QK operand of a tile: token row lq, channels 256half + 32c + 8lg .. +7.  One
-  // register slot per K step; each slot is refilled with the next tile's K step
-  // as soon as it has been consumed, so a whole tile of loads stays in flight.
-  auto row_of = [&](int tile) -> const v4i* {
-    int slot = tile * TILE_TOK + lq;
-    uint32_t row = (tile < ntile && slot < nslot) ? trow[slot] : 0xFFFFFFFFu;
-    return row != 0xFFFFFFFFu
-               ? reinterpret_cast<const v4i*>(P.latent + (size_t)row * LAT_DIM + half * HALF_DIM + lg * 8)
-               : nullptr;
+  // QK operand of a tile: for each 16-token block bk, token row bk*16 + lq,
+  // channels 256half + 32c + 8lg .. +7.  Loads are unconditional (an invisible
+  // token reads row 0 of the pool and is zeroed by a mask), so no branch
+  // separates a load from its use and the compiler waits for exactly the slot
+  // it consumes; each slot is refilled with the next tile's K step as soon as
+  // it has been consumed, so a whole tile of loads stays in flight.
+  auto row_of = [&](int tile, int bk, int& mask) -> const v4i* {
+    const int slot = tile * TILE_TOK + bk * 16 + lq;
+    const uint32_t t = trow[min(slot, MAX_GPS * GROUP - 1)];  // always in range; masked below
+    const bool vis = tile < ntile && slot < nslot && t != 0xFFFFFFFFu;
+    mask = vis ? -1 : 0;
+    const uint32_t row = vis ? t : 0u;
+    return reinterpret_cast<const v4i*>(P.latent + (size_t)row * LAT_DIM + half * HALF_DIM + lg * 8);
   };
-  v4i buf[KSTEPS];
+  // The first tile is issued in the loop's own order (K step by K step, both
+  // token blocks), pinned by scheduling barriers: the wait counter at the loop
+  // head merges this entry with the back edge, so any other order here would
+  // turn the per-slot waits into a wait for every load.
+  v4i buf[2][KSTEPS];
+  int bmask[2];
   {
-    const v4i* src = row_of(0);
-#pragma unroll
-    for (int c = 0; c < KSTEPS; ++c) buf[c] = src ? src[c * 4] : v4i{0, 0, 0, 0};
-  }
-  for (int tile = 0; tile < ntile; ++tile) {
-    const v4i* nsrc = row_of(tile + 1);
-    v4f sacc = {0.f, 0.f, 0.f, 0.f};
+    const v4i* src0 = row_of(0, 0, bmask[0]);
+    const v4i* src1 = row_of(0, 1, bmask[1]);
 #pragma unroll
     for (int c = 0; c < KSTEPS; ++c) {
-      const v4i rr = buf[c];
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, rr), qop[c], sacc, 0, 0, 0);
-      if ((c >> 1) == hb) {  // this wave's eighth of V^T: token lq, channels 256half + 32c + 8lg .. +7
+      buf[0][c] = src0[c * 4];
+      buf[1][c] = src1[c * 4];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  for (int tile = 0; tile < ntile; ++tile) {
+    const int vb = tile & 1;  // V^T / exchange buffer of this tile
+    _Float16* vtb = vt[vb];
+    // visibility of the tile's tokens: bit t of vis[bk] <-> token bk*16 + t
+    const uint64_t vis0 = __ballot(bmask[0] != 0), vis1 = __ballot(bmask[1] != 0);
+    int nmask[2];
+    const v4i* nsrc0 = row_of(tile + 1, 0, nmask[0]);
+    const v4i* nsrc1 = row_of(tile + 1, 1, nmask[1]);
+    v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < KSTEPS; ++c) {
+      const v4i r0 = buf[0][c] & bmask[0], r1 = buf[1][c] & bmask[1];
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, r0), qop[c], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, r1), qop[c], s1, 0, 0, 0);
+      if ((c >> 1) == hb) {  // this wave's eighth of V^T: tokens lq, 16 + lq; channels 256half + 32c + 8lg ..
         const int d0 = half * HALF_DIM + c * 32 + lg * 8;
-        const uint32_t w[4] = {(uint32_t)rr.x, (uint32_t)rr.y, (uint32_t)rr.z, (uint32_t)rr.w};
+        const int k0 = kperm(lq), k1 = kperm(16 + lq);
+        const uint32_t w0[4] = {(uint32_t)r0.x, (uint32_t)r0.y, (uint32_t)r0.z, (uint32_t)r0.w};
+        const uint32_t w1[4] = {(uint32_t)r1.x, (uint32_t)r1.y, (uint32_t)r1.z, (uint32_t)r1.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          vt[(d0 + 2 * i) * VT_STRIDE + lq] = (_Float16)__uint_as_float(w[i] << 16);
-          vt[(d0 + 2 * i + 1) * VT_STRIDE + lq] = (_Float16)__uint_as_float(w[i] & 0xFFFF0000u);
+          vtb[(d0 + 2 * i) * VT_STRIDE + k0] = (_Float16)__uint_as_float(w0[i] << 16);
+          vtb[(d0 + 2 * i + 1) * VT_STRIDE + k0] = (_Float16)__uint_as_float(w0[i] & 0xFFFF0000u);
+          vtb[(d0 + 2 * i) * VT_STRIDE + k1] = (_Float16)__uint_as_float(w1[i] << 16);
+          vtb[(d0 + 2 * i + 1) * VT_STRIDE + k1] = (_Float16)__uint_as_float(w1[i] & 0xFFFF0000u);
         }
       }
-      buf[c] = nsrc ? nsrc[c * 4] : v4i{0, 0, 0, 0};
+      buf[0][c] = nsrc0[c * 4];
+      buf[1][c] = nsrc1[c * 4];
     }
-    sx[tid] = sacc;
-    __syncthreads();  // V^T and the partial scores complete
-    const v4f other = sx[tid ^ (4 * 64)];  // same heads, the other channel half
-    // the accumulator holds head lq of tokens 4lg + i
-    float x[4];
+    bmask[0] = nmask[0];
+    bmask[1] = nmask[1];
+    sx[vb][0][tid] = s0;
+    sx[vb][1][tid] = s1;
+    lds_barrier();  // V^T and partial scores of this tile complete (double-buffered: one barrier per tile)
+    const v4f o0 = sx[vb][0][tid ^ (4 * 64)], o1 = sx[vb][1][tid ^ (4 * 64)];  // the other channel half
+    // the accumulators hold head lq of tokens 4lg + i (block 0) and 16 + 4lg + i (block 1)
+    float x[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int slot = tile * TILE_TOK + 4 * lg + i;
-      bool vis = slot < nslot && trow[slot] != 0xFFFFFFFFu;
-      x[i] = vis ? (sacc[i] + other[i]) * P.c2 : -INFINITY;
+      x[i] = (vis0 >> (4 * lg + i)) & 1 ? (s0[i] + o0[i]) * P.c2 : -INFINITY;
+      x[4 + i] = (vis1 >> (4 * lg + i)) & 1 ? (s1[i] + o1[i]) * P.c2 : -INFINITY;
     }
-    float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    // move the reference only when some head's max got 2^8 above it: p stays <= 256
+    float mt = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mt = fmaxf(mt, x[i]);
+    // move the exponent reference only when some head's scores got 2^8 above it
+    // (p then stays <= 256); the max over the four lanes of a head is needed
+    // only then.  Both waves of a head block see identical scores.
     if (__any(mt > m_ref + RESCALE_LOG2)) {
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
       const float m_new = fmaxf(m_ref, mt);
       const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_ref - m_new);
       l_run *= alpha;
@@ -198,21 +238,20 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[nb][i] *= al[i];
     }
-    v4h pop;
+    v8h pop;
     float ps = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float p = m_ref == -INFINITY ? 0.f : exp2f(x[i] - m_ref);
+    for (int i = 0; i < 8; ++i) {
+      const float p = m_ref == -INFINITY ? 0.f : exp2f(x[i] - m_ref);
       ps += p;
       pop[i] = (_Float16)p;
     }
     l_run += ps;
 #pragma unroll
     for (int nb = 0; nb < NBLK; ++nb) {
-      const v2i v = *reinterpret_cast<const v2i*>(&vt[(half * HALF_DIM + nb * 16 + lq) * VT_STRIDE + lg * 4]);
-      o[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pop, __builtin_bit_cast(v4h, v), o[nb], 0, 0, 0);
+      const v4i vv = *reinterpret_cast<const v4i*>(&vtb[(half * HALF_DIM + nb * 16 + lq) * VT_STRIDE + lg * 8]);
+      o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, __builtin_bit_cast(v8h, vv), o[nb], 0, 0, 0);
     }
-    __syncthreads();  // V^T and sx free for the next tile
   }
 
   // per-head sum over the four lanes holding the head
