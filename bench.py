@@ -33,7 +33,7 @@ INT8_PEAK_TOPS = 5000.0
 N_POOL_COPIES = 4
 N_QSETS = 16
 KERNEL_SOURCES = {
-    "k_indexer_decode": ["indexer_decode.hip", "select_device.hpp", "isa_common.hpp", "isa_launch.hpp"],
+    "k_indexer_score": ["indexer_decode.hip", "select_device.hpp", "isa_common.hpp", "isa_launch.hpp"],
 }
 
 
@@ -96,7 +96,11 @@ class Decode:
         G = [wl.groups(b) for b in range(B)]
         sel_tok = [min(L, 4 * self.k) for L in wl.lens]  # tokens gathered (dense rows: all of them)
         # algorithmic bytes of one step
-        self.bytes_topk = sum(128 * g for g in G if g > self.k) + B * (32 * 128 + 32) + B * (self.k * 4 + 4)
+        # scoring kernel: 128 B per pooled group of every sequence longer than k groups,
+        # plus each sequence's int8 query (32 x 128) and head weights (32)
+        self.groups_scored = sum(g for g in G if g > self.k)
+        self.bytes_score = 128 * self.groups_scored + B * (32 * 128 + 32)
+        self.bytes_topk = self.bytes_score + B * (self.k * 4 + 4)
         self.bytes_att = sum(1024 * t for t in sel_tok) + B * (64 * 512 * 2 + 64 * 512 * 4 + 64 * 4) + \
             B * (self.k * 4 + 4)
         self.bytes_step = self.bytes_topk + self.bytes_att
@@ -120,6 +124,7 @@ class Decode:
         self.i += 1
 
     def time_steps(self, steps, warmup):
+        """Seconds per step over exactly `steps` back-to-back steps after `warmup`."""
         torch = self.torch
         for _ in range(warmup):
             self.step()
@@ -129,6 +134,33 @@ class Decode:
             self.step()
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / steps
+
+    def time_kernel_events(self, steps):
+        """Average durations of the scoring kernel and of the attention kernel over
+        `steps` more back-to-back steps: HIP events that the library records just
+        before and after those two launches, on the stream it launches on.  This
+        pass is separate from the headline timing because the four event records
+        per step slow the step itself."""
+        torch, m = self.torch, self.m
+        n = min(steps, 4096)
+        evs = {k: ([torch.cuda.Event(enable_timing=True) for _ in range(n)],
+                   [torch.cuda.Event(enable_timing=True) for _ in range(n)])
+               for k in (m.ISA_TIMER_INDEXER_SCORE, m.ISA_TIMER_MLA_SPLIT)}
+        for a, b in evs.values():
+            for e in a + b:
+                e.record()  # creates the event
+        torch.cuda.synchronize()
+        for k, (a, b) in evs.items():  # beyond 4096 steps the ring holds the last 4096 launches
+            m.isa_set_kernel_timer(k, a, b)
+        try:
+            for _ in range(steps):
+                self.step()
+            torch.cuda.synchronize()
+        finally:
+            for k in evs:
+                m.isa_set_kernel_timer(k, [], [])
+        avg = {k: sum(x.elapsed_time(y) for x, y in zip(a, b)) / n * 1e-3 for k, (a, b) in evs.items()}
+        return avg[m.ISA_TIMER_INDEXER_SCORE], avg[m.ISA_TIMER_MLA_SPLIT]
 
     def time_kernels(self, reps):
         """Average durations of the indexer launch and of the attention launches,
@@ -152,11 +184,12 @@ class Decode:
         self.torch.cuda.empty_cache()
 
 
-def oracle_step_time(dec, budget_s=25.0):
-    """The CPU oracle on one full decode step of the same workload: scores of every
+def oracle_step_time(dec, min_s=10.0, budget_s=25.0):
+    """The CPU oracle on whole decode steps of the same workload: scores of every
     group, top-512 selection and 64-head attention for each sequence, from the
-    GPU's pooled keys (rotation set 0).  Rows are processed until the time budget
-    is spent; the step time is scaled from the rows done."""
+    GPU's pooled keys (rotation set 0).  Sequences are processed, step after step,
+    until at least `min_s` seconds are spent (stopping early once `budget_s` is
+    passed); steps/s is scaled from the sequences done."""
     import oracle
 
     wl, db = dec.wl, dec.db
@@ -170,19 +203,20 @@ def oracle_step_time(dec, budget_s=25.0):
         pooled.append(dec.pooled[0][pages].reshape(-1, 128)[: wl.groups(b)].cpu().numpy())
     threads = oracle.n_threads()
     t0 = time.perf_counter()
-    rows = 0
-    for b in range(B):
+    done = 0
+    while True:
+        b = done % B
         S = oracle.scores(q[b], hw[b], pooled[b], threads=threads)
         idx, cnt = oracle.topk(S, 512)
         oracle.attention(qa[b], lat[to[b]: to[b + 1]], wl.lens[b], wl.lens[b] - 1, idx, cnt, 1.0 / math.sqrt(512))
-        rows += 1
-        if time.perf_counter() - t0 > budget_s:
+        done += 1
+        spent = time.perf_counter() - t0
+        if (spent >= min_s and done % B == 0) or spent > budget_s:
             break
-    spent = time.perf_counter() - t0
-    step_s = spent * B / rows
+    step_s = spent * B / done
     return {"value": round(1.0 / step_s, 4), "unit": "steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} of {B} sequences of one decode step of {wl.name} (every pooled group scored, "
-                      f"top-512 selected, 64-head attention over the selection), scaled to the whole step; "
+            "sample": f"{done} sequence passes ({done / B:g} decode steps of {wl.name}: every pooled group scored, "
+                      f"top-512 selected, 64-head attention over the selection), scaled to steps/s; "
                       f"scoring spread over {threads} threads, selection and attention on one",
             "seconds": round(spent, 2)}
 
@@ -271,6 +305,75 @@ def bench_pool(dec):
     return out
 
 
+COPY_BYTES = 1 << 30  # plain device copy used to calibrate the HBM byte counters
+
+
+def traffic_run(steps=5):
+    """Workload for the counter passes: a few decode steps of the 8 x 1M workload,
+    then a plain 1 GiB device-to-device copy three times (known bytes: 1 GiB read
+    and 1 GiB written per copy), which calibrates FETCH_SIZE / WRITE_SIZE."""
+    import torch
+
+    from synth.configs import workload
+
+    torch.cuda.set_device(0)
+    dec = Decode(workload(2), N_POOL_COPIES, N_QSETS)
+    for _ in range(3 + steps):
+        dec.step()
+    torch.cuda.synchronize()
+    dec.free()
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("traffic run done")
+
+
+def _counter_rows(path):
+    """(kernel name, counter, value) of every dispatch in a rocprofv3 counter CSV."""
+    import csv
+
+    out = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            out.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"]), r.get("Dispatch_Id")))
+    return out
+
+
+def summarize_traffic(fetch_csv, write_csv, kernel="k_indexer_score", workload_name="decode_b8_L1048576"):
+    """HBM bytes per launch of `kernel` from a FETCH_SIZE pass and a WRITE_SIZE pass
+    (KiB per dispatch), each scaled by what the same counter reads for the 1 GiB
+    copy; writes profiles/traffic_<kernel>_<workload>.json."""
+    def per_dispatch(rows, counter, pred):
+        vals = {}
+        for name, c, v, d in rows:
+            if c.startswith(counter) and pred(name):
+                vals[d] = vals.get(d, 0.0) + v
+        return sorted(vals.values())
+
+    is_kernel = lambda n: f"isa::{kernel}" in n or n.startswith(kernel)
+    is_copy = lambda n: "copyBuffer" in n  # torch's device-to-device copy_ is a runtime blit
+    fr, wr = _counter_rows(fetch_csv), _counter_rows(write_csv)
+    f_k, w_k = per_dispatch(fr, "FETCH_SIZE", is_kernel), per_dispatch(wr, "WRITE_SIZE", is_kernel)
+    f_c, w_c = per_dispatch(fr, "FETCH_SIZE", is_copy), per_dispatch(wr, "WRITE_SIZE", is_copy)
+    if not (f_k and w_k and f_c and w_c):
+        raise SystemExit(f"missing dispatches: {len(f_k)} {len(w_k)} {len(f_c)} {len(w_c)}")
+    med = lambda v: v[len(v) // 2]
+    copy_fetch, copy_write = max(f_c) * 1024, max(w_c) * 1024  # the 1 GiB copies are the largest copy dispatches
+    ff, wf = copy_fetch / COPY_BYTES, copy_write / COPY_BYTES
+    fetch_b, write_b = med(f_k) * 1024, med(w_k) * 1024
+    d = {"kernel": kernel, "workload": workload_name, "source_hash": source_hash(kernel),
+         "fetch_kib_per_launch": med(f_k), "write_kib_per_launch": med(w_k), "launches": len(f_k),
+         "copy_bytes": COPY_BYTES, "copy_fetch_kib": copy_fetch / 1024, "copy_write_kib": copy_write / 1024,
+         "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
+         "hbm_bytes_per_launch": int(fetch_b / ff + write_b / wf)}
+    out = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload_name}.json")
+    with open(out, "w") as f:
+        json.dump(d, f, indent=1)
+    print(json.dumps(d))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,10 +381,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--primary-only", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-run", action="store_true", help="workload for the rocprofv3 counter passes")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_k_indexer_score_*.json from two counter CSVs (no GPU)")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic)
+        return
+    if args.traffic_run:
+        traffic_run()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (sharding is described in DESIGN.md); "
-              "run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (a decode batch would shard by "
+              "sequence with no exchange); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -295,13 +407,17 @@ def main():
     wl = workload(2)
     dec = Decode(wl, N_POOL_COPIES, N_QSETS, keep_host=not args.no_cpu_baseline)
     sec_per_step = dec.time_steps(args.steps, args.warmup)
+    t_score, t_split = dec.time_kernel_events(args.steps)
     t_topk, t_att = dec.time_kernels(20)
-    log(f"{wl.name}: {1 / sec_per_step:.1f} steps/s, indexer {t_topk * 1e6:.1f} us, attention {t_att * 1e6:.1f} us")
+    log(f"{wl.name}: {1 / sec_per_step:.1f} steps/s; scoring kernel {t_score * 1e6:.1f} us, attention kernel "
+        f"{t_split * 1e6:.1f} us; indexer call {t_topk * 1e6:.1f} us, attention call {t_att * 1e6:.1f} us")
     steps_per_s = 1.0 / sec_per_step
-    traffic = measured_traffic("k_indexer_decode", wl.name)
-    roof = {"kernel": "k_indexer_decode", "bound": "hbm", "achieved": round(dec.bytes_topk / t_topk / 1e9, 1),
-            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dec.bytes_topk / t_topk / 1e9 / HBM_PEAK_GBPS, 4),
-            "traffic": traffic, "alg_bytes_per_launch": dec.bytes_topk, "avg_launch_us": round(t_topk * 1e6, 2)}
+    traffic = measured_traffic("k_indexer_score", wl.name)
+    achieved = dec.bytes_score / t_score / 1e9
+    roof = {"kernel": "k_indexer_score", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+            "alg_bytes_per_launch": dec.bytes_score, "groups_per_launch": dec.groups_scored,
+            "alg_bytes_per_group": 128, "avg_launch_us": round(t_score * 1e6, 2)}
     result = {
         "metric": METRIC, "value": round(steps_per_s, 1), "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(sec_per_step * 1e3, 4), "higher_is_better": True,
@@ -312,7 +428,9 @@ def main():
         "hbm_frac": round(dec.bytes_step * steps_per_s / 1e9 / HBM_PEAK_GBPS, 4),
         "alg_bytes_per_step": dec.bytes_step,
         "roofline": roof,
-        "kernels_us": {"indexer_topk": round(t_topk * 1e6, 2), "sparse_mla": round(t_att * 1e6, 2)},
+        "kernels_us": {"k_indexer_score": round(t_score * 1e6, 2), "k_mla_split": round(t_split * 1e6, 2),
+                       "isa_indexer_topk_call": round(t_topk * 1e6, 2),
+                       "isa_sparse_mla_decode_call": round(t_att * 1e6, 2)},
     }
     if not args.no_cpu_baseline:
         log("oracle baseline")

@@ -107,6 +107,18 @@ isa_status isa_device_error(void* ws, isa_stream_t stream, uint32_t* err_word, i
 const char* isa_status_string(isa_status status);
 const char* isa_version(void);
 
+/* Kernel timing hook, for benchmarks.  `starts` and `stops` [host] are arrays
+ * of n hipEvent_t handles, or NULL with n = 0 to switch the hook off.  While it
+ * is set, the i-th later launch of `kernel` (counting from this call) records
+ * starts[i % n] on the call's stream just before the launch and stops[i % n]
+ * just after it, so hipEventElapsedTime gives that launch's own duration.  The
+ * arrays are copied (at most 4096 pairs); the events stay the caller's.  The
+ * setting is process-wide and not thread-safe.  ISA_ERR_INVALID_ARG for an
+ * unknown kernel id, n outside 0..4096 or a NULL handle. */
+#define ISA_TIMER_INDEXER_SCORE 1 /* scoring kernel of isa_indexer_topk (decode mode) */
+#define ISA_TIMER_MLA_SPLIT 2     /* main kernel of isa_sparse_mla_decode */
+isa_status isa_set_kernel_timer(int32_t kernel, void* const* starts, void* const* stops, int32_t n);
+
 #define ISA_SCALE_DYNAMIC 0u /* scales[b] := max|pooled| / 127 of sequence b (1 if all zero) */
 #define ISA_SCALE_GIVEN 1u   /* use scales[b] as given (> 0), single pass, clamp to +-127 */
 

@@ -6,7 +6,7 @@ A thin ctypes binding over ``libisa.so`` (the HIP kernels and the C ABI of
 Every step of the path runs in the library's kernels; there is no fallback: if
 the library is not built, importing the binding raises.
 
-Build the library with ``python -m long_context_sparse_indexpool_amd.build``.
+Build the library with ``python long_context_sparse_indexpool_amd/build.py``.
 """
 from __future__ import annotations
 
@@ -29,8 +29,11 @@ ISA_OP_INDEXPOOL, ISA_OP_INDEXER_TOPK, ISA_OP_SPARSE_MLA, ISA_OP_PREFILL_SCORES 
 ISA_SCALE_DYNAMIC, ISA_SCALE_GIVEN = 0, 1
 DERR_PAGE_OOB, DERR_HEADW_RANGE, DERR_SCORE_OVERFLOW, DERR_ROW_RANGE, DERR_NONFINITE = 1, 2, 4, 8, 16
 
+ISA_TIMER_INDEXER_SCORE, ISA_TIMER_MLA_SPLIT = 1, 2
+
 EXPORTS = ("isa_workspace_size", "isa_workspace_init", "isa_device_error", "isa_status_string", "isa_version",
-           "isa_indexpool", "isa_indexer_topk", "isa_sparse_mla_decode", "isa_indexer_prefill_scores")
+           "isa_set_kernel_timer", "isa_indexpool", "isa_indexer_topk", "isa_sparse_mla_decode",
+           "isa_indexer_prefill_scores")
 
 
 class IsaError(RuntimeError):
@@ -47,7 +50,7 @@ class isa_seqs(ctypes.Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run: python -m long_context_sparse_indexpool_amd.build")
+        raise ImportError(f"{LIB_PATH} is not built; run: python long_context_sparse_indexpool_amd/build.py")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, sz, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_uint32
     sp = ctypes.POINTER(isa_seqs)
@@ -58,11 +61,12 @@ def _load() -> ctypes.CDLL:
     lib.isa_status_string.argtypes = [ctypes.c_int]
     lib.isa_status_string.restype = ctypes.c_char_p
     lib.isa_version.restype = ctypes.c_char_p
+    lib.isa_set_kernel_timer.argtypes = [i32, vp, vp, i32]
     lib.isa_indexpool.argtypes = [vp, vp, sp, vp, vp, u32, vp, sz, vp]
     lib.isa_indexer_topk.argtypes = [vp, vp, vp, sp, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.isa_sparse_mla_decode.argtypes = [vp, vp, sp, vp, vp, i32, vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.isa_indexer_prefill_scores.argtypes = [vp, vp, vp, i32, vp, sp, vp, i32, vp, sz, vp]
-    for f in ("isa_workspace_init", "isa_device_error", "isa_indexpool", "isa_indexer_topk",
+    for f in ("isa_workspace_init", "isa_device_error", "isa_set_kernel_timer", "isa_indexpool", "isa_indexer_topk",
               "isa_sparse_mla_decode", "isa_indexer_prefill_scores"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
@@ -126,6 +130,20 @@ def workspace_size(op: int, seqs: Optional[Seqs], rows: int = 0, cols: int = 0) 
 def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
     """A zero-filled workspace (zero fill is the only initialisation the library needs)."""
     return torch.zeros(max(256, (nbytes + 255) // 256 * 256), dtype=torch.uint8, device=device)
+
+
+def isa_set_kernel_timer(kernel: int, starts: Sequence[torch.cuda.Event], stops: Sequence[torch.cuda.Event]) -> None:
+    """Record starts[i % n] / stops[i % n] around the i-th later launch of
+    ``kernel`` (ISA_TIMER_*), on the stream of the call; empty lists switch it
+    off.  The events (timing-enabled, already recorded once so that they exist)
+    must stay alive while the hook is set."""
+    n = len(starts)
+    if n != len(stops):
+        raise ValueError("starts and stops differ in length")
+    arr = ctypes.c_void_p * max(n, 1)
+    a = arr(*[e.cuda_event for e in starts]) if n else None
+    b = arr(*[e.cuda_event for e in stops]) if n else None
+    _check("isa_set_kernel_timer", lib.isa_set_kernel_timer(kernel, a, b, n))
 
 
 def isa_workspace_init(ws: torch.Tensor, stream=None) -> None:

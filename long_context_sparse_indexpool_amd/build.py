@@ -1,6 +1,6 @@
 """Build libisa.so (the gfx950 HIP kernels and the C ABI) in-tree with hipcc.
 
-Usage: python -m long_context_sparse_indexpool_amd.build [--verbose]
+Usage: python long_context_sparse_indexpool_amd/build.py [--verbose]
 """
 from __future__ import annotations
 

@@ -88,6 +88,8 @@ isa_status launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? ISA_OK : ISA_ERR_HIP;
 }
 
+KernelTimer g_timer[3];
+
 }  // namespace isa
 
 using namespace isa;
@@ -95,6 +97,21 @@ using namespace isa;
 extern "C" {
 
 const char* isa_version(void) { return "isa 0.1 (gfx950)"; }
+
+isa_status isa_set_kernel_timer(int32_t kernel, void* const* starts, void* const* stops, int32_t n) {
+  if (kernel != ISA_TIMER_INDEXER_SCORE && kernel != ISA_TIMER_MLA_SPLIT) return ISA_ERR_INVALID_ARG;
+  if (n < 0 || n > isa::TIMER_MAX || (n > 0 && (starts == nullptr || stops == nullptr))) return ISA_ERR_INVALID_ARG;
+  for (int i = 0; i < n; ++i)
+    if (starts[i] == nullptr || stops[i] == nullptr) return ISA_ERR_INVALID_ARG;
+  isa::KernelTimer& t = isa::g_timer[kernel];
+  for (int i = 0; i < n; ++i) {
+    t.start[i] = (hipEvent_t)starts[i];
+    t.stop[i] = (hipEvent_t)stops[i];
+  }
+  t.next = 0;
+  t.n = n;
+  return ISA_OK;
+}
 
 const char* isa_status_string(isa_status st) {
   switch (st) {

@@ -53,4 +53,24 @@ isa_status launch_prefill_scores(const BatchArgs& a, const int8_t* q, const int8
 
 isa_status launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 
+// Benchmark timing hook (isa_set_kernel_timer): a ring of event pairs recorded
+// around the launches of one kernel.
+constexpr int TIMER_MAX = 4096;
+struct KernelTimer {
+  int n = 0, next = 0;
+  hipEvent_t start[TIMER_MAX], stop[TIMER_MAX];
+};
+extern KernelTimer g_timer[3];
+inline void timer_begin(int k, hipStream_t s) {
+  KernelTimer& t = g_timer[k];
+  if (t.n) (void)hipEventRecord(t.start[t.next], s);
+}
+inline void timer_end(int k, hipStream_t s) {
+  KernelTimer& t = g_timer[k];
+  if (t.n) {
+    (void)hipEventRecord(t.stop[t.next], s);
+    t.next = (t.next + 1) % t.n;
+  }
+}
+
 }  // namespace isa

@@ -56,6 +56,35 @@ constexpr int MAX_SPLITS = 32;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
+// Two bf16 values (low half first) to two fp16 values.  Exact for values in
+// the fp16 normal range, which the latent rows are required to stay in; the
+// conversion truncates, which for these values is the same as rounding.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u));
+  return __builtin_bit_cast(uint32_t, h);
+}
+// low (high) halves of a and b, a's in the low half of the result
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+// 4x4 transpose inside each quad of lanes: lane i holds v = M[i][0..3] on
+// entry and M[0..3][i] on exit.  Two exchange rounds (lane bit 0 with element
+// bit 0, then bit 1 with bit 1), each a DPP quad permutation plus selects.
+__device__ __forceinline__ void quad_transpose(uint32_t (&v)[4], int i) {
+  const bool b0 = i & 1, b1 = i & 2;
+#pragma unroll
+  for (int p = 0; p < 4; p += 2) {
+    const uint32_t r = (uint32_t)__builtin_amdgcn_mov_dpp((int)(b0 ? v[p] : v[p + 1]), 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+    v[p] = b0 ? r : v[p];
+    v[p + 1] = b0 ? v[p + 1] : r;
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const uint32_t r = (uint32_t)__builtin_amdgcn_mov_dpp((int)(b1 ? v[p] : v[p + 2]), 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+    v[p] = b1 ? r : v[p];
+    v[p + 2] = b1 ? v[p + 2] : r;
+  }
+}
+
 struct MlaPtrs {
   const uint16_t* q;
   const uint16_t* latent;
@@ -188,18 +217,28 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
       const v4i r0 = buf[0][c] & bmask[0], r1 = buf[1][c] & bmask[1];
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, r0), qop[c], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, r1), qop[c], s1, 0, 0, 0);
-      if ((c >> 1) == hb) {  // this wave's eighth of V^T: tokens lq, 16 + lq; channels 256half + 32c + 8lg ..
-        const int d0 = half * HALF_DIM + c * 32 + lg * 8;
-        const int k0 = kperm(lq), k1 = kperm(16 + lq);
-        const uint32_t w0[4] = {(uint32_t)r0.x, (uint32_t)r0.y, (uint32_t)r0.z, (uint32_t)r0.w};
-        const uint32_t w1[4] = {(uint32_t)r1.x, (uint32_t)r1.y, (uint32_t)r1.z, (uint32_t)r1.w};
+      if ((c >> 1) == hb) {  // this wave's eighth of V^T: channels 256half + 32c + 8lg .. +7
+        // Lane (m = lq/4, i = lq%4) holds tokens at slots 8m+i (block 0) and
+        // 8m+4+i (block 1).  A 4x4 transpose of channel pairs inside the quad
+        // gives lane i channels 2i, 2i+1 of all eight slots 8m..8m+7, which it
+        // stores as two 16-byte rows of V^T.
+        uint32_t x[4], y[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          vtb[(d0 + 2 * i) * VT_STRIDE + k0] = (_Float16)__uint_as_float(w0[i] << 16);
-          vtb[(d0 + 2 * i + 1) * VT_STRIDE + k0] = (_Float16)__uint_as_float(w0[i] & 0xFFFF0000u);
-          vtb[(d0 + 2 * i) * VT_STRIDE + k1] = (_Float16)__uint_as_float(w1[i] << 16);
-          vtb[(d0 + 2 * i + 1) * VT_STRIDE + k1] = (_Float16)__uint_as_float(w1[i] & 0xFFFF0000u);
+        for (int p = 0; p < 4; ++p) {
+          x[p] = bf16x2_to_f16x2((uint32_t)r0[p]);
+          y[p] = bf16x2_to_f16x2((uint32_t)r1[p]);
         }
+        const int qi = lq & 3;
+        quad_transpose(x, qi);
+        quad_transpose(y, qi);
+        const int d = half * HALF_DIM + c * 32 + lg * 8 + 2 * qi;
+        const int slot = 8 * (lq >> 2);
+        const v4i lo = {(int)pack_lo(x[0], x[1]), (int)pack_lo(x[2], x[3]), (int)pack_lo(y[0], y[1]),
+                        (int)pack_lo(y[2], y[3])};
+        const v4i hi = {(int)pack_hi(x[0], x[1]), (int)pack_hi(x[2], x[3]), (int)pack_hi(y[0], y[1]),
+                        (int)pack_hi(y[2], y[3])};
+        *reinterpret_cast<v4i*>(&vtb[d * VT_STRIDE + slot]) = lo;
+        *reinterpret_cast<v4i*>(&vtb[(d + 1) * VT_STRIDE + slot]) = hi;
       }
       buf[0][c] = nsrc0[c * 4];
       buf[1][c] = nsrc1[c * 4];
@@ -348,8 +387,10 @@ isa_status launch_sparse_mla(const BatchArgs& a, const MlaPlan& p, const uint16_
                              float* lse, const MlaWs& w, hipStream_t stream) {
   MlaPtrs P{q, latent, bt, row_seq, row_pos, idx, count, out, lse, w.o_part, w.ml_part, w.err, k,
             sm_scale * LOG2E, p.splits, p.groups_per_split};
+  timer_begin(ISA_TIMER_MLA_SPLIT, stream);
   hipLaunchKernelGGL(k_mla_split, dim3(p.rows * p.splits), dim3(MLA_THREADS), 0, stream, a, P);
   if (hipGetLastError() != hipSuccess) return ISA_ERR_HIP;
+  timer_end(ISA_TIMER_MLA_SPLIT, stream);
   if (p.splits > 1) {
     hipLaunchKernelGGL(k_mla_combine, dim3(p.rows * ATT_HEADS), dim3(128), 0, stream, P);
     if (hipGetLastError() != hipSuccess) return ISA_ERR_HIP;

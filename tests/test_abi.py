@@ -164,3 +164,18 @@ def test_workspace_helpers_reject(m):
     assert m.lib.isa_workspace_init(None, 1024, None) == m.ISA_ERR_INVALID_ARG
     assert m.lib.isa_workspace_init(P, 100, None) == m.ISA_ERR_INVALID_ARG
     assert m.lib.isa_device_error(None, None, None, 0) == m.ISA_ERR_INVALID_ARG
+
+
+def test_kernel_timer_rejects(m):
+    """The timing hook only stores handles: unknown kernels, bad counts and NULL
+    handles are rejected, clearing is accepted (no event is touched here)."""
+    two = (ctypes.c_void_p * 2)(P, P)
+    one_null = (ctypes.c_void_p * 2)(P, None)
+    assert m.lib.isa_set_kernel_timer(0, None, None, 0) == m.ISA_ERR_INVALID_ARG
+    assert m.lib.isa_set_kernel_timer(3, None, None, 0) == m.ISA_ERR_INVALID_ARG
+    assert m.lib.isa_set_kernel_timer(m.ISA_TIMER_INDEXER_SCORE, None, two, 2) == m.ISA_ERR_INVALID_ARG
+    assert m.lib.isa_set_kernel_timer(m.ISA_TIMER_INDEXER_SCORE, two, one_null, 2) == m.ISA_ERR_INVALID_ARG
+    assert m.lib.isa_set_kernel_timer(m.ISA_TIMER_MLA_SPLIT, two, two, -1) == m.ISA_ERR_INVALID_ARG
+    assert m.lib.isa_set_kernel_timer(m.ISA_TIMER_MLA_SPLIT, two, two, 4097) == m.ISA_ERR_INVALID_ARG
+    for k in (m.ISA_TIMER_INDEXER_SCORE, m.ISA_TIMER_MLA_SPLIT):
+        assert m.lib.isa_set_kernel_timer(k, None, None, 0) == m.ISA_OK
