@@ -1,0 +1,124 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (whole batch per call, scores not requested), against the CPU
+oracle.
+
+Decode workloads (8192 tokens; 64 x 131,072; 8 x 1,048,576; 32 ragged paged
+sequences up to 2^20): pooled keys of every sequence within 1 LSB, every score
+bit-exact (from a second call that also writes the scores), every selected id
+bit-exact, and attention within tolerance for every row.  The prefill chunk
+(2048 queries at the end of one 2^20-token sequence) checks the mask of all
+2048 score rows at full size and sampled rows one by one: scores, selection and
+attention.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth.configs import SM_SCALE, TOPK_GROUPS, workload
+
+import harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_full(i: int):
+    wl = workload(i)
+    B = wl.batch
+    H.log(f"{wl.name}: generating inputs")
+    db = H.make_batch(wl, keep_host=True)
+    H.run_pool(db)
+    H.log(f"{wl.name}: pool parity, {B} sequences")
+    H.check_pool(db)
+
+    q, hw = wl.q_idx(0, B), wl.head_w(0, B)
+    H.log(f"{wl.name}: top-k as timed (no score output)")
+    idx, cnt, _, _ = H.run_topk(db, with_scores=False, q=q, hw=hw)
+    _, _, sc, _ = H.run_topk(db, with_scores=True, q=q, hw=hw)
+    idx2, cnt2, _, _ = H.run_topk(db, with_scores=False, q=q, hw=hw)
+    assert np.array_equal(idx, idx2) and np.array_equal(cnt, cnt2), "selection differs between calls"
+
+    H.log(f"{wl.name}: oracle scores and selection")
+    refs = oracle.map_rows(lambda b: H.oracle_scores_for(db, b), range(B))
+    for b in range(B):
+        G = wl.groups(b)
+        assert np.array_equal(sc[b, :G].astype(np.int64), refs[b]), f"scores of sequence {b}"
+        H.check_topk_row(refs[b], TOPK_GROUPS, idx[b], int(cnt[b]))
+
+    H.log(f"{wl.name}: attention, {B} rows")
+    idx_d = torch.from_numpy(idx).cuda()
+    cnt_d = torch.from_numpy(cnt).cuda()
+    out, lse = H.run_attention(db, idx_d, cnt_d, TOPK_GROUPS, q=wl.q_attn(0, B))
+    qa, lat, to = db.host["q_attn"], db.host["latent"], wl.token_offsets
+
+    def one(b):
+        L = wl.lens[b]
+        return oracle.attention(qa[b], lat[to[b]: to[b + 1]], L, L - 1, idx[b], int(cnt[b]), SM_SCALE)
+
+    ref_att = oracle.map_rows(one, range(B))
+    for b in range(B):
+        H.attention_tolerance(out[b], ref_att[b][0], lse[b], ref_att[b][1])
+    H.log(f"{wl.name}: done")
+
+
+def test_full_decode_b1_L8192():
+    _decode_full(0)
+
+
+def test_full_decode_b64_L131072():
+    _decode_full(1)
+
+
+def test_full_decode_b8_L1048576():
+    _decode_full(2)
+
+
+def test_full_ragged_paged_b32():
+    _decode_full(4)
+
+
+def test_full_prefill_q2048_L1048576():
+    m = H.isa()
+    wl = workload(3)
+    Q, G, L = wl.rows, wl.groups(0), wl.lens[0]
+    H.log(f"{wl.name}: generating inputs")
+    db = H.make_batch(wl, keep_host=True)
+    H.run_pool(db)
+    qh, hwh, qpos = wl.q_idx(), wl.head_w(), wl.row_pos()
+    sc = torch.empty((Q, G), dtype=torch.int32, device="cuda")
+    ws = m.alloc_workspace(256)
+    H.log(f"{wl.name}: prefill scores {Q} x {G}")
+    m.isa_indexer_prefill_scores(torch.from_numpy(qh).cuda(), torch.from_numpy(hwh).cuda(),
+                                 torch.from_numpy(qpos).cuda(), Q, db.pooled, db.seqs, sc, G, ws)
+    torch.cuda.synchronize()
+    assert m.isa_device_error(ws) == 0
+    # the block-causal mask on every row, at full size: -1 exactly after the query's own group
+    last = torch.from_numpy(qpos // 4).cuda().long()
+    cols = torch.arange(G, device="cuda")
+    masked = cols[None, :] > last[:, None]
+    assert bool((sc[masked] == -1).all()), "masked entries must be -1"
+    assert bool((sc[~masked] >= 0).all()), "visible entries must be valid scores"
+    del masked
+
+    idx = torch.empty((Q, TOPK_GROUPS), dtype=torch.int32, device="cuda")
+    cnt = torch.empty(Q, dtype=torch.int32, device="cuda")
+    m.isa_indexer_topk(None, None, None, None, sc, Q, G, TOPK_GROUPS, idx, cnt, None, ws)
+    torch.cuda.synchronize()
+    out, lse = H.run_attention(db, idx, cnt, TOPK_GROUPS, row_seq=np.zeros(Q, np.int32), row_pos=qpos, rows=Q)
+
+    rows = [0, 1, 2, 3, 511, 1024, 1537, 2045, 2046, 2047]
+    H.log(f"{wl.name}: oracle on rows {rows}")
+    k8 = H.pooled_logical(db, 0)
+    S = sc[rows].cpu().numpy()
+    idxh, cnth = idx[rows].cpu().numpy(), cnt[rows].cpu().numpy()
+    refs = oracle.map_rows(lambda j: oracle.prefill_scores(qh[rows[j]], hwh[rows[j]], int(qpos[rows[j]]), k8),
+                           range(len(rows)))
+    qa, lat = db.host["q_attn"], db.host["latent"]
+    ref_att = oracle.map_rows(
+        lambda j: oracle.attention(qa[rows[j]], lat, L, int(qpos[rows[j]]), idxh[j], int(cnth[j]), SM_SCALE),
+        range(len(rows)))
+    for j, r in enumerate(rows):
+        assert np.array_equal(S[j].astype(np.int64), refs[j]), f"scores of query {r}"
+        H.check_topk_row(refs[j], TOPK_GROUPS, idxh[j], int(cnth[j]))
+        H.attention_tolerance(out[r], ref_att[j][0], lse[r], ref_att[j][1])
+    H.log(f"{wl.name}: done")
