@@ -11,27 +11,28 @@
 // "의견이 갈리는 지점 — 위치 인코딩": qk_rope_head_dim = 0, so no rotary part.  The
 // absorbed form is used: keys = values = the 512-d latent row.
 //
-// Design.  A workgroup is (query row, token split) with eight waves: wave w owns
-// heads 16(w%4)..+15 and latent channels 256(w/4)..+255, so each wave's output
-// accumulator is 16 heads x 256 channels (64 registers per lane).  The split's
-// selected groups are first turned into a table of physical latent rows (one
-// block-table lookup per group).  Then, per tile of 16 tokens:
-//  * Partial scores S^T = C Q^T over the wave's 256 channels with
-//    v_mfma_f32_16x16x32_bf16: tokens are M, the wave's 16 heads are N.  Each
-//    lane loads 16 contiguous bytes of a latent row per K step straight from
-//    HBM into a ring of register slots; a slot is refilled with the next tile's
-//    K step as soon as it is consumed, so a whole tile of loads is in flight.
-//    The two waves sharing a head block add their halves through LDS (both
-//    then hold identical scores and make identical softmax decisions).
-//  * Each wave also converts one eighth of the tile's channels to fp16 (exact
-//    for bf16 values inside the fp16 range) and stores them transposed in LDS
-//    (V^T).  Computing S^T leaves every lane with four probabilities of one
-//    head in exactly the A-operand layout the P.V product needs.
-//  * Softmax in fp32, base 2.  The exponent reference of a head moves only when
-//    its running max exceeds it by more than 8 (so p <= 256 in fp16), which
-//    makes the rescale of the output accumulator rare.
-//  * O += P V with v_mfma_f32_16x16x16f16: heads are M, 16 channels per N
-//    block, the 16 tokens are K; V^T comes from LDS with one 8-byte read.
+// Design.  A workgroup is (query row, token split) with eight waves, and every
+// byte of a latent tile is loaded by exactly one of them: wave (cg, th) owns
+// latent channels 128cg..128cg+127 and tokens 16th..16th+15 of each 32-token
+// tile.  (A layout where several waves load the same rows -- one per block of
+// heads -- is capped near 2.3 TB/s of unique bytes by the vector memory path;
+// without replication the same gather reaches about 6 TB/s.)  Per tile:
+//  * Partial scores S^T = C Q^T over the wave's 128 channels for its 16 tokens
+//    and all 64 heads (v_mfma_f32_16x16x32_bf16, tokens = M, heads = N, the
+//    query block in registers).  Each lane loads 16 contiguous bytes of a
+//    latent row per K step straight from HBM, two tiles ahead.
+//  * The same registers, converted to fp16 (exact for bf16 values in the fp16
+//    normal range), are stored token-major in LDS as V; the P.V product reads
+//    them back transposed (ds_read_b64_tr_b16).  The partial scores go to LDS
+//    too.
+//  * Wave w owns the softmax of heads 8w..8w+7: it sums the four channel
+//    groups' partials for its heads over the 32 tokens, keeps the running
+//    reference and sum (base 2; the reference moves only when a head's scores
+//    exceed it by more than 8, so p <= 256 in fp16 and the output rescale is
+//    rare) and writes P in fp16 to LDS.
+//  * Every wave then accumulates O[64 heads x its 64 channels] += P V^T with
+//    v_mfma_f32_16x16x32_f16 (heads = M, channels = N, the 32 tokens = K).
+// Two workgroup barriers per tile, both LDS-only; V is double-buffered.
 // With one split the workgroup normalises and writes the output; otherwise it
 // writes its unnormalised partial (O, reference, sum) and k_mla_combine merges
 // the splits by log-sum-exp weights.
@@ -39,19 +40,21 @@
 
 namespace isa {
 
-constexpr int MLA_THREADS = 512;  // 8 waves: 4 head blocks x 2 channel halves
-constexpr int HALF_DIM = LAT_DIM / 2;
-constexpr int KSTEPS = HALF_DIM / 32;  // K steps of the score product per wave
-constexpr int NBLK = HALF_DIM / 16;    // 16-channel blocks of the output per wave
+constexpr int MLA_THREADS = 512;  // 8 waves: 4 channel groups x 2 token halves
+constexpr int CG_DIM = LAT_DIM / 4;   // channels of a wave's score share (its channel group)
+constexpr int KSTEPS = CG_DIM / 32;   // K steps of the score product per wave
+constexpr int HBLK = ATT_HEADS / 16;  // 16-head blocks
+constexpr int OUT_DIM = LAT_DIM / 8;  // output channels per wave
+constexpr int NBLK = OUT_DIM / 16;    // 16-channel blocks of the output per wave
+constexpr int OWN_HEADS = ATT_HEADS / 8;  // heads whose softmax a wave owns
 constexpr float RESCALE_LOG2 = 8.f;
-
-// token slot inside the 32-token K block, in the order the S^T accumulators
-// hand the probabilities to the P.V operand
-__device__ __forceinline__ int kperm(int t) { return 8 * ((t & 15) >> 2) + (t & 3) + 4 * (t >> 4); }
 constexpr int TILE_TOK = 32;
-constexpr int TILE_GRP = TILE_TOK / GROUP;
-constexpr int VT_STRIDE = 40;  // halves per V^T row (32 tokens + 8 pad, 80 B)
+constexpr int V_STRIDE = LAT_DIM + 16;  // halves per V row in LDS (1 KiB + 32 B: rows 8 banks apart)
+constexpr int P_STRIDE = 40;   // halves per P row (32 tokens + 8 pad, 80 B)
+constexpr int SP_LANES = 96;   // partial-score slots per (half, group, head block): 64 lanes + 8 pad per 16
 constexpr int MAX_GPS = MAX_K; // groups per split held in LDS
+constexpr int BT_LDS = 1024;   // block-table entries of a row staged in LDS (sequences up to 256K tokens;
+                               // for longer rows staging costs more than the round trip it saves)
 constexpr int MAX_SPLITS = 32;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -63,27 +66,23 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
   const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u));
   return __builtin_bit_cast(uint32_t, h);
 }
-// low (high) halves of a and b, a's in the low half of the result
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
-// 4x4 transpose inside each quad of lanes: lane i holds v = M[i][0..3] on
-// entry and M[0..3][i] on exit.  Two exchange rounds (lane bit 0 with element
-// bit 0, then bit 1 with bit 1), each a DPP quad permutation plus selects.
-__device__ __forceinline__ void quad_transpose(uint32_t (&v)[4], int i) {
-  const bool b0 = i & 1, b1 = i & 2;
-#pragma unroll
-  for (int p = 0; p < 4; p += 2) {
-    const uint32_t r = (uint32_t)__builtin_amdgcn_mov_dpp((int)(b0 ? v[p] : v[p + 1]), 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
-    v[p] = b0 ? r : v[p];
-    v[p + 1] = b0 ? v[p + 1] : r;
-  }
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const uint32_t r = (uint32_t)__builtin_amdgcn_mov_dpp((int)(b1 ? v[p] : v[p + 2]), 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
-    v[p] = b1 ? r : v[p];
-    v[p + 2] = b1 ? v[p + 2] : r;
-  }
+// LDS row of token slot t of a tile: slots 8..15 and 24..31 swap their halves,
+// so the two 16-lane groups of a transposed read (tokens 8g + 4h + 0..3,
+// g = 0, 1) fall on disjoint banks.
+__device__ __forceinline__ int vrow(int t) { return t ^ (((t >> 3) & 1) << 2); }
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+// Transposed LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane i
+// receives element i%4 of the 8-byte rows addressed by lanes i/4, 4 + i/4,
+// 8 + i/4, 12 + i/4.  With lane s addressing token t0 + s/4, channels
+// c0 + 4(s%4) .. +3 of a token-major tile, lane i gets channel c0 + i of
+// tokens t0 .. t0+3: a quarter of an MFMA operand with tokens as K.
+__device__ __forceinline__ v4s lds_read_tr16(const _Float16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)((__attribute__((address_space(3))) _Float16*)p));
 }
+// slot of a writer lane's partial-score accumulator (8 pad slots per 16 lanes
+// keep both the writes and the owners' gathers free of bank conflicts)
+__device__ __forceinline__ int sp_slot(int lane) { return lane + 8 * (lane >> 4); }
 
 struct MlaPtrs {
   const uint16_t* q;
@@ -105,12 +104,17 @@ struct MlaPtrs {
 };
 
 __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, const MlaPtrs P) {
-  __shared__ _Float16 vt[2][LAT_DIM * VT_STRIDE];  // 2 x 40 KiB: V^T of a 32-token tile, double-buffered
-  __shared__ v4f sx[2][2][MLA_THREADS];            // 2 x 16 KiB: partial scores exchanged between wave pairs
-  __shared__ uint32_t trow[MAX_GPS * GROUP];    // latent row of each token slot, or ~0 if not visible
+  __shared__ __attribute__((aligned(16))) _Float16 vt[2][TILE_TOK * V_STRIDE];  // 2 x 33 KiB: fp16 V of a tile, double-buffered
+  __shared__ v4f sp[2][4][HBLK][SP_LANES];                // 48 KiB: partial S^T [half][group][head block][lane]
+  __shared__ _Float16 pb[ATT_HEADS * P_STRIDE];           // 5 KiB: P of the tile [head][token]
+  __shared__ __attribute__((aligned(16))) float alpha_s[ATT_HEADS];
+  __shared__ __attribute__((aligned(16))) uint32_t flag_s[8];
+  __shared__ float fin_s[2][ATT_HEADS];
+  __shared__ __attribute__((aligned(16))) uint32_t trow[MAX_GPS * GROUP];  // latent row of each token slot, ~0 if not visible
+  __shared__ int32_t bt_s[BT_LDS];                        // 4 KiB: the row's block-table entries
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hb = wave & 3, half = wave >> 2;  // heads 16hb.., channels 256half..
+  const int cg = wave & 3, th = wave >> 2;   // channels 128cg.., tokens 16th.. of each tile
   const int r = blockIdx.x / P.splits;
   const int split = blockIdx.x % P.splits;
   const int lq = lane & 15, lg = lane >> 4;  // column / row-group of the 16x16 layouts
@@ -130,6 +134,22 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
     const int j = tid + e * MLA_THREADS;
     gid[e] = (j < P.gps && jbeg0 + j < P.k) ? P.idx[(size_t)r * P.k + jbeg0 + j] : -1;
   }
+  // query operand (B = Q^T): lane -> head 16hb + lq, channels 128cg + 32c + 8lg .. +7
+  v8bf qop[HBLK][KSTEPS];
+  {
+    const uint16_t* qp = P.q + ((size_t)r * ATT_HEADS + lq) * LAT_DIM + cg * CG_DIM + lg * 8;
+#pragma unroll
+    for (int hb = 0; hb < HBLK; ++hb)
+#pragma unroll
+      for (int c = 0; c < KSTEPS; ++c)
+        qop[hb][c] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qp + (size_t)hb * 16 * LAT_DIM + c * 32));
+  }
+  // the row's block-table entries, fetched in the same round as the group ids
+  // (one dependent global round trip less before the first latent load)
+  const int npg = (L + PAGE_TOK - 1) / PAGE_TOK;
+  const bool bt_staged = npg <= BT_LDS;
+  if (bt_staged)
+    for (int j = tid; j < npg; j += MLA_THREADS) bt_s[j] = P.bt[(size_t)seq * a.max_pages + j];
   if (!seq_ok || pos < 0 || pos >= L || cnt < 0 || cnt > P.k) {
     if (tid == 0) report(P.err, ISA_DERR_ROW_RANGE);
     cnt = 0;
@@ -138,6 +158,7 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
   const int jbeg = min(cnt, jbeg0);
   const int jend = min(cnt, jbeg + P.gps);
   const int ng = jend - jbeg;
+  if (bt_staged) __syncthreads();  // uniform across the workgroup
   // token table of the split: one block-table lookup per selected group
 #pragma unroll
   for (int e = 0; e < MAX_GPS / MLA_THREADS + 1; ++e) {
@@ -145,8 +166,17 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
     if (j >= ng) continue;
     const int g = gid[e];
     int pg = -1;
-    if (g < 0 || g >= G) report(P.err, ISA_DERR_ROW_RANGE);
-    else pg = phys_page(P.bt, a.max_pages, a.num_pages, seq, (g * GROUP) / PAGE_TOK, P.err);
+    if (g < 0 || g >= G) {
+      report(P.err, ISA_DERR_ROW_RANGE);
+    } else if (bt_staged) {
+      pg = bt_s[(g * GROUP) / PAGE_TOK];
+      if (pg < 0 || pg >= a.num_pages) {
+        report(P.err, ISA_DERR_PAGE_OOB);
+        pg = -1;
+      }
+    } else {
+      pg = phys_page(P.bt, a.max_pages, a.num_pages, seq, (g * GROUP) / PAGE_TOK, P.err);
+    }
 #pragma unroll
     for (int i = 0; i < GROUP; ++i) {
       int tok = g * GROUP + i;
@@ -154,173 +184,203 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
       trow[j * GROUP + i] = vis ? (uint32_t)pg * PAGE_TOK + (uint32_t)(tok % PAGE_TOK) : 0xFFFFFFFFu;
     }
   }
-
-  // query operand (B = Q^T): lane -> head 16hb + lq, channels 256half + 32c + 8lg .. +7
-  v8bf qop[KSTEPS];
-  {
-    const uint16_t* qp = P.q + ((size_t)r * ATT_HEADS + hb * 16 + lq) * LAT_DIM + half * HALF_DIM + lg * 8;
+  v4f o[HBLK][NBLK];
 #pragma unroll
-    for (int c = 0; c < KSTEPS; ++c) {
-      v4i v = *reinterpret_cast<const v4i*>(qp + c * 32);
-      qop[c] = __builtin_bit_cast(v8bf, v);
-    }
-  }
-  v4f o[NBLK];
+  for (int hb = 0; hb < HBLK; ++hb)
 #pragma unroll
-  for (int nb = 0; nb < NBLK; ++nb) o[nb] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY, l_run = 0.f;  // exponent reference (log2 units) and partial sum of the head
-  __syncthreads();
+    for (int nb = 0; nb < NBLK; ++nb) o[hb][nb] = v4f{0.f, 0.f, 0.f, 0.f};
+  // softmax state of the owned head h = 8 wave + lane % 8 (identical in the
+  // eight lanes of a head; l_run is this lane's share of the sum)
+  const int own_h = OWN_HEADS * wave + (lane & 7);
+  const int own_tq = lane >> 3;  // tokens 4 own_tq .. +3 of the tile
+  float m_ref = -INFINITY, l_run = 0.f;
+  lds_barrier();  // token table complete
 
   const int nslot = ng * GROUP;
   const int ntile = (nslot + TILE_TOK - 1) / TILE_TOK;
-  // QK operand of a tile: for each 16-token block bk, token row bk*16 + lq,
-  // channels 256half + 32c + 8lg .. +7.  Loads are unconditional (an invisible
-  // token reads row 0 of the pool and is zeroed by a mask), so no branch
-  // separates a load from its use and the compiler waits for exactly the slot
-  // it consumes; each slot is refilled with the next tile's K step as soon as
-  // it has been consumed, so a whole tile of loads stays in flight.
-  auto row_of = [&](int tile, int bk, int& mask) -> const v4i* {
-    const int slot = tile * TILE_TOK + bk * 16 + lq;
-    const uint32_t t = trow[min(slot, MAX_GPS * GROUP - 1)];  // always in range; masked below
-    const bool vis = tile < ntile && slot < nslot && t != 0xFFFFFFFFu;
+  // This lane's load of tile t: token 16th + lq, channels 128cg + 8lg + 32c.
+  // Loads are unconditional (an invisible token reads row 0 of the pool and is
+  // zeroed by its mask), so no branch separates a load from its use and the
+  // compiler waits for exactly the loads it consumes.
+  auto row_of = [&](int t, int& mask) -> const v4i* {
+    const int slot = t * TILE_TOK + th * 16 + lq;
+    const uint32_t tr = trow[min(slot, MAX_GPS * GROUP - 1)];  // always in range; masked below
+    const bool vis = t < ntile && slot < nslot && tr != 0xFFFFFFFFu;
     mask = vis ? -1 : 0;
-    const uint32_t row = vis ? t : 0u;
-    return reinterpret_cast<const v4i*>(P.latent + (size_t)row * LAT_DIM + half * HALF_DIM + lg * 8);
+    const uint32_t row = vis ? tr : 0u;
+    return reinterpret_cast<const v4i*>(P.latent + (size_t)row * LAT_DIM + cg * CG_DIM + lg * 8);
   };
-  // The first tile is issued in the loop's own order (K step by K step, both
-  // token blocks), pinned by scheduling barriers: the wait counter at the loop
-  // head merges this entry with the back edge, so any other order here would
-  // turn the per-slot waits into a wait for every load.
-  v4i buf[2][KSTEPS];
-  int bmask[2];
-  {
-    const v4i* src0 = row_of(0, 0, bmask[0]);
-    const v4i* src1 = row_of(0, 1, bmask[1]);
+
+  // one tile: partial scores, V, softmax of the owned heads, P.V
+  auto tile_step = [&](int t, v4i (&buf)[KSTEPS], int& bmask) {
+    const int vb = t & 1;
+    _Float16* vtb = vt[vb];
+    v4f acc[HBLK];
+#pragma unroll
+    for (int hb = 0; hb < HBLK; ++hb) acc[hb] = v4f{0.f, 0.f, 0.f, 0.f};
+    int nmask;
+    const v4i* nsrc = row_of(t + 2, nmask);
 #pragma unroll
     for (int c = 0; c < KSTEPS; ++c) {
-      buf[0][c] = src0[c * 4];
-      buf[1][c] = src1[c * 4];
+      const v4i kv = buf[c] & bmask;
+#pragma unroll
+      for (int hb = 0; hb < HBLK; ++hb)
+        acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kv), qop[hb][c], acc[hb], 0, 0, 0);
+      // V in fp16, token-major: this lane's 8 channels of token 16th + lq
+      const v4i vh = {(int)bf16x2_to_f16x2((uint32_t)kv[0]), (int)bf16x2_to_f16x2((uint32_t)kv[1]),
+                      (int)bf16x2_to_f16x2((uint32_t)kv[2]), (int)bf16x2_to_f16x2((uint32_t)kv[3])};
+      *reinterpret_cast<v4i*>(&vtb[vrow(th * 16 + lq) * V_STRIDE + cg * CG_DIM + c * 32 + lg * 8]) = vh;
+      buf[c] = nsrc[c * 4];  // refill with tile t + 2
+    }
+    bmask = nmask;
+#pragma unroll
+    for (int hb = 0; hb < HBLK; ++hb) sp[th][cg][hb][sp_slot(lane)] = acc[hb];
+    lds_barrier();  // partial scores and V of this tile complete
+
+    // ---- softmax of the owned heads over the tile's 32 tokens ----
+    {
+      const int hb = own_h >> 4, hl = own_h & 15;
+      const int tq = own_tq, th2 = tq >> 2;
+      v4f s = sp[th2][0][hb][sp_slot(hl + 16 * (tq & 3))];
+#pragma unroll
+      for (int g2 = 1; g2 < 4; ++g2) s += sp[th2][g2][hb][sp_slot(hl + 16 * (tq & 3))];
+      const int sbase = t * TILE_TOK + 4 * tq;
+      const uint4 tr = *reinterpret_cast<const uint4*>(&trow[min(sbase, MAX_GPS * GROUP - 4)]);
+      const uint32_t trv[4] = {tr.x, tr.y, tr.z, tr.w};
+      float x[4];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool vis = sbase + i < nslot && trv[i] != 0xFFFFFFFFu;
+        x[i] = vis ? s[i] * P.c2 : -INFINITY;
+        mt = fmaxf(mt, x[i]);
+      }
+      const bool moved = __any(mt > m_ref + RESCALE_LOG2);
+      float alpha = 1.f;
+      if (moved) {  // wave-uniform: move the reference of every owned head to its max so far
+        mt = fmaxf(mt, __shfl_xor(mt, 8, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float m_new = fmaxf(m_ref, mt);
+        alpha = m_new == -INFINITY ? 1.f : exp2f(m_ref - m_new);
+        l_run *= alpha;
+        m_ref = m_new;
+      }
+      // every owner publishes its heads' factors (1 when it did not move) and
+      // whether it moved, so one rescale pass serves all heads
+      if (tq == 0) alpha_s[own_h] = alpha;
+      if (lane == 0) flag_s[wave] = moved ? 1u : 0u;
+      float ps = 0.f;
+      v4h ph;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pr = m_ref == -INFINITY ? 0.f : exp2f(x[i] - m_ref);
+        ps += pr;
+        ph[i] = (_Float16)pr;
+      }
+      l_run += ps;
+      *reinterpret_cast<v4h*>(&pb[own_h * P_STRIDE + 4 * tq]) = ph;
+    }
+    lds_barrier();  // P, reference moves complete
+
+    // ---- O[64 heads x this wave's 64 channels] += P V ----
+    const uint4 f0 = *reinterpret_cast<const uint4*>(&flag_s[0]);
+    const uint4 f1 = *reinterpret_cast<const uint4*>(&flag_s[4]);
+    if ((f0.x | f0.y | f0.z | f0.w | f1.x | f1.y | f1.z | f1.w) != 0u) {
+#pragma unroll
+      for (int hb = 0; hb < HBLK; ++hb) {
+        const float4 al = *reinterpret_cast<const float4*>(&alpha_s[hb * 16 + 4 * lg]);
+#pragma unroll
+        for (int nb = 0; nb < NBLK; ++nb) {
+          o[hb][nb][0] *= al.x;
+          o[hb][nb][1] *= al.y;
+          o[hb][nb][2] *= al.z;
+          o[hb][nb][3] *= al.w;
+        }
+      }
+    }
+    v8h pv[HBLK];
+#pragma unroll
+    for (int hb = 0; hb < HBLK; ++hb)
+      pv[hb] = __builtin_bit_cast(v8h, *reinterpret_cast<const v4i*>(&pb[(hb * 16 + lq) * P_STRIDE + lg * 8]));
+    // V operand: lane (lq, lg) gets channel 16nb + lq of tokens 8lg .. 8lg+7
+    const _Float16* vr0 = &vtb[vrow(8 * lg + (lq >> 2)) * V_STRIDE + wave * OUT_DIM + 4 * (lq & 3)];
+    const _Float16* vr1 = &vtb[vrow(8 * lg + 4 + (lq >> 2)) * V_STRIDE + wave * OUT_DIM + 4 * (lq & 3)];
+#pragma unroll
+    for (int nb = 0; nb < NBLK; ++nb) {
+      const v4s v0 = lds_read_tr16(vr0 + nb * 16), v1 = lds_read_tr16(vr1 + nb * 16);
+      const v8h vv = __builtin_bit_cast(v8h, v4i{__builtin_bit_cast(v2i, v0).x, __builtin_bit_cast(v2i, v0).y,
+                                                  __builtin_bit_cast(v2i, v1).x, __builtin_bit_cast(v2i, v1).y});
+#pragma unroll
+      for (int hb = 0; hb < HBLK; ++hb) o[hb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pv[hb], vv, o[hb][nb], 0, 0, 0);
+    }
+  };
+
+  // Tiles 0 and 1 are issued before the loop in the loop's own order, pinned
+  // by scheduling barriers: the wait counter at the loop head merges this
+  // entry with the back edge, so any other order would make each K step wait
+  // for every load in flight.  The loop is unrolled by two (a register buffer
+  // per parity); an odd last tile is followed by an all-masked one.
+  v4i buf0[KSTEPS], buf1[KSTEPS];
+  int bm0, bm1;
+  {
+    const v4i* s0 = row_of(0, bm0);
+#pragma unroll
+    for (int c = 0; c < KSTEPS; ++c) {
+      buf0[c] = s0[c * 4];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const v4i* s1 = row_of(1, bm1);
+#pragma unroll
+    for (int c = 0; c < KSTEPS; ++c) {
+      buf1[c] = s1[c * 4];
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  for (int tile = 0; tile < ntile; ++tile) {
-    const int vb = tile & 1;  // V^T / exchange buffer of this tile
-    _Float16* vtb = vt[vb];
-    // visibility of the tile's tokens: bit t of vis[bk] <-> token bk*16 + t
-    const uint64_t vis0 = __ballot(bmask[0] != 0), vis1 = __ballot(bmask[1] != 0);
-    int nmask[2];
-    const v4i* nsrc0 = row_of(tile + 1, 0, nmask[0]);
-    const v4i* nsrc1 = row_of(tile + 1, 1, nmask[1]);
-    v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < ntile; t += 2) {
+    tile_step(t, buf0, bm0);
+    tile_step(t + 1, buf1, bm1);
+  }
+
+  // ---- finish: per-head sums of the owned heads, then every wave's channels ----
+  float l_tot = l_run + __shfl_xor(l_run, 8, 64);
+  l_tot += __shfl_xor(l_tot, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  if (own_tq == 0) {
+    fin_s[0][own_h] = l_tot > 0.f ? m_ref : -INFINITY;
+    fin_s[1][own_h] = l_tot;
+  }
+  __syncthreads();
+  const int d_base = wave * OUT_DIM;
+  if (P.splits == 1) {
+    float* orow = P.out + (size_t)r * ATT_HEADS * LAT_DIM;
 #pragma unroll
-    for (int c = 0; c < KSTEPS; ++c) {
-      const v4i r0 = buf[0][c] & bmask[0], r1 = buf[1][c] & bmask[1];
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, r0), qop[c], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, r1), qop[c], s1, 0, 0, 0);
-      if ((c >> 1) == hb) {  // this wave's eighth of V^T: channels 256half + 32c + 8lg .. +7
-        // Lane (m = lq/4, i = lq%4) holds tokens at slots 8m+i (block 0) and
-        // 8m+4+i (block 1).  A 4x4 transpose of channel pairs inside the quad
-        // gives lane i channels 2i, 2i+1 of all eight slots 8m..8m+7, which it
-        // stores as two 16-byte rows of V^T.
-        uint32_t x[4], y[4];
+    for (int hb = 0; hb < HBLK; ++hb) {
+      float inv[4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          x[p] = bf16x2_to_f16x2((uint32_t)r0[p]);
-          y[p] = bf16x2_to_f16x2((uint32_t)r1[p]);
-        }
-        const int qi = lq & 3;
-        quad_transpose(x, qi);
-        quad_transpose(y, qi);
-        const int d = half * HALF_DIM + c * 32 + lg * 8 + 2 * qi;
-        const int slot = 8 * (lq >> 2);
-        const v4i lo = {(int)pack_lo(x[0], x[1]), (int)pack_lo(x[2], x[3]), (int)pack_lo(y[0], y[1]),
-                        (int)pack_lo(y[2], y[3])};
-        const v4i hi = {(int)pack_hi(x[0], x[1]), (int)pack_hi(x[2], x[3]), (int)pack_hi(y[0], y[1]),
-                        (int)pack_hi(y[2], y[3])};
-        *reinterpret_cast<v4i*>(&vtb[d * VT_STRIDE + slot]) = lo;
-        *reinterpret_cast<v4i*>(&vtb[(d + 1) * VT_STRIDE + slot]) = hi;
+      for (int i = 0; i < 4; ++i) {
+        const float li = fin_s[1][hb * 16 + 4 * lg + i];
+        inv[i] = li > 0.f ? 1.f / li : 0.f;
       }
-      buf[0][c] = nsrc0[c * 4];
-      buf[1][c] = nsrc1[c * 4];
-    }
-    bmask[0] = nmask[0];
-    bmask[1] = nmask[1];
-    sx[vb][0][tid] = s0;
-    sx[vb][1][tid] = s1;
-    lds_barrier();  // V^T and partial scores of this tile complete (double-buffered: one barrier per tile)
-    const v4f o0 = sx[vb][0][tid ^ (4 * 64)], o1 = sx[vb][1][tid ^ (4 * 64)];  // the other channel half
-    // the accumulators hold head lq of tokens 4lg + i (block 0) and 16 + 4lg + i (block 1)
-    float x[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = (vis0 >> (4 * lg + i)) & 1 ? (s0[i] + o0[i]) * P.c2 : -INFINITY;
-      x[4 + i] = (vis1 >> (4 * lg + i)) & 1 ? (s1[i] + o1[i]) * P.c2 : -INFINITY;
-    }
-    float mt = x[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mt = fmaxf(mt, x[i]);
-    // move the exponent reference only when some head's scores got 2^8 above it
-    // (p then stays <= 256); the max over the four lanes of a head is needed
-    // only then.  Both waves of a head block see identical scores.
-    if (__any(mt > m_ref + RESCALE_LOG2)) {
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m_ref, mt);
-      const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_ref - m_new);
-      l_run *= alpha;
-      m_ref = m_new;
-      float al[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * lg + i, 64);
 #pragma unroll
       for (int nb = 0; nb < NBLK; ++nb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[nb][i] *= al[i];
+        for (int i = 0; i < 4; ++i)
+          orow[(size_t)(hb * 16 + 4 * lg + i) * LAT_DIM + d_base + nb * 16 + lq] = o[hb][nb][i] * inv[i];
     }
-    v8h pop;
-    float ps = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = m_ref == -INFINITY ? 0.f : exp2f(x[i] - m_ref);
-      ps += p;
-      pop[i] = (_Float16)p;
-    }
-    l_run += ps;
-#pragma unroll
-    for (int nb = 0; nb < NBLK; ++nb) {
-      const v4i vv = *reinterpret_cast<const v4i*>(&vtb[(half * HALF_DIM + nb * 16 + lq) * VT_STRIDE + lg * 8]);
-      o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, __builtin_bit_cast(v8h, vv), o[nb], 0, 0, 0);
-    }
-  }
-
-  // per-head sum over the four lanes holding the head
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  const int h0 = hb * 16;
-  const int d_base = half * HALF_DIM;
-  if (P.splits == 1) {
-    float inv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float li = __shfl(l_tot, 4 * lg + i, 64);
-      inv[i] = li > 0.f ? 1.f / li : 0.f;
-    }
-    float* orow = P.out + (size_t)r * ATT_HEADS * LAT_DIM;
-#pragma unroll
-    for (int nb = 0; nb < NBLK; ++nb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        orow[(size_t)(h0 + 4 * lg + i) * LAT_DIM + d_base + nb * 16 + lq] = o[nb][i] * inv[i];
-    if (P.lse && half == 0 && lane < 16)
-      P.lse[(size_t)r * ATT_HEADS + h0 + lq] = l_tot > 0.f ? m_ref * LN2 + logf(l_tot) : -INFINITY;
+    if (P.lse && own_tq == 0)
+      P.lse[(size_t)r * ATT_HEADS + own_h] = l_tot > 0.f ? m_ref * LN2 + logf(l_tot) : -INFINITY;
   } else {
     float* op = P.o_part + ((size_t)r * P.splits + split) * ATT_HEADS * LAT_DIM;
 #pragma unroll
-    for (int nb = 0; nb < NBLK; ++nb)
+    for (int hb = 0; hb < HBLK; ++hb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) op[(size_t)(h0 + 4 * lg + i) * LAT_DIM + d_base + nb * 16 + lq] = o[nb][i];
-    if (half == 0 && lane < 16) {
-      float* mp = P.ml_part + (((size_t)r * P.splits + split) * ATT_HEADS + h0 + lq) * 2;
+      for (int nb = 0; nb < NBLK; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          op[(size_t)(hb * 16 + 4 * lg + i) * LAT_DIM + d_base + nb * 16 + lq] = o[hb][nb][i];
+    if (own_tq == 0) {
+      float* mp = P.ml_part + (((size_t)r * P.splits + split) * ATT_HEADS + own_h) * 2;
       mp[0] = l_tot > 0.f ? m_ref : -INFINITY;
       mp[1] = l_tot;
     }
@@ -368,11 +428,11 @@ __global__ __launch_bounds__(128) void k_mla_combine(const MlaPtrs P) {
 }
 
 MlaPlan plan_mla(int32_t rows, int32_t k) {
-  // about 256 workgroups in flight, at least 16 groups (64 tokens) per split
+  // about 256 workgroups in flight, at least 32 groups (four 32-token tiles) per split
   MlaPlan p;
   p.rows = rows;
   int s = (256 + rows - 1) / rows;
-  int smax = (k + 15) / 16;
+  int smax = (k + 31) / 32;
   if (s > smax) s = smax;
   if (s > MAX_SPLITS) s = MAX_SPLITS;
   if (s < 1) s = 1;
