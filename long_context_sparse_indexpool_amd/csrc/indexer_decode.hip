@@ -13,12 +13,14 @@
 // 8-XCD part a device-scope fence writes back the whole L2, which cost more
 // than the streaming itself; the kernel boundary gives coherence for free).
 //
-// k_indexer_score: one workgroup per work tile of 4096 pooled groups (64
-// pages) of one sequence.  Its eight waves stream the tile's int8 keys straight
-// from HBM into v_mfma_i32_32x32x32_i8 operands -- the 32 indexer heads are M
-// (the query stays in registers), 32 groups are N, four MFMAs span the 128
-// channels, each lane loading 64 contiguous bytes of one key, two steps of
-// loads kept in flight.  The epilogue applies ReLU and the head weights exactly
+// k_indexer_score: one workgroup per work tile of 8192 pooled groups (128
+// pages) of one sequence, one workgroup per CU.  Its sixteen waves stream the
+// tile's int8 keys straight from HBM into v_mfma_i32_32x32x32_i8 operands --
+// the 32 indexer heads are M (the query stays in registers), 32 groups are N,
+// four MFMAs span the 128 channels, each lane loading 64 contiguous bytes of
+// one key.  Waves take 32-group chunks from an LDS counter (two chunks of
+// loads in flight per wave), so a wave that the memory system serves slowly
+// does not hold back the workgroup's epilogue.  The epilogue applies ReLU and the head weights exactly
 // in u32 (every partial stays below 2^32) and adds the two lane halves.  The
 // workgroup then keeps only candidates that can still reach the global top-k:
 // it histograms its scores by an 11-bit monotone key, finds the bin of its own
@@ -34,10 +36,7 @@
 
 namespace isa {
 
-constexpr int DEC_THREADS = 512;
-constexpr int DEC_GPS = DEC_THREADS / 2;      // groups per step: 32 per wave
-constexpr int DEC_STEPS = TILE_G / DEC_GPS;
-constexpr int DEC_PF = 2;                // steps of key loads in flight per wave
+constexpr int DEC_THREADS = 1024;
 constexpr int SEL_THREADS = 512;
 constexpr int SEL_CAND = 2048;           // boundary candidates resolved in LDS
 constexpr int SEL_LDS_PAIRS = 8192;      // (bin, count) pairs fetched into LDS in the first round
@@ -64,6 +63,7 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
   __shared__ uint32_t hist[NBINS];  // tile histogram -> emission cursors
   __shared__ uint32_t scr[SCR_WORDS];
   __shared__ int32_t pages[TILE_G / PAGE_GRP];
+  __shared__ uint32_t chunk_ctr;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile = blockIdx.x;
@@ -82,6 +82,7 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
   }
 
   for (int i = tid; i < NBINS; i += DEC_THREADS) hist[i] = 0;
+  if (tid == 0) chunk_ctr = 2 * (DEC_THREADS / 64);
   if (tid < TILE_G / PAGE_GRP) {
     int j = (g0 / PAGE_GRP) + tid;
     pages[tid] = (tid * PAGE_GRP < gN) ? phys_page(P.bt, a.max_pages, a.num_pages, b, j, P.err) : -1;
@@ -112,49 +113,72 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
   }
   __syncthreads();
 
-  // ---- stream the tile: 16 steps of 128 groups (32 per wave) ----
+  // ---- stream the tile: waves take 32-group chunks from an LDS counter ----
+  constexpr int NCH = TILE_G / 32;
+  constexpr int NW = DEC_THREADS / 64;
   const int8_t* kbase = P.pooled + (lane >> 5) * 64;
-  // Tiles walk their steps from different starting points, so that the
-  // workgroups streaming at the same moment do not all sit at the same offset
-  // of their (power-of-two spaced) tiles.
-  const int rot = tile % DEC_STEPS;
-  auto load_step = [&](int step, v4i (&kb)[4]) {
-    int gl = ((step + rot) % DEC_STEPS) * DEC_GPS + wave * 32 + (lane & 31);
-    int pg = pages[gl / PAGE_GRP];
-    if (gl < gN && pg >= 0) {
-      const v4i* p = reinterpret_cast<const v4i*>(kbase + ((size_t)pg * PAGE_GRP + (gl % PAGE_GRP)) * IDX_DIM);
-      kb[0] = p[0];
-      kb[1] = p[1];
-      kb[2] = p[2];
-      kb[3] = p[3];
-    } else {
-      kb[0] = kb[1] = kb[2] = kb[3] = v4i{0, 0, 0, 0};
-    }
+  // Loads are unconditional (a group past the end, or on a page outside the
+  // pool, reads row 0 and is zeroed by its mask), so the compiler waits for
+  // exactly the chunk it consumes.
+  auto load_chunk = [&](int c, v4i (&kb)[4], int& mask) {
+    const int gl = min(c, NCH - 1) * 32 + (lane & 31);
+    const int pg = pages[gl / PAGE_GRP];
+    const bool ok = c < NCH && gl < gN && pg >= 0;
+    mask = ok ? -1 : 0;
+    const size_t row = ok ? (size_t)pg * PAGE_GRP + (gl % PAGE_GRP) : 0;
+    const v4i* p = reinterpret_cast<const v4i*>(kbase + row * IDX_DIM);
+    kb[0] = p[0];
+    kb[1] = p[1];
+    kb[2] = p[2];
+    kb[3] = p[3];
   };
-  v4i buf[DEC_PF + 1][4];
-#pragma unroll
-  for (int s = 0; s < DEC_PF; ++s) load_step(s, buf[s]);
   bool overflow = false;
-#pragma unroll
-  for (int step = 0; step < DEC_STEPS; ++step) {
-    if (step + DEC_PF < DEC_STEPS) load_step(step + DEC_PF, buf[(step + DEC_PF) % (DEC_PF + 1)]);
-    v4i(&cur)[4] = buf[step % (DEC_PF + 1)];
+  auto compute = [&](int c, v4i (&kb)[4], int mask) {
     v16i acc = {0};
-    acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[0], cur[0], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[1], cur[1], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[2], cur[2], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[3], cur[3], acc, 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[q], kb[q] & mask, acc, 0, 0, 0);
     uint32_t s = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s += wv[i] * (uint32_t)max(acc[i], 0);  // ReLU <= 2,064,512 < 2^24
     s += __shfl_xor(s, 32, 64);
-    const int gl = ((step + rot) % DEC_STEPS) * DEC_GPS + wave * 32 + (lane & 31);
+    const int gl = c * 32 + (lane & 31);
     if (lane < 32) {
       bool valid = gl < gN;
       sc[gl] = valid ? s : INVALID_SCORE;
       if (valid && !dense) atomicAdd(&hist[score_bin(s)], 1u);  // histogram built while streaming
       overflow |= valid && s > 0x7FFFFFFFu;
       if (P.scores_out && valid) P.scores_out[(size_t)b * P.ld_scores + g0 + gl] = (int32_t)s;
+    }
+  };
+  auto grab = [&]() -> int {
+    uint32_t v = 0;
+    if (lane == 0) v = atomicAdd(&chunk_ctr, 1u);
+    return __builtin_amdgcn_readfirstlane((int)v);
+  };
+  // two register buffers; a chunk is grabbed when the buffer holding the
+  // previous one is consumed, and the counter only grows, so a wave's current
+  // chunk in A always precedes the one in B
+  v4i bA[4], bB[4];
+  int mA, mB;
+  int cA = wave, cB = wave + NW;
+  load_chunk(cA, bA, mA);
+  __builtin_amdgcn_sched_barrier(0);
+  load_chunk(cB, bB, mB);
+  __builtin_amdgcn_sched_barrier(0);
+  for (;;) {
+    if (cA >= NCH) break;
+    {
+      const int nA = grab();
+      compute(cA, bA, mA);
+      cA = nA;
+      load_chunk(cA, bA, mA);
+    }
+    if (cB >= NCH) break;
+    {
+      const int nB = grab();
+      compute(cB, bB, mB);
+      cB = nB;
+      load_chunk(cB, bB, mB);
     }
   }
   if (__any(overflow) && lane == 0) report(P.err, ISA_DERR_SCORE_OVERFLOW);

@@ -5,7 +5,7 @@
 
 namespace isa {
 
-constexpr int TILE_G = 4096;  // pooled groups per decode work tile (64 pages)
+constexpr int TILE_G = 8192;  // pooled groups per decode work tile (128 pages)
 constexpr int TILE_MAX_PER_SEQ = (ISA_MAX_SEQ_LEN / GROUP + TILE_G - 1) / TILE_G;
 
 constexpr int PAIR_CAP = NBINS;  // (bin, count) pairs a decode tile can emit

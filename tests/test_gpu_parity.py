@@ -78,6 +78,33 @@ def test_topk_decode_without_score_output_matches(ragged_batch):
     assert np.array_equal(idx1, idx2) and np.array_equal(cnt1, cnt2)
 
 
+# sequences spanning several 8192-group scoring tiles, each with a ragged last tile
+MULTI_TILE = [131075, 65536, 32769, 100003, 24581]
+
+
+def test_decode_multi_tile_parity():
+    """Scores, selection and attention where every sequence spans several
+    scoring work tiles (8192 groups each) and ends in a partial tile."""
+    wl = custom("multi_tile", 13, MULTI_TILE, paged_random=True)
+    db = H.make_batch(wl)
+    H.run_pool(db)
+    H.check_pool(db)
+    idx, cnt, sc, _ = H.run_topk(db, with_scores=True)
+    idx2, cnt2, _, _ = H.run_topk(db, with_scores=False)
+    assert np.array_equal(idx, idx2) and np.array_equal(cnt, cnt2)
+    for b in range(wl.batch):
+        S = H.oracle_scores_for(db, b)
+        G = wl.groups(b)
+        assert np.array_equal(sc[b, :G].astype(np.int64), S), f"scores of sequence {b}"
+        H.check_topk_row(S, 512, idx[b], int(cnt[b]))
+    out, lse = H.run_attention(db, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), 512)
+    q, lat, to = db.host["q_attn"], db.host["latent"], wl.token_offsets
+    for b in range(wl.batch):
+        L = wl.lens[b]
+        ref, ref_lse = oracle.attention(q[b], lat[to[b]: to[b + 1]], L, L - 1, idx[b], int(cnt[b]), SM_SCALE)
+        H.attention_tolerance(out[b], ref, lse[b], ref_lse)
+
+
 def _batch_with_keys(name, lens, keys_logical, seed=5, paged=True):
     wl = custom(name, seed, lens, paged_random=paged)
     db = H.make_batch(wl, with_keys=False, with_latent=False)
