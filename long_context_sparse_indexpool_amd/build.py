@@ -17,6 +17,9 @@ SOURCES = ["api.hip", "pool.hip", "indexer_decode.hip", "topk_rows.hip", "mla_de
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
          # packed fp32 instructions are kept out of every kernel
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# per-source additions: the prefill contraction keeps its MFMA accumulators in
+# ordinary VGPRs, so the epilogue reads them without accvgpr moves
+EXTRA_FLAGS = {"score_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def build(verbose: bool = False, resource_usage: bool = False) -> str:
@@ -25,7 +28,7 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if resource_usage:
             cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -45,7 +45,7 @@ int decode_tiles(int32_t L, int32_t k) {
 int pool_tiles(int32_t L) { return (int)((groups_of(L) + POOL_TILE_G - 1) / POOL_TILE_G); }
 
 struct DecodeLayout {
-  size_t tile_meta, tile_pairs, tile_list, total;
+  size_t tile_meta, tile_pairs, tile_list, seq_hist, total;
 };
 DecodeLayout decode_layout(const isa_seqs* s, int32_t k) {
   DecodeLayout d;
@@ -54,7 +54,8 @@ DecodeLayout decode_layout(const isa_seqs* s, int32_t k) {
   d.tile_meta = HDR;
   d.tile_pairs = d.tile_meta + up256((size_t)nt * 8);
   d.tile_list = d.tile_pairs + up256((size_t)nt * PAIR_CAP * 4);
-  d.total = d.tile_list + up256((size_t)nt * TILE_G * 8);
+  d.seq_hist = d.tile_list + up256((size_t)nt * TILE_G * 8);
+  d.total = d.seq_hist + up256((size_t)s->batch * NBINS * 4);
   return d;
 }
 
@@ -206,7 +207,7 @@ isa_status isa_indexer_topk(const int8_t* q, const int8_t* head_w, const int8_t*
   a.tile_start[s->batch] = t;
   char* base = (char*)ws;
   DecodeWs w{(uint32_t*)base, (uint2*)(base + d.tile_meta), (uint32_t*)(base + d.tile_pairs),
-             (uint64_t*)(base + d.tile_list)};
+             (uint64_t*)(base + d.tile_list), (uint32_t*)(base + d.seq_hist)};
   return launch_indexer_decode(a, q, head_w, pooled, s->block_table, w, out_idx, out_count, scores_out, ld_scores,
                                (hipStream_t)stream);
 }

@@ -51,6 +51,7 @@ struct DecodePtrs {
   uint2* tile_meta;     // [ntiles] (candidates, pairs)
   uint32_t* tile_pairs; // [ntiles][PAIR_CAP] (bin << 16 | count), descending bins
   uint64_t* tile_list;  // [ntiles][TILE_G] (score << 32 | group), descending bins
+  uint32_t* seq_hist;   // [B][NBINS] candidates per score bin, summed over the tiles; zero between calls
   int32_t* out_idx;     // [B][k]
   int32_t* out_count;   // [B]
   int32_t* scores_out;  // [B][ld] or null
@@ -139,8 +140,8 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
     for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[q], kb[q] & mask, acc, 0, 0, 0);
     uint32_t s = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s += wv[i] * (uint32_t)max(acc[i], 0);  // ReLU <= 2,064,512 < 2^24
-    s += __shfl_xor(s, 32, 64);
+    for (int i = 0; i < 16; ++i) s += __umul24((uint32_t)max(acc[i], 0), wv[i]);  // ReLU <= 2,064,512 < 2^24: 24-bit multiply
+    s += __builtin_amdgcn_permlane32_swap(s, s, false, false)[1];  // lanes < 32: + lane l+32
     const int gl = c * 32 + (lane & 31);
     if (lane < 32) {
       bool valid = gl < gN;
@@ -216,7 +217,10 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
       int bin = hi - 1 - j;
       if (bin < blo) break;
       uint32_t c = hist[bin];
-      if (c) pairs[po++] = ((uint32_t)bin << 16) | c;
+      if (c) {
+        pairs[po++] = ((uint32_t)bin << 16) | c;
+        atomicAdd(&P.seq_hist[(size_t)b * NBINS + bin], c);  // the sequence's candidate histogram
+      }
       hist[bin] = run;
       run += c;
     }
@@ -277,7 +281,8 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
   __shared__ uint32_t bbase[SEL_BUCKETS];
   __shared__ uint32_t bstage[MAX_K];
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NWV = SEL_THREADS / 64;
   const int b = blockIdx.x;
   const int G = (a.lens[b] + GROUP - 1) / GROUP;
   const uint32_t K = (uint32_t)a.k;
@@ -288,7 +293,12 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
   const int lh = min(64, (SEL_LDS_HEAD / nt) & ~1);    // candidates of a tile kept in LDS
   const int pu_per_tile = per / 4, hu_per_tile = lh / 2;
 
-  // 1. one batch of loads
+  // 1. one batch of loads: the sequence's candidate histogram (summed by the
+  //    scoring tiles), every tile's pair count, the head of its (bin, count)
+  //    list and the head of its candidate list
+  static_assert(NBINS == 4 * SEL_THREADS, "one uint4 of the histogram per thread");
+  uint4* gh = reinterpret_cast<uint4*>(P.seq_hist + (size_t)b * NBINS);
+  const uint4 hcnt = gh[tid];
   constexpr int UP = SEL_LDS_PAIRS / 4 / SEL_THREADS, UH = SEL_LDS_HEAD / 2 / SEL_THREADS;
   uint4 pv[UP], hv[UH];
   uint32_t pnp[UP];
@@ -312,8 +322,8 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
   }
   uint32_t my_np = 0;
   if (tid < nt) my_np = P.tile_meta[t0 + tid].y;
-  for (int i = tid; i < NBINS; i += SEL_THREADS) hist[i] = 0;
-  __syncthreads();
+  reinterpret_cast<uint4*>(hist)[tid] = hcnt;
+  gh[tid] = uint4{0u, 0u, 0u, 0u};  // the histogram is zero again for the next call
 #pragma unroll
   for (int k = 0; k < UP; ++k) {
     const int u = tid + k * SEL_THREADS;
@@ -321,13 +331,8 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
       const int j = u / pu_per_tile, part = u % pu_per_tile;
       const uint32_t w[4] = {pv[k].x, pv[k].y, pv[k].z, pv[k].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t p = part * 4 + e;
-        if (p < pnp[k]) {
-          lpairs[j * per + p] = w[e];
-          atomicAdd(&hist[w[e] >> 16], w[e] & 0xFFFFu);
-        }
-      }
+      for (int e = 0; e < 4; ++e)
+        if (part * 4 + e < (int)pnp[k]) lpairs[j * per + part * 4 + e] = w[e];
     }
   }
 #pragma unroll
@@ -339,45 +344,39 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
       lhead[j * lh + part * 2 + 1] = ((uint64_t)hv[k].w << 32) | hv[k].z;
     }
   }
-  // pairs beyond the LDS slice: prefix over tiles, then one flat round
+  // pairs beyond a tile's LDS slice (rare: a tile spread over more than `per`
+  // bins) are read again from global memory, as one flat range over tiles
   {
     const uint32_t o = (tid < nt && my_np > (uint32_t)per) ? my_np - per : 0u;
-    if (tid < nt) {
-      npr[tid] = my_np;
-      ngt[tid] = nbd[tid] = 0;
-    }
+    if (tid < nt) npr[tid] = my_np;
     uint32_t tot;
-    const uint32_t e = block_exclusive_scan(o, scr, &tot);
+    const uint32_t e = block_exclusive_scan(o, scr, &tot);  // (its barriers also publish hist, pairs, heads)
     if (tid < nt) ovf_off[tid] = e;
     if (tid == 0) ovf_off[nt] = tot;
   }
-  __syncthreads();
-  const uint32_t novf = ovf_off[nt];
-  for (uint32_t i = tid; i < novf; i += SEL_THREADS) {
-    const int j = owner_of(ovf_off, nt, i);
-    const uint32_t w = P.tile_pairs[(size_t)(t0 + j) * PAIR_CAP + per + (i - ovf_off[j])];
-    atomicAdd(&hist[w >> 16], w & 0xFFFFu);
-  }
-  __syncthreads();
   int bstar;
   uint32_t n_gt, total;
   find_boundary(hist, K, &bstar, &n_gt, &total, scr);
   // bstar >= 0: the tiles together kept at least k candidates.
   const uint32_t m = K - n_gt;
-  // 2. per tile: candidates above the boundary bin and in it (one thread walks
-  //    its tile's pairs, highest bin first, and stops below the boundary)
-  if (tid < nt) {
-    const uint32_t np = min(npr[tid], (uint32_t)per);
+  const uint32_t novf = ovf_off[nt];
+  // 2. per tile: candidates above the boundary bin and in it -- one wave per
+  //    tile sums its pairs (a tile's pairs cover distinct bins)
+  for (int j = wave; j < nt; j += NWV) {
+    const uint32_t np = min(npr[j], (uint32_t)per);
     uint32_t g_ = 0, d_ = 0;
-    for (uint32_t p = 0; p < np; ++p) {
-      const uint32_t w = lpairs[tid * per + p];
+    if ((uint32_t)lane < np) {
+      const uint32_t w = lpairs[j * per + lane];
       const int bin = (int)(w >> 16);
-      if (bin < bstar) break;
-      if (bin > bstar) g_ += w & 0xFFFFu;
-      else d_ = w & 0xFFFFu;
+      if (bin > bstar) g_ = w & 0xFFFFu;
+      else if (bin == bstar) d_ = w & 0xFFFFu;
     }
-    ngt[tid] = g_;
-    nbd[tid] = d_;
+    g_ = __builtin_amdgcn_readlane((int)wave_inclusive_scan(g_), 63);
+    d_ = __builtin_amdgcn_readlane((int)wave_inclusive_scan(d_), 63);
+    if (lane == 0) {
+      ngt[j] = g_;
+      nbd[j] = d_;
+    }
   }
   __syncthreads();
   for (uint32_t i = tid; i < novf; i += SEL_THREADS) {
@@ -387,7 +386,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
     if (bin > bstar) atomicAdd(&ngt[j], w & 0xFFFFu);
     else if (bin == bstar) nbd[j] = w & 0xFFFFu;
   }
-  __syncthreads();
+  if (novf) __syncthreads();  // uniform
   {
     const uint32_t g_ = tid < nt ? ngt[tid] : 0u, d_ = tid < nt ? nbd[tid] : 0u;
     uint32_t tg, tb;
@@ -403,24 +402,30 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
     }
   }
   __syncthreads();
-  // 3. candidates
-  const uint32_t nsure = sure_off[nt];
+  // 3. candidates: one wave per tile copies the tile's entries above the
+  //    boundary bin to the selection and its boundary-bin entries (as
+  //    (score, -id) keys) to the boundary list (both are prefixes of the
+  //    tile's bin-ordered list, read from its LDS head where possible)
   const uint32_t nbnd = bnd_off[nt];
   auto entry = [&](int j, uint32_t e) -> uint64_t {  // e-th candidate of tile j
     return e < (uint32_t)lh ? lhead[j * lh + e] : P.tile_list[(size_t)(t0 + j) * TILE_G + e];
   };
-  for (uint32_t i = tid; i < nsure && i < MAX_K; i += SEL_THREADS) {
-    const int j = owner_of(sure_off, nt, i);
-    sel[i] = (uint32_t)entry(j, i - sure_off[j]);
+  const bool in_lds = nbnd <= SEL_CAND;
+  for (int j = wave; j < nt; j += NWV) {
+    const uint32_t gj = ngt[j], nj = gj + (in_lds ? nbd[j] : 0u);
+    const uint32_t so = sure_off[j], bo = bnd_off[j];
+    for (uint32_t e = lane; e < nj; e += 64) {
+      const uint64_t ent = entry(j, e);
+      if (e < gj) sel[so + e] = (uint32_t)ent;
+      else cand[bo + (e - gj)] = rank_key(key_score(ent), (uint32_t)ent);
+    }
   }
+  const uint32_t nsure = sure_off[nt];
   auto bnd_key = [&](uint32_t i) -> uint64_t {
     const int j = owner_of(bnd_off, nt, i);
     const uint64_t e = entry(j, ngt[j] + (i - bnd_off[j]));
     return rank_key(key_score(e), (uint32_t)e);
   };
-  const bool in_lds = nbnd <= SEL_CAND;
-  if (in_lds)
-    for (uint32_t i = tid; i < nbnd; i += SEL_THREADS) cand[i] = bnd_key(i);
   __syncthreads();
   // 4. the m best boundary candidates
   if (in_lds) {
@@ -504,8 +509,8 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
 isa_status launch_indexer_decode(const BatchArgs& a, const int8_t* q, const int8_t* hw, const int8_t* pooled,
                                  const int32_t* bt, const DecodeWs& w, int32_t* out_idx, int32_t* out_count,
                                  int32_t* scores_out, int32_t ld_scores, hipStream_t stream) {
-  DecodePtrs P{q, hw, pooled, bt, w.tile_meta, w.tile_pairs, w.tile_list, out_idx, out_count, scores_out,
-               ld_scores, w.err};
+  DecodePtrs P{q, hw, pooled, bt, w.tile_meta, w.tile_pairs, w.tile_list, w.seq_hist, out_idx, out_count,
+               scores_out, ld_scores, w.err};
   const int ntiles = a.tile_start[a.batch];
   timer_begin(ISA_TIMER_INDEXER_SCORE, stream);
   hipLaunchKernelGGL(k_indexer_score, dim3(ntiles), dim3(DEC_THREADS), 0, stream, a, P);

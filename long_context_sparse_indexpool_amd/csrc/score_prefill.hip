@@ -27,7 +27,7 @@ namespace isa {
 constexpr int PF_THREADS = 256;
 constexpr int PF_QW = 4;                      // queries per wave
 constexpr int PF_QB = PF_QW * (PF_THREADS / 64);  // queries per workgroup
-constexpr int PF_GT = 1024;                   // groups per workgroup
+constexpr int PF_GT = 4096;                   // groups per workgroup
 constexpr int N_XCD = 8;
 
 struct PrefillPtrs {
@@ -46,7 +46,8 @@ struct PrefillPtrs {
 
 __global__ __launch_bounds__(PF_THREADS) void k_prefill_scores(const BatchArgs a, const PrefillPtrs P) {
   __shared__ int32_t pages[PF_GT / PAGE_GRP];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: query indices and bases stay scalar
   const int xcd = blockIdx.x % N_XCD;
   const int i = blockIdx.x / N_XCD;
   const int qb = i % P.n_qb;
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_scores(const BatchArgs a
 
   // this wave's queries: operands, head weights of the accumulator rows, visible range
   v4i qa[PF_QW][4];
-  uint32_t wv[PF_QW][16];
+  uint32_t wv[PF_QW][8];  // head weights of the accumulator rows, two 16-bit halves per register
   int lastg[PF_QW];
   bool bad = false;
 #pragma unroll
@@ -80,63 +81,102 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_scores(const BatchArgs a
     for (int r = 0; r < 16; ++r) {
       int w = hp[(r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)];
       bad |= (w < 0) | (w > 64);
-      wv[qq][r] = (uint32_t)w;
+      wv[qq][r >> 1] = (r & 1) ? (wv[qq][r >> 1] | ((uint32_t)w << 16)) : (uint32_t)w;
     }
     int p = P.q_pos[qc];
     if (live && (p < 0 || p >= L)) {
       bad = true;
       p = -4;
     }
-    lastg[qq] = live ? p / GROUP : -2;  // -2: query beyond Q, nothing stored
+    lastg[qq] = __builtin_amdgcn_readfirstlane(live ? p / GROUP : -2);  // -2: query beyond Q, nothing stored
   }
   if (__any(bad) && lane == 0) report(P.err, ISA_DERR_HEADW_RANGE | ISA_DERR_ROW_RANGE);
   __syncthreads();
 
   const int8_t* kbase = P.pooled + (lane >> 5) * 64;
-  auto load_blk = [&](int blk, v4i (&kb)[4]) {
-    int gl = blk * 32 + (lane & 31);
-    int pg = gl < gN ? pages[gl / PAGE_GRP] : -1;
-    if (pg >= 0) {
-      const v4i* p = reinterpret_cast<const v4i*>(kbase + ((size_t)pg * PAGE_GRP + gl % PAGE_GRP) * IDX_DIM);
-      kb[0] = p[0];
-      kb[1] = p[1];
-      kb[2] = p[2];
-      kb[3] = p[3];
-    } else {
-      kb[0] = kb[1] = kb[2] = kb[3] = v4i{0, 0, 0, 0};
+  // Loads are unconditional (a group past the range, or on a page outside the
+  // pool, reads row 0 and is zeroed by its mask) and the two register buffers
+  // alternate by block parity, so each block waits for its own loads only.
+  auto load_blk = [&](int blk, v4i (&kb)[4], int& mask) {
+    const int gi = blk * 32 + (lane & 31);
+    const int gl = min(gi, PF_GT - 1);
+    const int pg = pages[gl / PAGE_GRP];
+    const bool ok = gi < gN && pg >= 0;
+    mask = ok ? -1 : 0;
+    const size_t row = ok ? (size_t)pg * PAGE_GRP + gl % PAGE_GRP : 0;
+    const v4i* p = reinterpret_cast<const v4i*>(kbase + row * IDX_DIM);
+    kb[0] = p[0];
+    kb[1] = p[1];
+    kb[2] = p[2];
+    kb[3] = p[3];
+  };
+  // each query's score row as a buffer resource (scalar base, 32-bit offsets,
+  // stores past the row's end dropped by the range check)
+  __amdgpu_buffer_rsrc_t rows[PF_QW];
+#pragma unroll
+  for (int qq = 0; qq < PF_QW; ++qq) {
+    const int qi = min(qb * PF_QB + wave * PF_QW + qq, P.Q - 1);
+    rows[qq] = __builtin_amdgcn_make_buffer_rsrc(P.scores + (size_t)qi * P.ld, 0, (g0 + gN) * 4, 0x00020000);
+  }
+  uint32_t smax = 0;  // largest visible score of this lane (overflow check after the loop)
+  // score of the lane's group for query qq from its 32 x 32 accumulator block:
+  // the lane holds 16 heads of group l%32; the other 16 are in lane l^32.
+  // gb: first group of the block (uniform)
+  auto epilogue = [&](const v16i& acc, int qq, int gb) {
+    uint32_t s = 0;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2)  // ReLU <= 2^21: 24-bit multiplies by the packed weights
+      s += __umul24((uint32_t)max(acc[r], 0), wv[qq][r >> 1] & 0xFFFFu) +
+           __umul24((uint32_t)max(acc[r + 1], 0), wv[qq][r >> 1] >> 16);
+    s += __builtin_amdgcn_permlane32_swap(s, s, false, false)[1];  // lanes < 32: + lane l+32
+    const int lg = lastg[qq];
+    if (lg == -2) return;  // uniform: query beyond Q
+    const int g = gb + (lane & 31);
+    const bool vis = g <= lg;
+    smax = max(smax, vis ? s : 0u);
+    if (lane < 32)  // groups past the sequence fall outside the row's range and are dropped
+      __builtin_amdgcn_raw_buffer_store_b32(vis ? (int32_t)s : -1, rows[qq], g * 4, 0, 2 /* nontemporal */);
+  };
+  // one block of 32 groups for the wave's queries; the MFMAs of the next query
+  // are issued before the epilogue of the current one, so the matrix core and
+  // the VALU work side by side
+  auto do_blk = [&](int blk, const v4i (&kb)[4], int mask) {
+    const int g = g0 + blk * 32;
+    const v4i k[4] = {kb[0] & mask, kb[1] & mask, kb[2] & mask, kb[3] & mask};
+    auto mm = [&](int qq) {
+      v16i acc = {0};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[qq][c], k[c], acc, 0, 0, 0);
+      return acc;
+    };
+    static_assert(PF_QW % 2 == 0, "queries are pipelined in pairs");
+    v16i a0 = mm(0), a1;
+#pragma unroll
+    for (int qq = 0; qq < PF_QW; qq += 2) {
+      a1 = mm(qq + 1);
+      epilogue(a0, qq, g);
+      if (qq + 2 < PF_QW) a0 = mm(qq + 2);
+      epilogue(a1, qq + 1, g);
     }
   };
   const int nblk = (gN + 31) / 32;
-  v4i cur[4], nxt[4];
-  load_blk(0, cur);
-  bool overflow = false;
-  for (int blk = 0; blk < nblk; ++blk) {
-    if (blk + 1 < nblk) load_blk(blk + 1, nxt);
-    const int g = g0 + blk * 32 + (lane & 31);
-#pragma unroll
-    for (int qq = 0; qq < PF_QW; ++qq) {
-      v16i acc = {0};
-      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[qq][0], cur[0], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[qq][1], cur[1], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[qq][2], cur[2], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[qq][3], cur[3], acc, 0, 0, 0);
-      uint32_t s = 0;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s += wv[qq][r] * (uint32_t)max(acc[r], 0);
-      s += __shfl_xor(s, 32, 64);
-      if (lane < 32 && g < g0 + gN && lastg[qq] != -2) {
-        int qi = qb * PF_QB + wave * PF_QW + qq;
-        bool vis = g <= lastg[qq];
-        overflow |= vis && s > 0x7FFFFFFFu;
-        __builtin_nontemporal_store(vis ? (int32_t)s : -1, P.scores + (size_t)qi * P.ld + g);
-      }
-    }
-    cur[0] = nxt[0];
-    cur[1] = nxt[1];
-    cur[2] = nxt[2];
-    cur[3] = nxt[3];
+  v4i bA[4], bB[4], bC[4];
+  int mA, mB, mC;
+  load_blk(0, bA, mA);
+  __builtin_amdgcn_sched_barrier(0);
+  load_blk(1, bB, mB);
+  __builtin_amdgcn_sched_barrier(0);
+  load_blk(2, bC, mC);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int blk = 0; blk < nblk; blk += 3) {  // trailing blocks past the range store nothing
+    do_blk(blk, bA, mA);
+    load_blk(blk + 3, bA, mA);
+    do_blk(blk + 1, bB, mB);
+    load_blk(blk + 4, bB, mB);
+    do_blk(blk + 2, bC, mC);
+    load_blk(blk + 5, bC, mC);
   }
-  if (__any(overflow) && lane == 0) report(P.err, ISA_DERR_SCORE_OVERFLOW);
+  if (__any(lane < 32 && smax > 0x7FFFFFFFu) && lane == 0) report(P.err, ISA_DERR_SCORE_OVERFLOW);  // (lanes >= 32 hold doubled sums)
 }
 
 isa_status launch_prefill_scores(const BatchArgs& a, const int8_t* q, const int8_t* hw, const int32_t* q_pos,
