@@ -137,10 +137,10 @@ class Decode:
 
     def time_kernel_events(self, steps):
         """Average durations of the scoring kernel and of the attention kernel over
-        `steps` more back-to-back steps: HIP events that the library records just
-        before and after those two launches, on the stream it launches on.  This
-        pass is separate from the headline timing because the four event records
-        per step slow the step itself."""
+        `steps` more back-to-back steps: HIP events that the library attaches to
+        those two dispatches (hipExtLaunchKernelGGL), on the stream it launches
+        on.  This pass is separate from the headline timing so that the timed
+        steps carry no instrumentation."""
         torch, m = self.torch, self.m
         n = min(steps, 4096)
         evs = {k: ([torch.cuda.Event(enable_timing=True) for _ in range(n)],

@@ -109,9 +109,10 @@ const char* isa_version(void);
 
 /* Kernel timing hook, for benchmarks.  `starts` and `stops` [host] are arrays
  * of n hipEvent_t handles, or NULL with n = 0 to switch the hook off.  While it
- * is set, the i-th later launch of `kernel` (counting from this call) records
- * starts[i % n] on the call's stream just before the launch and stops[i % n]
- * just after it, so hipEventElapsedTime gives that launch's own duration.  The
+ * is set, the i-th later launch of `kernel` (counting from this call) is
+ * dispatched with starts[i % n] / stops[i % n] as its start and stop events
+ * (hipExtLaunchKernelGGL), so hipEventElapsedTime gives that kernel's own
+ * execution time.  The
  * arrays are copied (at most 4096 pairs); the events stay the caller's.  The
  * setting is process-wide and not thread-safe.  ISA_ERR_INVALID_ARG for an
  * unknown kernel id, n outside 0..4096 or a NULL handle. */

@@ -512,10 +512,9 @@ isa_status launch_indexer_decode(const BatchArgs& a, const int8_t* q, const int8
   DecodePtrs P{q, hw, pooled, bt, w.tile_meta, w.tile_pairs, w.tile_list, w.seq_hist, out_idx, out_count,
                scores_out, ld_scores, w.err};
   const int ntiles = a.tile_start[a.batch];
-  timer_begin(ISA_TIMER_INDEXER_SCORE, stream);
-  hipLaunchKernelGGL(k_indexer_score, dim3(ntiles), dim3(DEC_THREADS), 0, stream, a, P);
-  if (hipGetLastError() != hipSuccess) return ISA_ERR_HIP;
-  timer_end(ISA_TIMER_INDEXER_SCORE, stream);
+  if (launch_timed(ISA_TIMER_INDEXER_SCORE, k_indexer_score, dim3(ntiles), dim3(DEC_THREADS), stream, a, P) !=
+      hipSuccess)
+    return ISA_ERR_HIP;
   bool any_sparse = false;
   for (int b = 0; b < a.batch; ++b) any_sparse |= (a.lens[b] + GROUP - 1) / GROUP > a.k;
   if (any_sparse) {

@@ -1,6 +1,8 @@
 // isa_launch.hpp -- host-side launchers of the gfx950 kernels (internal to libisa).
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "isa_common.hpp"
 
 namespace isa {
@@ -54,24 +56,25 @@ isa_status launch_prefill_scores(const BatchArgs& a, const int8_t* q, const int8
 
 isa_status launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 
-// Benchmark timing hook (isa_set_kernel_timer): a ring of event pairs recorded
-// around the launches of one kernel.
+// Benchmark timing hook (isa_set_kernel_timer): a ring of event pairs that the
+// dispatch itself records (hipExtLaunchKernelGGL), so the elapsed time is the
+// kernel's own execution.
 constexpr int TIMER_MAX = 4096;
 struct KernelTimer {
   int n = 0, next = 0;
   hipEvent_t start[TIMER_MAX], stop[TIMER_MAX];
 };
 extern KernelTimer g_timer[3];
-inline void timer_begin(int k, hipStream_t s) {
-  KernelTimer& t = g_timer[k];
-  if (t.n) (void)hipEventRecord(t.start[t.next], s);
-}
-inline void timer_end(int k, hipStream_t s) {
-  KernelTimer& t = g_timer[k];
+template <class Kernel, class... Args>
+hipError_t launch_timed(int timer, Kernel kernel, dim3 grid, dim3 block, hipStream_t stream, Args... args) {
+  KernelTimer& t = g_timer[timer];
   if (t.n) {
-    (void)hipEventRecord(t.stop[t.next], s);
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, t.start[t.next], t.stop[t.next], 0, args...);
     t.next = (t.next + 1) % t.n;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
   }
+  return hipGetLastError();
 }
 
 }  // namespace isa

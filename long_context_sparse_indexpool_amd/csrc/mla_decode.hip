@@ -447,10 +447,9 @@ isa_status launch_sparse_mla(const BatchArgs& a, const MlaPlan& p, const uint16_
                              float* lse, const MlaWs& w, hipStream_t stream) {
   MlaPtrs P{q, latent, bt, row_seq, row_pos, idx, count, out, lse, w.o_part, w.ml_part, w.err, k,
             sm_scale * LOG2E, p.splits, p.groups_per_split};
-  timer_begin(ISA_TIMER_MLA_SPLIT, stream);
-  hipLaunchKernelGGL(k_mla_split, dim3(p.rows * p.splits), dim3(MLA_THREADS), 0, stream, a, P);
-  if (hipGetLastError() != hipSuccess) return ISA_ERR_HIP;
-  timer_end(ISA_TIMER_MLA_SPLIT, stream);
+  if (launch_timed(ISA_TIMER_MLA_SPLIT, k_mla_split, dim3(p.rows * p.splits), dim3(MLA_THREADS), stream, a, P) !=
+      hipSuccess)
+    return ISA_ERR_HIP;
   if (p.splits > 1) {
     hipLaunchKernelGGL(k_mla_combine, dim3(p.rows * ATT_HEADS), dim3(128), 0, stream, P);
     if (hipGetLastError() != hipSuccess) return ISA_ERR_HIP;
