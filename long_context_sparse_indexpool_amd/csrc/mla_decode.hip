@@ -262,7 +262,7 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
         mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
         const float m_new = fmaxf(m_ref, mt);
-        alpha = m_new == -INFINITY ? 1.f : exp2f(m_ref - m_new);
+        alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
         l_run *= alpha;
         m_ref = m_new;
       }
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
       v4h ph;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float pr = m_ref == -INFINITY ? 0.f : exp2f(x[i] - m_ref);
+        const float pr = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[i] - m_ref);
         ps += pr;
         ph[i] = (_Float16)pr;
       }
@@ -286,7 +286,8 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
     // ---- O[64 heads x this wave's 64 channels] += P V ----
     const uint4 f0 = *reinterpret_cast<const uint4*>(&flag_s[0]);
     const uint4 f1 = *reinterpret_cast<const uint4*>(&flag_s[4]);
-    if ((f0.x | f0.y | f0.z | f0.w | f1.x | f1.y | f1.z | f1.w) != 0u) {
+    // the flags are the same in every lane: a scalar branch
+    if (__builtin_amdgcn_readfirstlane(f0.x | f0.y | f0.z | f0.w | f1.x | f1.y | f1.z | f1.w) != 0u) {
 #pragma unroll
       for (int hb = 0; hb < HBLK; ++hb) {
         const float4 al = *reinterpret_cast<const float4*>(&alpha_s[hb * 16 + 4 * lg]);
