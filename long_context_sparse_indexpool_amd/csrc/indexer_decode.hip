@@ -264,7 +264,6 @@ __device__ __forceinline__ int owner_of(const uint32_t* off, int n, uint32_t i) 
 //     in LDS, or radix select when there are too many -- and the k ids are
 //     placed in ascending order by counting, straight into the output row.
 __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs a, const DecodePtrs P) {
-  __shared__ uint32_t hist[NBINS];
   __shared__ uint32_t lpairs[SEL_LDS_PAIRS];
   __shared__ uint64_t lhead[SEL_LDS_HEAD];
   __shared__ uint32_t npr[TILE_MAX_PER_SEQ];
@@ -289,16 +288,22 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
   if (G <= (int)K) return;  // dense row: written by the scoring kernel
   const int t0 = a.tile_start[b];
   const int nt = a.tile_start[b + 1] - t0;
-  const int per = min(64, (SEL_LDS_PAIRS / nt) & ~3);  // pairs of a tile kept in LDS
-  const int lh = min(64, (SEL_LDS_HEAD / nt) & ~1);    // candidates of a tile kept in LDS
+  constexpr int per = SEL_LDS_PAIRS / TILE_MAX_PER_SEQ;  // pairs of a tile kept in LDS
+  static_assert(per == 64, "one pair per lane of a wave");
+  const int lh_sh = nt <= SEL_LDS_HEAD / 64 ? 6 : 5;     // candidates of a tile kept in LDS: 64, or 32
+  const int lh = 1 << lh_sh;
+  static_assert(SEL_LDS_HEAD / 32 >= TILE_MAX_PER_SEQ, "list heads of every tile fit");
   const int pu_per_tile = per / 4, hu_per_tile = lh / 2;
 
   // 1. one batch of loads: the sequence's candidate histogram (summed by the
   //    scoring tiles), every tile's pair count, the head of its (bin, count)
   //    list and the head of its candidate list
+  //    (thread t holds bins NBINS - 4t - 4 .. NBINS - 4t - 1: ascending threads
+  //    walk the bins in descending order)
   static_assert(NBINS == 4 * SEL_THREADS, "one uint4 of the histogram per thread");
   uint4* gh = reinterpret_cast<uint4*>(P.seq_hist + (size_t)b * NBINS);
-  const uint4 hcnt = gh[tid];
+  const int hq = SEL_THREADS - 1 - tid;
+  const uint4 hcnt = gh[hq];
   constexpr int UP = SEL_LDS_PAIRS / 4 / SEL_THREADS, UH = SEL_LDS_HEAD / 2 / SEL_THREADS;
   uint4 pv[UP], hv[UH];
   uint32_t pnp[UP];
@@ -322,8 +327,12 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
   }
   uint32_t my_np = 0;
   if (tid < nt) my_np = P.tile_meta[t0 + tid].y;
-  reinterpret_cast<uint4*>(hist)[tid] = hcnt;
-  gh[tid] = uint4{0u, 0u, 0u, 0u};  // the histogram is zero again for the next call
+  gh[hq] = uint4{0u, 0u, 0u, 0u};  // the histogram is zero again for the next call
+  for (int i = tid; i < SEL_BUCKETS; i += SEL_THREADS) bcnt[i] = 0;
+  if (tid < nt) {
+    ngt[tid] = 0;
+    nbd[tid] = 0;
+  }
 #pragma unroll
   for (int k = 0; k < UP; ++k) {
     const int u = tid + k * SEL_THREADS;
@@ -344,38 +353,69 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
       lhead[j * lh + part * 2 + 1] = ((uint64_t)hv[k].w << 32) | hv[k].z;
     }
   }
-  // pairs beyond a tile's LDS slice (rare: a tile spread over more than `per`
-  // bins) are read again from global memory, as one flat range over tiles
-  {
-    const uint32_t o = (tid < nt && my_np > (uint32_t)per) ? my_np - per : 0u;
-    if (tid < nt) npr[tid] = my_np;
+  // Suffix counts of the histogram by wave, and the offsets of the pairs
+  // beyond a tile's LDS slice (rare: a tile spread over more than `per` bins),
+  // which are read again from global memory as one flat range over tiles.
+  const uint32_t local = hcnt.x + hcnt.y + hcnt.z + hcnt.w;
+  const uint32_t xin = wave_inclusive_scan(local);
+  if (lane == 63) scr[wave] = xin;
+  const uint32_t o = (tid < nt && my_np > (uint32_t)per) ? my_np - per : 0u;
+  if (tid < nt) npr[tid] = my_np;
+  if (nt <= 64 && wave == 0) {
     uint32_t tot;
-    const uint32_t e = block_exclusive_scan(o, scr, &tot);  // (its barriers also publish hist, pairs, heads)
+    const uint32_t e = wave_exclusive_scan(o, &tot);
     if (tid < nt) ovf_off[tid] = e;
     if (tid == 0) ovf_off[nt] = tot;
   }
+  __syncthreads();  // pairs, list heads, wave sums and offsets published
+  if (nt > 64) {    // uniform: more tiles than one wave scans
+    uint32_t tot;
+    const uint32_t e = block_exclusive_scan(o, scr + NWV, &tot);
+    if (tid < nt) ovf_off[tid] = e;
+    if (tid == 0) ovf_off[nt] = tot;
+    __syncthreads();
+  }
+  // the boundary: the highest bin whose suffix count reaches k
   int bstar;
-  uint32_t n_gt, total;
-  find_boundary(hist, K, &bstar, &n_gt, &total, scr);
+  uint32_t n_gt, total = 0, above = xin - local;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    const uint32_t t_ = scr[w];
+    total += t_;
+    if (w < wave) above += t_;
+  }
+  if (tid == 0 && total < K) {
+    scr[SCR_RES] = 0xFFFFFFFFu;
+    scr[SCR_RES + 1] = total;
+  }
+  if (total >= K && above < K && above + local >= K) {
+    const uint32_t c4[4] = {hcnt.w, hcnt.z, hcnt.y, hcnt.x};
+    uint32_t run = above;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (run + c4[j] >= K) {
+        scr[SCR_RES] = (uint32_t)(4 * hq + 3 - j);
+        scr[SCR_RES + 1] = run;
+        break;
+      }
+      run += c4[j];
+    }
+  }
+  __syncthreads();
+  bstar = (int)scr[SCR_RES];
+  n_gt = scr[SCR_RES + 1];
   // bstar >= 0: the tiles together kept at least k candidates.
   const uint32_t m = K - n_gt;
   const uint32_t novf = ovf_off[nt];
-  // 2. per tile: candidates above the boundary bin and in it -- one wave per
-  //    tile sums its pairs (a tile's pairs cover distinct bins)
-  for (int j = wave; j < nt; j += NWV) {
-    const uint32_t np = min(npr[j], (uint32_t)per);
-    uint32_t g_ = 0, d_ = 0;
-    if ((uint32_t)lane < np) {
-      const uint32_t w = lpairs[j * per + lane];
+  // 2. per tile: candidates above the boundary bin and in it, one thread per
+  //    LDS pair (a tile's pairs cover distinct bins; at most one is the boundary's)
+  for (int i = tid; i < nt * per; i += SEL_THREADS) {
+    const int j = i / per, p = i % per;
+    if ((uint32_t)p < npr[j]) {
+      const uint32_t w = lpairs[i];
       const int bin = (int)(w >> 16);
-      if (bin > bstar) g_ = w & 0xFFFFu;
-      else if (bin == bstar) d_ = w & 0xFFFFu;
-    }
-    g_ = __builtin_amdgcn_readlane((int)wave_inclusive_scan(g_), 63);
-    d_ = __builtin_amdgcn_readlane((int)wave_inclusive_scan(d_), 63);
-    if (lane == 0) {
-      ngt[j] = g_;
-      nbd[j] = d_;
+      if (bin > bstar) atomicAdd(&ngt[j], w & 0xFFFFu);
+      else if (bin == bstar) nbd[j] = w & 0xFFFFu;
     }
   }
   __syncthreads();
@@ -387,7 +427,27 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
     else if (bin == bstar) nbd[j] = w & 0xFFFFu;
   }
   if (novf) __syncthreads();  // uniform
-  {
+  // offsets of each tile's candidates in the selection and the boundary list;
+  // whether a tile has candidates past its LDS head (counted as if every
+  // boundary entry were copied, which covers both resolve paths)
+  if (tid == 0) scr[SCR_RES + 4] = 0;
+  if (nt <= 64) {  // uniform: one wave scans the tiles
+    if (wave == 0) {
+      const uint32_t g_ = tid < nt ? ngt[tid] : 0u, d_ = tid < nt ? nbd[tid] : 0u;
+      uint32_t tg, tb;
+      const uint32_t eg = wave_exclusive_scan(g_, &tg);
+      const uint32_t eb = wave_exclusive_scan(d_, &tb);
+      if (tid < nt) {
+        sure_off[tid] = eg;
+        bnd_off[tid] = eb;
+      }
+      if (tid == 0) {
+        sure_off[nt] = tg;
+        bnd_off[nt] = tb;
+      }
+      if (__any(g_ + d_ > (uint32_t)lh) && tid == 0) scr[SCR_RES + 4] = 1;
+    }
+  } else {
     const uint32_t g_ = tid < nt ? ngt[tid] : 0u, d_ = tid < nt ? nbd[tid] : 0u;
     uint32_t tg, tb;
     const uint32_t eg = block_exclusive_scan(g_, scr, &tg);
@@ -400,26 +460,44 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
       sure_off[nt] = tg;
       bnd_off[nt] = tb;
     }
+    if (g_ + d_ > (uint32_t)lh) scr[SCR_RES + 4] = 1;
   }
   __syncthreads();
+  const bool past_head = scr[SCR_RES + 4] != 0;
   // 3. candidates: one wave per tile copies the tile's entries above the
   //    boundary bin to the selection and its boundary-bin entries (as
   //    (score, -id) keys) to the boundary list (both are prefixes of the
   //    tile's bin-ordered list, read from its LDS head where possible)
   const uint32_t nbnd = bnd_off[nt];
+  // the sequence's candidate lists as a buffer resource: a global load the
+  // compiler cannot merge with the LDS read into one flat access
+  const auto lists = __builtin_amdgcn_make_buffer_rsrc(P.tile_list + (size_t)t0 * TILE_G, 0,
+                                                       nt * TILE_G * 8, 0x00020000);
   auto entry = [&](int j, uint32_t e) -> uint64_t {  // e-th candidate of tile j
-    return e < (uint32_t)lh ? lhead[j * lh + e] : P.tile_list[(size_t)(t0 + j) * TILE_G + e];
+    if (e < (uint32_t)lh) return lhead[j * lh + e];
+    const v2u w = __builtin_amdgcn_raw_buffer_load_b64(lists, (j * TILE_G + (int)e) * 8, 0, 0);
+    return ((uint64_t)w.y << 32) | w.x;
   };
   const bool in_lds = nbnd <= SEL_CAND;
-  for (int j = wave; j < nt; j += NWV) {
-    const uint32_t gj = ngt[j], nj = gj + (in_lds ? nbd[j] : 0u);
-    const uint32_t so = sure_off[j], bo = bnd_off[j];
-    for (uint32_t e = lane; e < nj; e += 64) {
-      const uint64_t ent = entry(j, e);
-      if (e < gj) sel[so + e] = (uint32_t)ent;
-      else cand[bo + (e - gj)] = rank_key(key_score(ent), (uint32_t)ent);
+  auto put = [&](int j, uint32_t e, uint64_t ent) {
+    const uint32_t gj = ngt[j];
+    if (e < gj) sel[sure_off[j] + e] = (uint32_t)ent;
+    else cand[bnd_off[j] + (e - gj)] = rank_key(key_score(ent), (uint32_t)ent);
+  };
+  // one thread per LDS head entry, then the entries past a head (rare) from
+  // global memory, one wave per tile
+  for (int i = tid; i < nt * lh; i += SEL_THREADS) {
+    const int j = i >> lh_sh;
+    const uint32_t e = (uint32_t)(i & (lh - 1));
+    if (e < ngt[j] + (in_lds ? nbd[j] : 0u)) put(j, e, lhead[i]);
+  }
+  if (past_head) {  // uniform
+    for (int j = wave; j < nt; j += NWV) {
+      const uint32_t nj = ngt[j] + (in_lds ? nbd[j] : 0u);
+      for (uint32_t e = lh + lane; e < nj; e += 64) put(j, e, entry(j, e));
     }
   }
+  if (tid == 0 && in_lds && (nbnd & 1)) cand[nbnd] = 0;  // pad to an even count for paired reads (ranks below all)
   const uint32_t nsure = sure_off[nt];
   auto bnd_key = [&](uint32_t i) -> uint64_t {
     const int j = owner_of(bnd_off, nt, i);
@@ -429,19 +507,29 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
   __syncthreads();
   // 4. the m best boundary candidates
   if (in_lds) {
-    if (tid == 0 && (nbnd & 1)) cand[nbnd] = 0;  // pad to an even count for paired reads (ranks below all)
-    __syncthreads();
+    // all-pairs rank: T adjacent lanes per candidate (T = 1 .. 64, the most
+    // that keeps every candidate in one pass when there are few), each
+    // counting over every T-th pair of keys, summed across the T lanes
     const uint32_t npair = (nbnd + 1) / 2;
     const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(cand);
-    for (uint32_t i = tid; i < nbnd; i += SEL_THREADS) {
-      const uint64_t ki = cand[i];
+    int T = 1;
+    while (T < 64 && nbnd * (uint32_t)T * 2 <= (uint32_t)SEL_THREADS) T *= 2;
+    const int per_pass = SEL_THREADS / T;
+    for (uint32_t base = 0; base < nbnd; base += per_pass) {  // uniform
+      const uint32_t i = base + tid / T;
+      const int part = tid % T;
       uint32_t rank = 0;
-#pragma unroll 8
-      for (uint32_t j = 0; j < npair; ++j) {
-        const ulonglong2 v = c2[j];
-        rank += (v.x > ki) + (v.y > ki);
+      uint64_t ki = 0;
+      if (i < nbnd) {
+        ki = cand[i];
+#pragma unroll 4
+        for (uint32_t j = part; j < npair; j += T) {
+          const ulonglong2 v = c2[j];
+          rank += (v.x > ki) + (v.y > ki);
+        }
       }
-      if (rank < m) sel[nsure + rank] = key_id(ki);
+      for (int o = 1; o < T; o <<= 1) rank += __shfl_xor(rank, o, 64);
+      if (i < nbnd && part == 0 && rank < m) sel[nsure + rank] = key_id(ki);
     }
   } else {
     const uint64_t thr = radix_select_threshold(
@@ -461,37 +549,29 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
   }
   __syncthreads();
   // ascending order: counting sort on the high bits of the id (buckets of
-  // 2^sh groups, at most SEL_BUCKETS of them), then a rank inside the bucket
+  // 2^sh groups, at most SEL_BUCKETS of them, zeroed at the start), then a
+  // rank inside the bucket
   int sh = 0;
   while ((G - 1) >> sh >= SEL_BUCKETS) ++sh;
-  const int nbk = ((G - 1) >> sh) + 1;
-  for (int i = tid; i < nbk; i += SEL_THREADS) bcnt[i] = 0;
-  __syncthreads();
   const bool mine = tid < (int)K;
   const uint32_t v = mine ? sel[tid] : 0u;
   const int bk = (int)(v >> sh);
   if (mine) atomicAdd(&bcnt[bk], 1u);
   __syncthreads();
   {
-    constexpr int PB = SEL_BUCKETS / SEL_THREADS;
-    uint32_t c_[PB], sc_ = 0;
+    static_assert(SEL_BUCKETS == 2 * SEL_THREADS, "two buckets per thread");
+    const uint32_t c0 = bcnt[2 * tid], c1 = bcnt[2 * tid + 1], cs = c0 + c1;
+    const uint32_t x = wave_inclusive_scan(cs);
+    if (lane == 63) scr[wave] = x;
+    __syncthreads();
+    uint32_t e = x - cs;
 #pragma unroll
-    for (int r = 0; r < PB; ++r) {
-      const int i = tid * PB + r;
-      c_[r] = i < nbk ? bcnt[i] : 0u;
-      sc_ += c_[r];
-    }
-    uint32_t tot;
-    uint32_t e = block_exclusive_scan(sc_, scr, &tot);
-#pragma unroll
-    for (int r = 0; r < PB; ++r) {
-      const int i = tid * PB + r;
-      if (i < nbk) {
-        bbase[i] = e;
-        bcnt[i] = 0;  // reused as the fill cursor
-      }
-      e += c_[r];
-    }
+    for (int w = 0; w < NWV; ++w)
+      if (w < wave) e += scr[w];
+    bbase[2 * tid] = e;
+    bbase[2 * tid + 1] = e + c0;
+    bcnt[2 * tid] = 0;  // reused as the fill cursor
+    bcnt[2 * tid + 1] = 0;
   }
   __syncthreads();
   if (mine) bstage[bbase[bk] + atomicAdd(&bcnt[bk], 1u)] = v;

@@ -37,6 +37,7 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 // Per-call description of the batch, passed by value in the kernel arguments so
 // that no host-to-device copy is needed: lengths and a tile prefix per sequence.
@@ -104,6 +105,14 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
   x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
   x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return x;
+}
+
+// Exclusive prefix sum over the lanes of one wave; *total receives the wave's
+// sum (the same in every lane).
+__device__ __forceinline__ uint32_t wave_exclusive_scan(uint32_t v, uint32_t* total) {
+  const uint32_t x = wave_inclusive_scan(v);
+  *total = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+  return x - v;
 }
 
 // Block-wide exclusive prefix sum of one value per thread (blockDim.x <= 1024,
