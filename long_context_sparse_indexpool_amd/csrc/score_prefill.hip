@@ -12,14 +12,17 @@
 // Scores of Q queries x G groups: [Q*32, 128] x [128, G] int8 -> int32, then
 // S[q][g] = sum_h w[q][h] * max(0, acc[q,h][g]).  v_mfma_i32_32x32x32_i8 with a
 // query's 32 heads as M and 32 groups as N; four MFMAs cover the 128 channels.
-// Each wave keeps 4 queries' operands and head weights in registers and
-// streams 32-group key blocks through them; the epilogue is two VALU ops per
-// element (max, 24-bit multiply-add) plus one cross-half add, which costs about
-// as much issue time as the MFMAs, so waves interleave the two.  A workgroup
-// covers 16 queries x 1024 groups.  Workgroups are numbered so that every
-// query block of one group range lands on the same XCD (dispatch is
-// round-robin over the 8 XCDs): the range's 128 KiB of keys is then fetched
-// into that XCD's L2 once and reused by all query blocks.
+// Each wave keeps 4 queries' operands and head weights (two 16-bit weights per
+// register) in registers and streams 32-group key blocks through them, three
+// blocks of loads in flight; the accumulators live in VGPRs.  The epilogue is
+// two VALU ops per element (max, 24-bit multiply-add with the weight's half
+// selected in the instruction) plus one cross-half add, which costs about as
+// much issue time as the MFMAs, so each wave issues the MFMAs of its next query
+// before the epilogue of the current one.  A workgroup covers 16 queries x
+// 4096 groups.  Workgroups are numbered so that every query block of one group
+// range lands on the same XCD (dispatch is round-robin over the 8 XCDs): the
+// range's 512 KiB of keys is then fetched into that XCD's L2 once and reused
+// by all query blocks.
 #include "isa_launch.hpp"
 
 namespace isa {
