@@ -184,6 +184,55 @@ class Decode:
         self.torch.cuda.empty_cache()
 
 
+def bench_index_share(dec, n_layers=4, steps=100, warmup=10):
+    """IndexShare on the headline workload: one indexer call and the attention
+    of n_layers layers over its selection, (a) in one shared call, (b) as
+    n_layers single-layer calls.  Layer l >= 1 has its own query and a latent
+    pool of its own (a device copy of layer 0's with sign-flipped channels)."""
+    import numpy as np
+    import torch
+
+    import harness as H
+    from synth.configs import SM_SCALE
+
+    m, wl = dec.m, dec.wl
+    B = wl.batch
+    pools = H.layer_latents(dec.db, n_layers)
+    qs = [torch.from_numpy(wl.q_attn(0, B, layer=l).view(np.int16)).cuda() for l in range(n_layers)]
+    outs = [torch.empty((B, 64, 512), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
+    lses = [torch.empty((B, 64), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
+    ws_sh = m.alloc_workspace(m.workspace_size(m.ISA_OP_SPARSE_MLA, dec.db.seqs, B, n_layers))
+
+    def shared(j):
+        dec.topk(j)
+        m.isa_sparse_mla_decode_shared(qs, pools, dec.db.seqs, None, None, B, dec.idx, dec.cnt, dec.k, SM_SCALE,
+                                       outs, lses, ws_sh)
+
+    def separate(j):
+        dec.topk(j)
+        for l in range(n_layers):
+            m.isa_sparse_mla_decode(qs[l], pools[l], dec.db.seqs, None, None, B, dec.idx, dec.cnt, dec.k, SM_SCALE,
+                                    outs[l], lses[l], dec.ws_att)
+
+    res = {"layers": n_layers}
+    for name, fn in (("shared", shared), ("separate", separate)):
+        for j in range(warmup):
+            fn(j)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for j in range(steps):
+            fn(j)
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / steps
+        res[f"steps_per_s_{name}"] = round(1 / sec, 1)
+        res[f"ms_per_step_{name}"] = round(sec * 1e3, 4)
+    del pools, qs, outs, lses, ws_sh
+    torch.cuda.empty_cache()
+    log(f"{wl.name}: IndexShare over {n_layers} layers: {res['steps_per_s_shared']} steps/s in one call, "
+        f"{res['steps_per_s_separate']} with separate calls")
+    return res
+
+
 def oracle_step_time(dec, min_s=10.0, budget_s=25.0):
     """The CPU oracle on whole decode steps of the same workload: scores of every
     group, top-512 selection and 64-head attention for each sequence, from the
@@ -439,6 +488,7 @@ def main():
     secondary = {}
     if not args.primary_only:
         secondary["indexpool"] = bench_pool(dec)
+        secondary["index_share"] = bench_index_share(dec)
     dec.free()
     if not args.primary_only:
         for i in (1, 4):

@@ -77,6 +77,7 @@ typedef enum {
 
 #define ISA_MAX_BATCH 256          /* sequences per call */
 #define ISA_MAX_SEQ_LEN (1 << 22)  /* tokens per sequence */
+#define ISA_MAX_LAYERS 8           /* layers sharing one selection (isa_sparse_mla_decode_shared) */
 #define ISA_MAX_K 512              /* groups selected per row */
 
 /* One batch of sequences that share page pools. */
@@ -93,8 +94,9 @@ enum { ISA_OP_INDEXPOOL = 1, ISA_OP_INDEXER_TOPK = 2, ISA_OP_SPARSE_MLA = 3, ISA
 
 /* Workspace bytes (a multiple of 256) that `op` needs for these sequences.
  * rows: query rows (attention and top-k from precomputed scores; ignored
- * otherwise); cols: score columns per row for top-k from precomputed scores.
- * Returns 0 for invalid arguments. */
+ * otherwise); cols: for ISA_OP_SPARSE_MLA the number of layers attended in one
+ * call of isa_sparse_mla_decode_shared (0 or 1 for isa_sparse_mla_decode),
+ * ignored otherwise.  Returns 0 for invalid arguments. */
 size_t isa_workspace_size(int op, const isa_seqs* s, int32_t rows, int32_t cols);
 
 /* Zero-fill a workspace on `stream` (needed once, before its first use). */
@@ -194,6 +196,27 @@ isa_status isa_sparse_mla_decode(const uint16_t* q, const uint16_t* latent, cons
                                  const int32_t* row_seq, const int32_t* row_pos, int32_t rows,
                                  const int32_t* idx, const int32_t* count, int32_t k, float sm_scale,
                                  float* out, float* lse, void* ws, size_t ws_bytes, isa_stream_t stream);
+
+/*
+ * (5) IndexShare: the attention of n_layers layers that reuse one selection
+ * ([REMIO] section on IndexShare: one indexer per group of four sparse
+ * attention layers; the other layers of the group attend over the positions it
+ * selected).  One call does what n_layers calls of isa_sparse_mla_decode with
+ * the same idx, count, rows, positions and block table would do, each layer
+ * with its own query and latent pool (same page geometry, same block table);
+ * the selected rows' page translation is done once for all layers.
+ *   n_layers      1..ISA_MAX_LAYERS
+ *   q, latent, out  [host] arrays of n_layers device pointers, each laid out as
+ *                 the single-layer call's argument of the same name
+ *   lse           NULL, or [host] array of n_layers device pointers (none NULL)
+ * Other arguments, results and errors as isa_sparse_mla_decode; the workspace
+ * is isa_workspace_size(ISA_OP_SPARSE_MLA, s, rows, n_layers).
+ */
+isa_status isa_sparse_mla_decode_shared(int32_t n_layers, const uint16_t* const* q, const uint16_t* const* latent,
+                                        const isa_seqs* s, const int32_t* row_seq, const int32_t* row_pos,
+                                        int32_t rows, const int32_t* idx, const int32_t* count, int32_t k,
+                                        float sm_scale, float* const* out, float* const* lse, void* ws,
+                                        size_t ws_bytes, isa_stream_t stream);
 
 /*
  * (4) Prefill indexer scores of Q queries of one sequence (s->batch == 1)

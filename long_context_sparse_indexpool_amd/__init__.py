@@ -27,13 +27,14 @@ MAX_BATCH, MAX_SEQ_LEN, MAX_K = 256, 1 << 22, 512
 ISA_OK, ISA_ERR_INVALID_ARG, ISA_ERR_UNSUPPORTED, ISA_ERR_WORKSPACE, ISA_ERR_HIP = range(5)
 ISA_OP_INDEXPOOL, ISA_OP_INDEXER_TOPK, ISA_OP_SPARSE_MLA, ISA_OP_PREFILL_SCORES = 1, 2, 3, 4
 ISA_SCALE_DYNAMIC, ISA_SCALE_GIVEN = 0, 1
+ISA_MAX_LAYERS = 8  # layers sharing one selection (isa_sparse_mla_decode_shared)
 DERR_PAGE_OOB, DERR_HEADW_RANGE, DERR_SCORE_OVERFLOW, DERR_ROW_RANGE, DERR_NONFINITE = 1, 2, 4, 8, 16
 
 ISA_TIMER_INDEXER_SCORE, ISA_TIMER_MLA_SPLIT = 1, 2
 
 EXPORTS = ("isa_workspace_size", "isa_workspace_init", "isa_device_error", "isa_status_string", "isa_version",
            "isa_set_kernel_timer", "isa_indexpool", "isa_indexer_topk", "isa_sparse_mla_decode",
-           "isa_indexer_prefill_scores")
+           "isa_sparse_mla_decode_shared", "isa_indexer_prefill_scores")
 
 
 class IsaError(RuntimeError):
@@ -65,9 +66,11 @@ def _load() -> ctypes.CDLL:
     lib.isa_indexpool.argtypes = [vp, vp, sp, vp, vp, u32, vp, sz, vp]
     lib.isa_indexer_topk.argtypes = [vp, vp, vp, sp, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.isa_sparse_mla_decode.argtypes = [vp, vp, sp, vp, vp, i32, vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp]
+    lib.isa_sparse_mla_decode_shared.argtypes = [i32, vp, vp, sp, vp, vp, i32, vp, vp, i32, ctypes.c_float, vp, vp,
+                                                 vp, sz, vp]
     lib.isa_indexer_prefill_scores.argtypes = [vp, vp, vp, i32, vp, sp, vp, i32, vp, sz, vp]
     for f in ("isa_workspace_init", "isa_device_error", "isa_set_kernel_timer", "isa_indexpool", "isa_indexer_topk",
-              "isa_sparse_mla_decode", "isa_indexer_prefill_scores"):
+              "isa_sparse_mla_decode", "isa_sparse_mla_decode_shared", "isa_indexer_prefill_scores"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -190,6 +193,29 @@ def isa_sparse_mla_decode(q: torch.Tensor, latent: torch.Tensor, seqs: Seqs, row
         _ptr(row_pos, torch.int32, "row_pos"), rows, _ptr(idx, torch.int32, "idx"),
         _ptr(count, torch.int32, "count"), k, float(sm_scale), _ptr(out, torch.float32, "out"),
         _ptr(lse, torch.float32, "lse"), _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
+
+
+def isa_sparse_mla_decode_shared(q: Sequence[torch.Tensor], latent: Sequence[torch.Tensor], seqs: Seqs,
+                                 row_seq: Optional[torch.Tensor], row_pos: Optional[torch.Tensor], rows: int,
+                                 idx: torch.Tensor, count: torch.Tensor, k: int, sm_scale: float,
+                                 out: Sequence[torch.Tensor], lse: Optional[Sequence[torch.Tensor]], ws: torch.Tensor,
+                                 stream=None) -> None:
+    """Attention of len(q) layers that reuse one selection: lists of per-layer
+    tensors, laid out as the arguments of isa_sparse_mla_decode."""
+    n = len(q)
+    if len(latent) != n or len(out) != n or (lse is not None and len(lse) != n):
+        raise ValueError("q, latent, out (and lse) need one tensor per layer")
+    arr = ctypes.c_void_p * max(n, 1)
+    qs = arr(*[_ptr(t if t.dtype == torch.int16 else t.view(torch.int16), torch.int16, "q") for t in q])
+    ls = arr(*[_ptr(t if t.dtype == torch.int16 else t.view(torch.int16), torch.int16, "latent") for t in latent])
+    os_ = arr(*[_ptr(t, torch.float32, "out") for t in out])
+    lses = arr(*[_ptr(t, torch.float32, "lse") for t in lse]) if lse is not None else None
+    _check("isa_sparse_mla_decode_shared", lib.isa_sparse_mla_decode_shared(
+        n, ctypes.cast(qs, ctypes.c_void_p), ctypes.cast(ls, ctypes.c_void_p), seqs.c,
+        _ptr(row_seq, torch.int32, "row_seq"), _ptr(row_pos, torch.int32, "row_pos"), rows,
+        _ptr(idx, torch.int32, "idx"), _ptr(count, torch.int32, "count"), k, float(sm_scale),
+        ctypes.cast(os_, ctypes.c_void_p), ctypes.cast(lses, ctypes.c_void_p) if lses is not None else None,
+        _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
 
 
 def isa_indexer_prefill_scores(q: torch.Tensor, head_w: torch.Tensor, q_pos: torch.Tensor, Q: int,

@@ -65,11 +65,11 @@ size_t pool_ws(const isa_seqs* s) {
   return HDR + up256((size_t)nt * 4 + (size_t)s->batch * 4);
 }
 
-size_t mla_ws(int32_t rows, int32_t k) {
-  MlaPlan p = plan_mla(rows, k);
+size_t mla_ws(int32_t rows, int32_t k, int32_t layers) {
+  MlaPlan p = plan_mla(rows, k, layers);
   if (p.splits <= 1) return HDR;
-  return HDR + up256((size_t)rows * p.splits * ATT_HEADS * LAT_DIM * 4) +
-         up256((size_t)rows * p.splits * ATT_HEADS * 2 * 4);
+  return HDR + up256((size_t)layers * rows * p.splits * ATT_HEADS * LAT_DIM * 4) +
+         up256((size_t)layers * rows * p.splits * ATT_HEADS * 2 * 4);
 }
 
 __global__ void k_fill_zero(uint4* p, size_t n16) {
@@ -126,15 +126,16 @@ const char* isa_status_string(isa_status st) {
 }
 
 size_t isa_workspace_size(int op, const isa_seqs* s, int32_t rows, int32_t cols) {
-  (void)cols;
   switch (op) {
     case ISA_OP_INDEXPOOL:
       return valid_seqs(s) ? pool_ws(s) : 0;
     case ISA_OP_INDEXER_TOPK:
       if (s == nullptr) return HDR;
       return valid_seqs(s) ? decode_layout(s, MAX_K).total : 0;
-    case ISA_OP_SPARSE_MLA:
-      return rows >= 1 ? mla_ws(rows, MAX_K) : 0;
+    case ISA_OP_SPARSE_MLA: {
+      const int32_t layers = cols < 1 ? 1 : cols;
+      return rows >= 1 && layers <= ISA_MAX_LAYERS ? mla_ws(rows, MAX_K, layers) : 0;
+    }
     case ISA_OP_PREFILL_SCORES:
       return HDR;
   }
@@ -212,28 +213,51 @@ isa_status isa_indexer_topk(const int8_t* q, const int8_t* head_w, const int8_t*
                                (hipStream_t)stream);
 }
 
-isa_status isa_sparse_mla_decode(const uint16_t* q, const uint16_t* latent, const isa_seqs* s,
-                                 const int32_t* row_seq, const int32_t* row_pos, int32_t rows, const int32_t* idx,
-                                 const int32_t* count, int32_t k, float sm_scale, float* out, float* lse, void* ws,
-                                 size_t ws_bytes, isa_stream_t stream) {
-  if (!q || !latent || !idx || !count || !out || !ws) return ISA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(latent) || !aligned16(idx) || !aligned16(count) || !aligned16(out) ||
-      !aligned16(ws) || (lse && !aligned16(lse)) || (row_seq && !aligned16(row_seq)) ||
+static isa_status sparse_mla(int32_t n_layers, const uint16_t* const* q, const uint16_t* const* latent,
+                             const isa_seqs* s, const int32_t* row_seq, const int32_t* row_pos, int32_t rows,
+                             const int32_t* idx, const int32_t* count, int32_t k, float sm_scale, float* const* out,
+                             float* const* lse, void* ws, size_t ws_bytes, isa_stream_t stream) {
+  if (n_layers < 1 || n_layers > ISA_MAX_LAYERS || !q || !latent || !out) return ISA_ERR_INVALID_ARG;
+  for (int l = 0; l < n_layers; ++l) {
+    if (!q[l] || !latent[l] || !out[l] || (lse && !lse[l])) return ISA_ERR_INVALID_ARG;
+    if (!aligned16(q[l]) || !aligned16(latent[l]) || !aligned16(out[l]) || (lse && !aligned16(lse[l])))
+      return ISA_ERR_INVALID_ARG;
+  }
+  if (!idx || !count || !ws) return ISA_ERR_INVALID_ARG;
+  if (!aligned16(idx) || !aligned16(count) || !aligned16(ws) || (row_seq && !aligned16(row_seq)) ||
       (row_pos && !aligned16(row_pos)))
     return ISA_ERR_INVALID_ARG;
   if (k < 1 || k > MAX_K || rows < 1 || !(sm_scale > 0.f) || sm_scale != sm_scale) return ISA_ERR_INVALID_ARG;
   if (!valid_seqs(s)) return ISA_ERR_INVALID_ARG;
   if (!row_seq && rows > s->batch) return ISA_ERR_INVALID_ARG;
-  MlaPlan p = plan_mla(rows, k);
-  if ((long long)rows * p.splits > 0x7FFFFFFF) return ISA_ERR_UNSUPPORTED;
-  if (ws_bytes < mla_ws(rows, k)) return ISA_ERR_WORKSPACE;
+  MlaPlan p = plan_mla(rows, k, n_layers);
+  if ((long long)rows * p.splits * n_layers * ATT_HEADS > 0x7FFFFFFF) return ISA_ERR_UNSUPPORTED;
+  if (ws_bytes < mla_ws(rows, k, n_layers)) return ISA_ERR_WORKSPACE;
   BatchArgs a;
   fill_batch(s, &a, k);
   char* base = (char*)ws;
   MlaWs w{(uint32_t*)base, (float*)(base + HDR),
-          (float*)(base + HDR + up256((size_t)rows * p.splits * ATT_HEADS * LAT_DIM * 4))};
-  return launch_sparse_mla(a, p, q, latent, s->block_table, row_seq, row_pos, idx, count, k, sm_scale, out, lse, w,
-                           (hipStream_t)stream);
+          (float*)(base + HDR + up256((size_t)n_layers * rows * p.splits * ATT_HEADS * LAT_DIM * 4))};
+  return launch_sparse_mla(a, p, n_layers, q, latent, s->block_table, row_seq, row_pos, idx, count, k, sm_scale,
+                           out, lse, w, (hipStream_t)stream);
+}
+
+isa_status isa_sparse_mla_decode(const uint16_t* q, const uint16_t* latent, const isa_seqs* s,
+                                 const int32_t* row_seq, const int32_t* row_pos, int32_t rows, const int32_t* idx,
+                                 const int32_t* count, int32_t k, float sm_scale, float* out, float* lse, void* ws,
+                                 size_t ws_bytes, isa_stream_t stream) {
+  if (!q || !latent || !out) return ISA_ERR_INVALID_ARG;
+  return sparse_mla(1, &q, &latent, s, row_seq, row_pos, rows, idx, count, k, sm_scale, &out, lse ? &lse : nullptr,
+                    ws, ws_bytes, stream);
+}
+
+isa_status isa_sparse_mla_decode_shared(int32_t n_layers, const uint16_t* const* q, const uint16_t* const* latent,
+                                        const isa_seqs* s, const int32_t* row_seq, const int32_t* row_pos,
+                                        int32_t rows, const int32_t* idx, const int32_t* count, int32_t k,
+                                        float sm_scale, float* const* out, float* const* lse, void* ws,
+                                        size_t ws_bytes, isa_stream_t stream) {
+  return sparse_mla(n_layers, q, latent, s, row_seq, row_pos, rows, idx, count, k, sm_scale, out, lse, ws, ws_bytes,
+                    stream);
 }
 
 isa_status isa_indexer_prefill_scores(const int8_t* q, const int8_t* head_w, const int32_t* q_pos, int32_t Q,

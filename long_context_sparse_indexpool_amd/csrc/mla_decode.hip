@@ -85,17 +85,19 @@ __device__ __forceinline__ v4s lds_read_tr16(const _Float16* p) {
 __device__ __forceinline__ int sp_slot(int lane) { return lane + 8 * (lane >> 4); }
 
 struct MlaPtrs {
-  const uint16_t* q;
-  const uint16_t* latent;
+  const uint16_t* q[ISA_MAX_LAYERS];       // per layer sharing the selection
+  const uint16_t* latent[ISA_MAX_LAYERS];
+  float* out[ISA_MAX_LAYERS];
+  float* lse[ISA_MAX_LAYERS];              // all null when not requested
+  int32_t n_layers;
+  int32_t rows;
   const int32_t* bt;
   const int32_t* row_seq;
   const int32_t* row_pos;
   const int32_t* idx;
   const int32_t* count;
-  float* out;
-  float* lse;
-  float* o_part;
-  float* ml_part;
+  float* o_part;   // [layers][rows][splits][64][512]
+  float* ml_part;  // [layers][rows][splits][64][2]
   uint32_t* err;
   int32_t k;
   float c2;  // sm_scale * log2(e)
@@ -115,8 +117,11 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cg = wave & 3, th = wave >> 2;   // channels 128cg.., tokens 16th.. of each tile
-  const int r = blockIdx.x / P.splits;
+  const int layer = blockIdx.x / (P.rows * P.splits);  // layers sharing the selection: one launch
+  const int r = (blockIdx.x / P.splits) % P.rows;
   const int split = blockIdx.x % P.splits;
+  const uint16_t* const q = P.q[layer];
+  const uint16_t* const latent = P.latent[layer];
   const int lq = lane & 15, lg = lane >> 4;  // column / row-group of the 16x16 layouts
 
   // row description, read by every thread (no barrier); the split's group ids
@@ -133,16 +138,6 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
   for (int e = 0; e < MAX_GPS / MLA_THREADS + 1; ++e) {
     const int j = tid + e * MLA_THREADS;
     gid[e] = (j < P.gps && jbeg0 + j < P.k) ? P.idx[(size_t)r * P.k + jbeg0 + j] : -1;
-  }
-  // query operand (B = Q^T): lane -> head 16hb + lq, channels 128cg + 32c + 8lg .. +7
-  v8bf qop[HBLK][KSTEPS];
-  {
-    const uint16_t* qp = P.q + ((size_t)r * ATT_HEADS + lq) * LAT_DIM + cg * CG_DIM + lg * 8;
-#pragma unroll
-    for (int hb = 0; hb < HBLK; ++hb)
-#pragma unroll
-      for (int c = 0; c < KSTEPS; ++c)
-        qop[hb][c] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qp + (size_t)hb * 16 * LAT_DIM + c * 32));
   }
   // the row's block-table entries, fetched in the same round as the group ids
   // (one dependent global round trip less before the first latent load)
@@ -184,20 +179,31 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
       trow[j * GROUP + i] = vis ? (uint32_t)pg * PAGE_TOK + (uint32_t)(tok % PAGE_TOK) : 0xFFFFFFFFu;
     }
   }
+  // softmax state of the owned head h = 8 wave + lane % 8 (identical in the
+  // eight lanes of a head; l_run is this lane's share of the sum)
+  const int own_h = OWN_HEADS * wave + (lane & 7);
+  const int own_tq = lane >> 3;  // tokens 4 own_tq .. +3 of the tile
+  lds_barrier();  // token table complete
+
+  const int nslot = ng * GROUP;
+  const int ntile = (nslot + TILE_TOK - 1) / TILE_TOK;
+  // query operand (B = Q^T): lane -> head 16hb + lq, channels 128cg + 32c + 8lg .. +7
+  v8bf qop[HBLK][KSTEPS];
+  {
+    const uint16_t* qp = q + ((size_t)r * ATT_HEADS + lq) * LAT_DIM + cg * CG_DIM + lg * 8;
+#pragma unroll
+    for (int hb = 0; hb < HBLK; ++hb)
+#pragma unroll
+      for (int c = 0; c < KSTEPS; ++c)
+        qop[hb][c] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qp + (size_t)hb * 16 * LAT_DIM + c * 32));
+  }
   v4f o[HBLK][NBLK];
 #pragma unroll
   for (int hb = 0; hb < HBLK; ++hb)
 #pragma unroll
     for (int nb = 0; nb < NBLK; ++nb) o[hb][nb] = v4f{0.f, 0.f, 0.f, 0.f};
-  // softmax state of the owned head h = 8 wave + lane % 8 (identical in the
-  // eight lanes of a head; l_run is this lane's share of the sum)
-  const int own_h = OWN_HEADS * wave + (lane & 7);
-  const int own_tq = lane >> 3;  // tokens 4 own_tq .. +3 of the tile
   float m_ref = -INFINITY, l_run = 0.f;
-  lds_barrier();  // token table complete
 
-  const int nslot = ng * GROUP;
-  const int ntile = (nslot + TILE_TOK - 1) / TILE_TOK;
   // This lane's load of tile t: token 16th + lq, channels 128cg + 8lg + 32c.
   // Loads are unconditional (an invisible token reads row 0 of the pool and is
   // zeroed by its mask), so no branch separates a load from its use and the
@@ -208,7 +214,7 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
     const bool vis = t < ntile && slot < nslot && tr != 0xFFFFFFFFu;
     mask = vis ? -1 : 0;
     const uint32_t row = vis ? tr : 0u;
-    return reinterpret_cast<const v4i*>(P.latent + (size_t)row * LAT_DIM + cg * CG_DIM + lg * 8);
+    return reinterpret_cast<const v4i*>(latent + (size_t)row * LAT_DIM + cg * CG_DIM + lg * 8);
   };
 
   // one tile: partial scores, V, softmax of the owned heads, P.V
@@ -354,7 +360,7 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
   __syncthreads();
   const int d_base = wave * OUT_DIM;
   if (P.splits == 1) {
-    float* orow = P.out + (size_t)r * ATT_HEADS * LAT_DIM;
+    float* orow = P.out[layer] + (size_t)r * ATT_HEADS * LAT_DIM;
 #pragma unroll
     for (int hb = 0; hb < HBLK; ++hb) {
       float inv[4];
@@ -369,10 +375,11 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
         for (int i = 0; i < 4; ++i)
           orow[(size_t)(hb * 16 + 4 * lg + i) * LAT_DIM + d_base + nb * 16 + lq] = o[hb][nb][i] * inv[i];
     }
-    if (P.lse && own_tq == 0)
-      P.lse[(size_t)r * ATT_HEADS + own_h] = l_tot > 0.f ? m_ref * LN2 + logf(l_tot) : -INFINITY;
+    if (P.lse[layer] && own_tq == 0)
+      P.lse[layer][(size_t)r * ATT_HEADS + own_h] = l_tot > 0.f ? m_ref * LN2 + logf(l_tot) : -INFINITY;
   } else {
-    float* op = P.o_part + ((size_t)r * P.splits + split) * ATT_HEADS * LAT_DIM;
+    const size_t part = blockIdx.x;  // (layer, row, split)
+    float* op = P.o_part + part * ATT_HEADS * LAT_DIM;
 #pragma unroll
     for (int hb = 0; hb < HBLK; ++hb)
 #pragma unroll
@@ -381,7 +388,7 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
         for (int i = 0; i < 4; ++i)
           op[(size_t)(hb * 16 + 4 * lg + i) * LAT_DIM + d_base + nb * 16 + lq] = o[hb][nb][i];
     if (own_tq == 0) {
-      float* mp = P.ml_part + (((size_t)r * P.splits + split) * ATT_HEADS + own_h) * 2;
+      float* mp = P.ml_part + (part * ATT_HEADS + own_h) * 2;
       mp[0] = l_tot > 0.f ? m_ref : -INFINITY;
       mp[1] = l_tot;
     }
@@ -390,12 +397,14 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
 
 // Merge the splits of one (row, head): weights 2^(m_s - M), then a weighted
 // sum of the partial outputs (128 threads x 4 channels, loads unrolled).
-__global__ __launch_bounds__(128) void k_mla_combine(const MlaPtrs P) {
+__global__ __launch_bounds__(128) void k_mla_combine(const MlaPtrs P, int32_t rows) {
   __shared__ float wsh[MAX_SPLITS];
   __shared__ float stat[2];
-  const int r = blockIdx.x / ATT_HEADS, h = blockIdx.x % ATT_HEADS;
+  const int layer = blockIdx.x / (rows * ATT_HEADS);
+  const int r = (blockIdx.x / ATT_HEADS) % rows, h = blockIdx.x % ATT_HEADS;
   const int S = P.splits;
-  const float* ml = P.ml_part + ((size_t)r * S * ATT_HEADS + h) * 2;
+  const size_t part0 = ((size_t)layer * rows + r) * S;  // (layer, row, split 0)
+  const float* ml = P.ml_part + (part0 * ATT_HEADS + h) * 2;
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     float m = lane < S ? ml[(size_t)lane * ATT_HEADS * 2] : -INFINITY;
@@ -412,7 +421,7 @@ __global__ __launch_bounds__(128) void k_mla_combine(const MlaPtrs P) {
     }
   }
   __syncthreads();
-  const float* op = P.o_part + ((size_t)r * S * ATT_HEADS + h) * LAT_DIM + threadIdx.x * 4;
+  const float* op = P.o_part + (part0 * ATT_HEADS + h) * LAT_DIM + threadIdx.x * 4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 8
   for (int s = 0; s < S; ++s) {
@@ -423,16 +432,18 @@ __global__ __launch_bounds__(128) void k_mla_combine(const MlaPtrs P) {
     acc.z = fmaf(f, v.z, acc.z);
     acc.w = fmaf(f, v.w, acc.w);
   }
-  *reinterpret_cast<float4*>(P.out + ((size_t)r * ATT_HEADS + h) * LAT_DIM + threadIdx.x * 4) = acc;
-  if (P.lse && threadIdx.x == 0)
-    P.lse[(size_t)r * ATT_HEADS + h] = stat[1] > 0.f ? stat[0] * LN2 + logf(stat[1]) : -INFINITY;
+  *reinterpret_cast<float4*>(P.out[layer] + ((size_t)r * ATT_HEADS + h) * LAT_DIM + threadIdx.x * 4) = acc;
+  if (P.lse[layer] && threadIdx.x == 0)
+    P.lse[layer][(size_t)r * ATT_HEADS + h] = stat[1] > 0.f ? stat[0] * LN2 + logf(stat[1]) : -INFINITY;
 }
 
-MlaPlan plan_mla(int32_t rows, int32_t k) {
-  // about 256 workgroups in flight, at least 32 groups (four 32-token tiles) per split
+MlaPlan plan_mla(int32_t rows, int32_t k, int32_t layers) {
+  // about 256 workgroups in flight over all layers, at least 32 groups (four
+  // 32-token tiles) per split
   MlaPlan p;
   p.rows = rows;
-  int s = (256 + rows - 1) / rows;
+  const long long units = (long long)rows * layers;
+  int s = (int)((256 + units - 1) / units);
   int smax = (k + 31) / 32;
   if (s > smax) s = smax;
   if (s > MAX_SPLITS) s = MAX_SPLITS;
@@ -442,17 +453,38 @@ MlaPlan plan_mla(int32_t rows, int32_t k) {
   return p;
 }
 
-isa_status launch_sparse_mla(const BatchArgs& a, const MlaPlan& p, const uint16_t* q, const uint16_t* latent,
-                             const int32_t* bt, const int32_t* row_seq, const int32_t* row_pos,
-                             const int32_t* idx, const int32_t* count, int32_t k, float sm_scale, float* out,
-                             float* lse, const MlaWs& w, hipStream_t stream) {
-  MlaPtrs P{q, latent, bt, row_seq, row_pos, idx, count, out, lse, w.o_part, w.ml_part, w.err, k,
-            sm_scale * LOG2E, p.splits, p.groups_per_split};
-  if (launch_timed(ISA_TIMER_MLA_SPLIT, k_mla_split, dim3(p.rows * p.splits), dim3(MLA_THREADS), stream, a, P) !=
+isa_status launch_sparse_mla(const BatchArgs& a, const MlaPlan& p, int32_t n_layers, const uint16_t* const* q,
+                             const uint16_t* const* latent, const int32_t* bt, const int32_t* row_seq,
+                             const int32_t* row_pos, const int32_t* idx, const int32_t* count, int32_t k,
+                             float sm_scale, float* const* out, float* const* lse, const MlaWs& w,
+                             hipStream_t stream) {
+  MlaPtrs P{};
+  for (int l = 0; l < n_layers; ++l) {
+    P.q[l] = q[l];
+    P.latent[l] = latent[l];
+    P.out[l] = out[l];
+    P.lse[l] = lse ? lse[l] : nullptr;
+  }
+  P.n_layers = n_layers;
+  P.rows = p.rows;
+  P.bt = bt;
+  P.row_seq = row_seq;
+  P.row_pos = row_pos;
+  P.idx = idx;
+  P.count = count;
+  P.o_part = w.o_part;
+  P.ml_part = w.ml_part;
+  P.err = w.err;
+  P.k = k;
+  P.c2 = sm_scale * LOG2E;
+  P.splits = p.splits;
+  P.gps = p.groups_per_split;
+  if (launch_timed(ISA_TIMER_MLA_SPLIT, k_mla_split, dim3(n_layers * p.rows * p.splits), dim3(MLA_THREADS), stream,
+                   a, P) !=
       hipSuccess)
     return ISA_ERR_HIP;
   if (p.splits > 1) {
-    hipLaunchKernelGGL(k_mla_combine, dim3(p.rows * ATT_HEADS), dim3(128), 0, stream, P);
+    hipLaunchKernelGGL(k_mla_combine, dim3(n_layers * p.rows * ATT_HEADS), dim3(128), 0, stream, P, p.rows);
     if (hipGetLastError() != hipSuccess) return ISA_ERR_HIP;
   }
   return ISA_OK;

@@ -25,6 +25,12 @@ Input recipe (tensor ids of the generator in parentheses):
   attention query (6)   N(0,1) -> bf16, [rows, 64, 512]
   lengths (7)           uniform double u_b (workload 4 only)
   page permutation (8)  Fisher-Yates with j = draw_i mod (i + 1) (workload 4 only)
+
+Layers that share one selection (IndexShare): layer 0 uses the tensors above;
+layer l >= 1 has its own attention query (tensor id 16 + l, same layout) and a
+latent cache equal to layer 0's with the sign bit flipped on the channels whose
+bit l - 1 is set -- still N(0,1) per element, a different cache per layer, and
+cheap to build on the device without generating a new 8 GiB pool.
 """
 from __future__ import annotations
 
@@ -47,6 +53,17 @@ PAGE_GROUPS = PAGE_TOKENS // GROUP
 SM_SCALE = 1.0 / math.sqrt(LAT_DIM)
 
 T_KEYS, T_POOLW, T_QIDX, T_HEADW, T_LATENT, T_QATT, T_LENS, T_PERM = 1, 2, 3, 4, 5, 6, 7, 8
+T_QATT_LAYER = 16  # attention query of layer l >= 1: tensor id 16 + l
+
+
+def layer_flip_view(bits, layer: int):
+    """The channels of layer `layer` (>= 1) whose latent sign bit is flipped
+    relative to layer 0, as a strided view of a [..., 512] array of bf16 bits
+    (numpy or torch, int16/uint16): channels c with bit layer-1 of c set.
+    XOR-ing 0x8000 into the view in place turns layer 0's cache into layer
+    `layer`'s, and back."""
+    w = 1 << (layer - 1)
+    return bits.reshape(-1, LAT_DIM // (2 * w), 2, w)[:, :, 1, :]
 
 
 @dataclass
@@ -160,9 +177,10 @@ class Workload:
         n = self.rows - r0 if n is None else n
         return uniform_i8(self.seed, T_HEADW, (n, IDX_HEADS), 0, 64, start=r0 * IDX_HEADS)
 
-    def q_attn(self, r0: int = 0, n: Optional[int] = None) -> np.ndarray:
+    def q_attn(self, r0: int = 0, n: Optional[int] = None, layer: int = 0) -> np.ndarray:
         n = self.rows - r0 if n is None else n
-        return normal_bf16(self.seed, T_QATT, (n, ATT_HEADS, LAT_DIM), start=r0 * ATT_HEADS * LAT_DIM)
+        tid = T_QATT if layer == 0 else T_QATT_LAYER + layer
+        return normal_bf16(self.seed, tid, (n, ATT_HEADS, LAT_DIM), start=r0 * ATT_HEADS * LAT_DIM)
 
     # ---- paged pools built from logical arrays (host side plumbing) --------
     def scatter_pages(self, logical: np.ndarray, per_page_rows: int, pad_value) -> np.ndarray:

@@ -137,6 +137,38 @@ def run_attention(db: DeviceBatch, idx: torch.Tensor, cnt: torch.Tensor, k: int,
     return out.cpu().numpy(), lse.cpu().numpy()
 
 
+def layer_latents(db: DeviceBatch, n_layers: int):
+    """Latent pools of layers 0..n_layers-1 sharing one selection: layer 0 is the
+    batch's pool, layer l a device copy with the sign bit of its flipped
+    channels set (the input recipe for shared layers)."""
+    from synth.configs import layer_flip_view
+    pools = [db.latent]
+    for layer in range(1, n_layers):
+        p = db.latent.clone()
+        layer_flip_view(p, layer).bitwise_xor_(-32768)
+        pools.append(p)
+    return pools
+
+
+def run_attention_shared(db: DeviceBatch, idx: torch.Tensor, cnt: torch.Tensor, k: int, pools, rows=None):
+    """isa_sparse_mla_decode_shared over len(pools) layers (queries from the
+    generator's per-layer tensors); returns per-layer (out, lse) on the host."""
+    m = isa()
+    wl = db.wl
+    rows = wl.batch if rows is None else rows
+    n = len(pools)
+    qs = [torch.from_numpy(wl.q_attn(0, rows, layer=l).view(np.int16)).cuda() for l in range(n)]
+    outs = [torch.full((rows, ATT_HEADS, LAT_DIM), float("nan"), dtype=torch.float32, device="cuda")
+            for _ in range(n)]
+    lses = [torch.full((rows, ATT_HEADS), float("nan"), dtype=torch.float32, device="cuda") for _ in range(n)]
+    ws = m.alloc_workspace(m.workspace_size(m.ISA_OP_SPARSE_MLA, db.seqs, rows, n))
+    m.isa_sparse_mla_decode_shared(qs, pools, db.seqs, None, None, rows, idx, cnt, k, SM_SCALE, outs, lses, ws)
+    torch.cuda.synchronize()
+    err = m.isa_device_error(ws)
+    assert err == 0, f"device error word {err:#x}"
+    return [(o.cpu().numpy(), l.cpu().numpy()) for o, l in zip(outs, lses)]
+
+
 # ------------------------------------------------------------------ comparisons
 def check_pool(db: DeviceBatch, bs=None):
     """GPU pooled keys within 1 LSB of the oracle's, scale within 1e-6 relative."""

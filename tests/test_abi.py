@@ -146,6 +146,46 @@ def test_sparse_mla_rejects(m, case):
     assert rc == (m.ISA_ERR_WORKSPACE if case == "ws_small" else m.ISA_ERR_INVALID_ARG)
 
 
+def test_shared_attention_workspace_scales_with_layers(m):
+    s = FakeSeqs(m, [1 << 20] * 8)
+    one = m.lib.isa_workspace_size(m.ISA_OP_SPARSE_MLA, s.c, 8, 1)
+    assert m.lib.isa_workspace_size(m.ISA_OP_SPARSE_MLA, s.c, 8, 0) == one
+    four = m.lib.isa_workspace_size(m.ISA_OP_SPARSE_MLA, s.c, 8, 4)
+    assert four > one and four % 256 == 0
+    assert m.lib.isa_workspace_size(m.ISA_OP_SPARSE_MLA, s.c, 8, m.ISA_MAX_LAYERS + 1) == 0
+
+
+@pytest.mark.parametrize("case", ["layers0", "too_many", "null_array", "null_entry", "misaligned_entry",
+                                  "null_lse_entry", "ws_small", "k0"])
+def test_shared_attention_rejects(m, case):
+    s = FakeSeqs(m, [8192] * 8)
+    n, k, wsb = 4, 512, 1 << 30
+    arr = ctypes.c_void_p * 8
+    q, lat, out = arr(*[P] * 8), arr(*[P] * 8), arr(*[P] * 8)
+    lse = None
+    if case == "layers0":
+        n = 0
+    elif case == "too_many":
+        n = m.ISA_MAX_LAYERS + 1
+    elif case == "null_array":
+        q = None
+    elif case == "null_entry":
+        lat[2] = None
+    elif case == "misaligned_entry":
+        out[3] = P + 8
+    elif case == "null_lse_entry":
+        lse = arr(*[P] * 8)
+        lse[1] = None
+    elif case == "ws_small":
+        wsb = 1000
+    elif case == "k0":
+        k = 0
+    c = lambda a: ctypes.cast(a, ctypes.c_void_p) if a is not None else None
+    rc = m.lib.isa_sparse_mla_decode_shared(n, c(q), c(lat), s.c, None, None, 8, P, P, k, 0.044, c(out), c(lse), P,
+                                            wsb, None)
+    assert rc == (m.ISA_ERR_WORKSPACE if case == "ws_small" else m.ISA_ERR_INVALID_ARG)
+
+
 @pytest.mark.parametrize("case", ["batch2", "q0", "ld_small", "null_pos"])
 def test_prefill_scores_rejects(m, case):
     s = FakeSeqs(m, [1 << 20] if case != "batch2" else [1000, 1000])

@@ -5,7 +5,9 @@ oracle.
 Decode workloads (8192 tokens; 64 x 131,072; 8 x 1,048,576; 32 ragged paged
 sequences up to 2^20): pooled keys of every sequence within 1 LSB, every score
 bit-exact (from a second call that also writes the scores), every selected id
-bit-exact, and attention within tolerance for every row.  The prefill chunk
+bit-exact, and attention within tolerance for every row.  At 8 x 1,048,576 also
+IndexShare: four layers' attention over the same selection in one call, every
+row of every layer against the oracle.  The prefill chunk
 (2048 queries at the end of one 2^20-token sequence) checks the mask of all
 2048 score rows at full size and sampled rows one by one: scores, selection and
 attention.
@@ -22,7 +24,7 @@ import harness as H
 pytestmark = pytest.mark.gpu
 
 
-def _decode_full(i: int):
+def _decode_full(i: int, share_layers: int = 0):
     wl = workload(i)
     B = wl.batch
     H.log(f"{wl.name}: generating inputs")
@@ -58,7 +60,37 @@ def _decode_full(i: int):
     ref_att = oracle.map_rows(one, range(B))
     for b in range(B):
         H.attention_tolerance(out[b], ref_att[b][0], lse[b], ref_att[b][1])
+    if share_layers:
+        _index_share_full(db, idx, cnt, idx_d, cnt_d, ref_att, share_layers)
     H.log(f"{wl.name}: done")
+
+
+def _index_share_full(db, idx, cnt, idx_d, cnt_d, ref0, n):
+    """n layers over the same selection in one call, every row of every layer
+    against the oracle (layer l's cache is layer 0's with its flipped channels)."""
+    from synth.configs import layer_flip_view
+    wl = db.wl
+    B = wl.batch
+    H.log(f"{wl.name}: IndexShare, {n} layers in one call")
+    pools = H.layer_latents(db, n)
+    res = H.run_attention_shared(db, idx_d, cnt_d, TOPK_GROUPS, pools)
+    del pools
+    for b in range(B):
+        H.attention_tolerance(res[0][0][b], ref0[b][0], res[0][1][b], ref0[b][1])
+    lat, to = db.host["latent"], wl.token_offsets
+    for layer in range(1, n):
+        qa = wl.q_attn(0, B, layer=layer)
+        view = layer_flip_view(lat, layer)
+        view ^= np.uint16(0x8000)
+        try:
+            def one(b):
+                L = wl.lens[b]
+                return oracle.attention(qa[b], lat[to[b]: to[b + 1]], L, L - 1, idx[b], int(cnt[b]), SM_SCALE)
+            ref = oracle.map_rows(one, range(B))
+        finally:
+            view ^= np.uint16(0x8000)
+        for b in range(B):
+            H.attention_tolerance(res[layer][0][b], ref[b][0], res[layer][1][b], ref[b][1])
 
 
 def test_full_decode_b1_L8192():
@@ -70,7 +102,7 @@ def test_full_decode_b64_L131072():
 
 
 def test_full_decode_b8_L1048576():
-    _decode_full(2)
+    _decode_full(2, share_layers=4)
 
 
 def test_full_ragged_paged_b32():

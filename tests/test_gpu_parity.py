@@ -187,6 +187,37 @@ def test_attention_parity_ragged(ragged_batch):
     H.log(f"attention worst max-abs {max(r[0] for r in res):.2e} rel {max(r[1] for r in res):.2e}")
 
 
+def test_index_share_layers():
+    """Four layers attending over one selection in one call: every layer
+    against the oracle with its own query and latent cache; one layer through
+    the shared call is bit-identical to the single-layer call."""
+    from synth.configs import layer_flip_view
+    wl = custom("index_share", 17, [9000, 3000, 20000, 700, 131075], paged_random=True)
+    db = H.make_batch(wl)
+    H.run_pool(db)
+    idx, cnt, _, _ = H.run_topk(db, with_scores=False)
+    idx_d, cnt_d = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
+    n = 4
+    pools = H.layer_latents(db, n)
+    res = H.run_attention_shared(db, idx_d, cnt_d, 512, pools)
+    lat, to = db.host["latent"], wl.token_offsets
+    for layer in range(n):
+        q = wl.q_attn(0, wl.batch, layer=layer)
+        if layer:
+            layer_flip_view(lat, layer).__ixor__(np.uint16(0x8000))
+        try:
+            for b in range(wl.batch):
+                L = wl.lens[b]
+                ref, ref_lse = oracle.attention(q[b], lat[to[b]: to[b + 1]], L, L - 1, idx[b], int(cnt[b]), SM_SCALE)
+                H.attention_tolerance(res[layer][0][b], ref, res[layer][1][b], ref_lse)
+        finally:
+            if layer:
+                layer_flip_view(lat, layer).__ixor__(np.uint16(0x8000))
+    one = H.run_attention_shared(db, idx_d, cnt_d, 512, pools[:1])
+    out1, lse1 = H.run_attention(db, idx_d, cnt_d, 512)
+    assert np.array_equal(one[0][0], out1) and np.array_equal(one[0][1], lse1)
+
+
 def test_attention_rows_with_positions(ragged_batch):
     """Rows that map to sequences with an earlier last-visible position (prefill rows)."""
     db = ragged_batch
