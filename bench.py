@@ -233,6 +233,44 @@ def bench_index_share(dec, n_layers=4, steps=100, warmup=10):
     return res
 
 
+def bench_append(batch=8, length=1 << 20, reps=200):
+    """Decode-time cache maintenance: isa_append_token for a batch of
+    `batch` sequences at `length` tokens (one new key and latent row each, the
+    token's group re-pooled at a fixed scale).  Only the pages around the new
+    tokens are allocated; a call touches ~2.5 KiB per sequence, so it is
+    launch- and latency-bound and reported as microseconds per call."""
+    import numpy as np
+    import torch
+
+    import long_context_sparse_indexpool_amd as m
+    B = batch
+    pages = B  # one physical page per sequence: the page of the new token
+    max_pages = (length + 255) // 256
+    bt = torch.full((B, max_pages), 0, dtype=torch.int32)
+    bt[:, (length - 1) // 256] = torch.arange(B, dtype=torch.int32)
+    bt = bt.cuda()
+    seqs = m.Seqs([length] * B, bt, pages)
+    keys = torch.zeros((pages, 256, 128), dtype=torch.int16, device="cuda")
+    lat = torch.zeros((pages, 256, 512), dtype=torch.int16, device="cuda")
+    pooled = torch.zeros((pages, 64, 128), dtype=torch.int8, device="cuda")
+    knew = torch.ones((B, 128), dtype=torch.int16, device="cuda")
+    lnew = torch.ones((B, 512), dtype=torch.int16, device="cuda")
+    sc = torch.ones(B, dtype=torch.float32, device="cuda")
+    ws = m.alloc_workspace(m.workspace_size(m.ISA_OP_APPEND_TOKEN, seqs))
+    w4 = [0.25, 0.25, 0.25, 0.25]
+    for _ in range(10):
+        m.isa_append_token(knew, lnew, w4, seqs, sc, keys, lat, pooled, ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        m.isa_append_token(knew, lnew, w4, seqs, sc, keys, lat, pooled, ws)
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / reps * 1e6
+    assert m.isa_device_error(ws) == 0
+    log(f"append token: batch {B} at {length} tokens: {us:.2f} us per call")
+    return {"batch": B, "seq_len": length, "us_per_call": round(us, 2)}
+
+
 def oracle_step_time(dec, min_s=10.0, budget_s=25.0):
     """The CPU oracle on whole decode steps of the same workload: scores of every
     group, top-512 selection and 64-head attention for each sequence, from the
@@ -489,6 +527,7 @@ def main():
     if not args.primary_only:
         secondary["indexpool"] = bench_pool(dec)
         secondary["index_share"] = bench_index_share(dec)
+        secondary["append_token"] = bench_append()
     dec.free()
     if not args.primary_only:
         for i in (1, 4):

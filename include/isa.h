@@ -90,7 +90,13 @@ typedef struct {
   const int32_t* block_table;   /* [dev]  [B, max_pages] physical page ids */
 } isa_seqs;
 
-enum { ISA_OP_INDEXPOOL = 1, ISA_OP_INDEXER_TOPK = 2, ISA_OP_SPARSE_MLA = 3, ISA_OP_PREFILL_SCORES = 4 };
+enum {
+  ISA_OP_INDEXPOOL = 1,
+  ISA_OP_INDEXER_TOPK = 2,
+  ISA_OP_SPARSE_MLA = 3,
+  ISA_OP_PREFILL_SCORES = 4,
+  ISA_OP_APPEND_TOKEN = 5
+};
 
 /* Workspace bytes (a multiple of 256) that `op` needs for these sequences.
  * rows: query rows (attention and top-k from precomputed scores; ignored
@@ -231,6 +237,35 @@ isa_status isa_sparse_mla_decode_shared(int32_t n_layers, const uint16_t* const*
 isa_status isa_indexer_prefill_scores(const int8_t* q, const int8_t* head_w, const int32_t* q_pos, int32_t Q,
                                       const int8_t* pooled, const isa_seqs* s, int32_t* scores,
                                       int32_t ld_scores, void* ws, size_t ws_bytes, isa_stream_t stream);
+
+/*
+ * (6) Decode-time cache maintenance: append one token to every sequence of the
+ * batch ([WIKI] IndexPool section: the indexer keeps one key per position and
+ * four consecutive keys pool into one; this call keeps the pooled cache in step
+ * as tokens arrive).  s->seq_lens_host holds the lengths AFTER the append
+ * (L_b >= 1): the new token sits at position L_b - 1, on logical page
+ * (L_b - 1) / 256, which the block table must map (the caller owns page
+ * allocation; a token at a multiple of 256 starts a new page).
+ *   key_new    [dev] bf16 bits [B, 128]: the new tokens' indexer keys
+ *   latent_new [dev] bf16 bits [B, 512], or NULL to leave the latent pool alone
+ *   w4         [host] fp32[4] pooling weights (as isa_indexpool)
+ *   scales     [dev] fp32 [B]: each sequence's fixed quantisation scale, e.g.
+ *              from an earlier isa_indexpool; used, never changed
+ *   keys       [dev] bf16 bits [num_pages, 256, 128]: the key is written at the new token
+ *   latent     [dev] bf16 bits [num_pages, 256, 512] (NULL iff latent_new is NULL)
+ *   pooled     [dev] int8 [num_pages, 64, 128]: group (L_b - 1) / 4 is pooled
+ *              again from its r = (L_b - 1) % 4 + 1 tokens (r < 4: the tail rule
+ *              of isa_indexpool) and quantised with scales[b], clamped to +-127
+ * After any sequence of appends the pooled cache equals what isa_indexpool with
+ * ISA_SCALE_GIVEN and the same scales writes for the extended sequences (same
+ * arithmetic, bit for bit).  Workspace: isa_workspace_size(ISA_OP_APPEND_TOKEN,
+ * ...) bytes (the error word).  Device errors: ISA_DERR_PAGE_OOB for an unmapped
+ * page (nothing written for that sequence), ISA_DERR_NONFINITE for a scale that
+ * is not positive and finite (1 is used).
+ */
+isa_status isa_append_token(const uint16_t* key_new, const uint16_t* latent_new, const float* w4, const isa_seqs* s,
+                            const float* scales, uint16_t* keys, uint16_t* latent, int8_t* pooled, void* ws,
+                            size_t ws_bytes, isa_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,7 @@ PAGE_TOKENS, PAGE_GROUPS = 256, 64
 MAX_BATCH, MAX_SEQ_LEN, MAX_K = 256, 1 << 22, 512
 
 ISA_OK, ISA_ERR_INVALID_ARG, ISA_ERR_UNSUPPORTED, ISA_ERR_WORKSPACE, ISA_ERR_HIP = range(5)
-ISA_OP_INDEXPOOL, ISA_OP_INDEXER_TOPK, ISA_OP_SPARSE_MLA, ISA_OP_PREFILL_SCORES = 1, 2, 3, 4
+ISA_OP_INDEXPOOL, ISA_OP_INDEXER_TOPK, ISA_OP_SPARSE_MLA, ISA_OP_PREFILL_SCORES, ISA_OP_APPEND_TOKEN = 1, 2, 3, 4, 5
 ISA_SCALE_DYNAMIC, ISA_SCALE_GIVEN = 0, 1
 ISA_MAX_LAYERS = 8  # layers sharing one selection (isa_sparse_mla_decode_shared)
 DERR_PAGE_OOB, DERR_HEADW_RANGE, DERR_SCORE_OVERFLOW, DERR_ROW_RANGE, DERR_NONFINITE = 1, 2, 4, 8, 16
@@ -34,7 +34,7 @@ ISA_TIMER_INDEXER_SCORE, ISA_TIMER_MLA_SPLIT = 1, 2
 
 EXPORTS = ("isa_workspace_size", "isa_workspace_init", "isa_device_error", "isa_status_string", "isa_version",
            "isa_set_kernel_timer", "isa_indexpool", "isa_indexer_topk", "isa_sparse_mla_decode",
-           "isa_sparse_mla_decode_shared", "isa_indexer_prefill_scores")
+           "isa_sparse_mla_decode_shared", "isa_indexer_prefill_scores", "isa_append_token")
 
 
 class IsaError(RuntimeError):
@@ -69,8 +69,10 @@ def _load() -> ctypes.CDLL:
     lib.isa_sparse_mla_decode_shared.argtypes = [i32, vp, vp, sp, vp, vp, i32, vp, vp, i32, ctypes.c_float, vp, vp,
                                                  vp, sz, vp]
     lib.isa_indexer_prefill_scores.argtypes = [vp, vp, vp, i32, vp, sp, vp, i32, vp, sz, vp]
+    lib.isa_append_token.argtypes = [vp, vp, vp, sp, vp, vp, vp, vp, vp, sz, vp]
     for f in ("isa_workspace_init", "isa_device_error", "isa_set_kernel_timer", "isa_indexpool", "isa_indexer_topk",
-              "isa_sparse_mla_decode", "isa_sparse_mla_decode_shared", "isa_indexer_prefill_scores"):
+              "isa_sparse_mla_decode", "isa_sparse_mla_decode_shared", "isa_indexer_prefill_scores",
+              "isa_append_token"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -169,6 +171,20 @@ def isa_indexpool(keys: torch.Tensor, w4: Sequence[float], seqs: Seqs, scales: t
     _check("isa_indexpool", lib.isa_indexpool(_ptr(k, torch.int16, "keys"), ctypes.cast(w, ctypes.c_void_p), seqs.c,
                                               _ptr(scales, torch.float32, "scales"), _ptr(pooled, torch.int8, "pooled"),
                                               flags, _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
+
+
+def isa_append_token(key_new: torch.Tensor, latent_new: Optional[torch.Tensor], w4: Sequence[float], seqs: Seqs,
+                     scales: torch.Tensor, keys: torch.Tensor, latent: Optional[torch.Tensor], pooled: torch.Tensor,
+                     ws: torch.Tensor, stream=None) -> None:
+    """Append one token per sequence (seqs holds the lengths after the append):
+    key_new bf16 bits [B,128], latent_new bf16 bits [B,512] or None."""
+    w = (ctypes.c_float * 4)(*[float(x) for x in w4])
+    v16 = lambda t: None if t is None else (t if t.dtype == torch.int16 else t.view(torch.int16))
+    _check("isa_append_token", lib.isa_append_token(
+        _ptr(v16(key_new), torch.int16, "key_new"), _ptr(v16(latent_new), torch.int16, "latent_new"),
+        ctypes.cast(w, ctypes.c_void_p), seqs.c, _ptr(scales, torch.float32, "scales"),
+        _ptr(v16(keys), torch.int16, "keys"), _ptr(v16(latent), torch.int16, "latent"),
+        _ptr(pooled, torch.int8, "pooled"), _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
 
 
 def isa_indexer_topk(q: Optional[torch.Tensor], head_w: Optional[torch.Tensor], pooled: Optional[torch.Tensor],

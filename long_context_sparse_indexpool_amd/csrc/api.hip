@@ -137,6 +137,7 @@ size_t isa_workspace_size(int op, const isa_seqs* s, int32_t rows, int32_t cols)
       return rows >= 1 && layers <= ISA_MAX_LAYERS ? mla_ws(rows, MAX_K, layers) : 0;
     }
     case ISA_OP_PREFILL_SCORES:
+    case ISA_OP_APPEND_TOKEN:
       return HDR;
   }
   return 0;
@@ -258,6 +259,24 @@ isa_status isa_sparse_mla_decode_shared(int32_t n_layers, const uint16_t* const*
                                         size_t ws_bytes, isa_stream_t stream) {
   return sparse_mla(n_layers, q, latent, s, row_seq, row_pos, rows, idx, count, k, sm_scale, out, lse, ws, ws_bytes,
                     stream);
+}
+
+isa_status isa_append_token(const uint16_t* key_new, const uint16_t* latent_new, const float* w4, const isa_seqs* s,
+                            const float* scales, uint16_t* keys, uint16_t* latent, int8_t* pooled, void* ws,
+                            size_t ws_bytes, isa_stream_t stream) {
+  if (!key_new || !w4 || !scales || !keys || !pooled || !ws) return ISA_ERR_INVALID_ARG;
+  if ((latent_new == nullptr) != (latent == nullptr)) return ISA_ERR_INVALID_ARG;
+  if (!aligned16(key_new) || !aligned16(keys) || !aligned16(pooled) || !aligned16(ws) || ((uintptr_t)scales & 3) ||
+      (latent_new && (!aligned16(latent_new) || !aligned16(latent))))
+    return ISA_ERR_INVALID_ARG;
+  if (!valid_seqs(s)) return ISA_ERR_INVALID_ARG;
+  for (int i = 0; i < 4; ++i)
+    if (!(w4[i] == w4[i])) return ISA_ERR_INVALID_ARG;
+  if (ws_bytes < HDR) return ISA_ERR_WORKSPACE;
+  BatchArgs a;
+  fill_batch(s, &a, MAX_K);
+  return launch_append(a, key_new, latent_new, w4, s->block_table, scales, keys, latent, pooled, (uint32_t*)ws,
+                       (hipStream_t)stream);
 }
 
 isa_status isa_indexer_prefill_scores(const int8_t* q, const int8_t* head_w, const int32_t* q_pos, int32_t Q,

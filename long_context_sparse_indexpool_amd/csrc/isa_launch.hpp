@@ -32,6 +32,9 @@ isa_status launch_indexpool(const BatchArgs& a, const uint16_t* keys, const floa
                             float* scales, int8_t* pooled, bool dynamic, float* amax_part, uint32_t* err,
                             hipStream_t stream);
 constexpr int POOL_TILE_G = 256;  // groups per pooling work tile (4 pages)
+isa_status launch_append(const BatchArgs& a, const uint16_t* key_new, const uint16_t* latent_new, const float w4[4],
+                         const int32_t* bt, const float* scales, uint16_t* keys, uint16_t* latent, int8_t* pooled,
+                         uint32_t* err, hipStream_t stream);
 
 // Sparse MLA attention: split plan chosen on the host.
 struct MlaPlan {

@@ -37,15 +37,17 @@ __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v 
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
 // Pooled fp32 values of channels 8c..8c+7 of group g (r tokens present).
-__device__ __forceinline__ void pool8(const PoolPtrs& P, const uint16_t* grp, int r, int c, float (&x)[8]) {
+// With `last` given, token r - 1 is taken from it instead of from memory.
+__device__ __forceinline__ void pool8(const float (&wt)[4], const uint16_t* grp, int r, int c, float (&x)[8],
+                                      const v4i* last = nullptr) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) x[i] = 0.f;
   float wsum = 0.f;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     if (t < r) {
-      v4i v = *reinterpret_cast<const v4i*>(grp + t * IDX_DIM + c * 8);
-      const float w = P.w[t];
+      v4i v = (last && t == r - 1) ? *last : *reinterpret_cast<const v4i*>(grp + t * IDX_DIM + c * 8);
+      const float w = wt[t];
       wsum += w;
       x[0] = fmaf(w, bf16_lo(v.x), x[0]);
       x[1] = fmaf(w, bf16_hi(v.x), x[1]);
@@ -61,6 +63,19 @@ __device__ __forceinline__ void pool8(const PoolPtrs& P, const uint16_t* grp, in
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = x[i] / wsum;
   }
+}
+
+// Eight pooled values quantised with `scale`: round half to even, clamp to
+// +-127, packed little-endian.
+__device__ __forceinline__ uint2 quant8(const float (&x)[8], float scale) {
+  uint32_t packed[2] = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float qv = __builtin_rintf(x[i] / scale);  // round half to even
+    qv = fminf(fmaxf(qv, -127.f), 127.f);
+    packed[i >> 2] |= ((uint32_t)((int32_t)qv) & 0xFFu) << (8 * (i & 3));
+  }
+  return make_uint2(packed[0], packed[1]);
 }
 
 template <bool QUANT>
@@ -100,17 +115,10 @@ __global__ __launch_bounds__(POOL_THREADS) void k_pool(const BatchArgs a, const 
     const int r = min(4, L - 4 * g);
     const uint16_t* grp = P.keys + ((size_t)pg * PAGE_TOK + (size_t)(4 * g) % PAGE_TOK) * IDX_DIM;
     float x[8];
-    pool8(P, grp, r, c, x);
+    pool8(P.w, grp, r, c, x);
     if (QUANT) {
-      uint32_t packed[2] = {0, 0};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float qv = __builtin_rintf(x[i] / scale);  // round half to even
-        qv = fminf(fmaxf(qv, -127.f), 127.f);
-        packed[i >> 2] |= ((uint32_t)((int32_t)qv) & 0xFFu) << (8 * (i & 3));
-      }
       int8_t* dst = P.pooled + ((size_t)pg * PAGE_GRP + g % PAGE_GRP) * IDX_DIM + c * 8;
-      *reinterpret_cast<uint2*>(dst) = make_uint2(packed[0], packed[1]);
+      *reinterpret_cast<uint2*>(dst) = quant8(x, scale);
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -150,6 +158,57 @@ __global__ __launch_bounds__(POOL_THREADS) void k_pool(const BatchArgs a, const 
     P.scales[b] = mm > 0.f ? mm / 127.f : 1.f;
     __hip_atomic_store(&P.tickets[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+// Decode-time append: one 64-thread workgroup per sequence writes the new
+// token (position L - 1) into the key and latent pools and re-pools its group
+// from the r tokens now present, with the same arithmetic as k_pool, so the
+// result equals a full re-pool at the given scale.  Threads 0..15 own 8 key
+// channels each; all 64 copy 16 B of the latent row.  The new key enters the
+// pooling from registers; the group's earlier tokens come from earlier calls.
+struct AppendPtrs {
+  const uint16_t* key_new;
+  const uint16_t* latent_new;
+  const int32_t* bt;
+  const float* scales;
+  uint16_t* keys;
+  uint16_t* latent;
+  int8_t* pooled;
+  uint32_t* err;
+  float w[4];
+};
+
+__global__ __launch_bounds__(64) void k_append(const BatchArgs a, const AppendPtrs A) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int t = a.lens[b] - 1;  // the new token
+  const int pg = phys_page(A.bt, a.max_pages, a.num_pages, b, t / PAGE_TOK, A.err);
+  if (pg < 0) return;
+  const size_t row = (size_t)pg * PAGE_TOK + t % PAGE_TOK;
+  if (A.latent_new) {
+    const v4i v = reinterpret_cast<const v4i*>(A.latent_new + (size_t)b * LAT_DIM)[tid];
+    reinterpret_cast<v4i*>(A.latent + row * LAT_DIM)[tid] = v;
+  }
+  if (tid >= IDX_DIM / 8) return;
+  const v4i k = reinterpret_cast<const v4i*>(A.key_new + (size_t)b * IDX_DIM)[tid];
+  reinterpret_cast<v4i*>(A.keys + row * IDX_DIM)[tid] = k;
+  const int g = t / GROUP, r = t % GROUP + 1;
+  float scale = A.scales[b];
+  if (!(scale > 0.f) || !isfinite(scale)) {
+    if (tid == 0) report(A.err, ISA_DERR_NONFINITE);
+    scale = 1.f;
+  }
+  const uint16_t* grp = A.keys + ((size_t)pg * PAGE_TOK + (size_t)(4 * g) % PAGE_TOK) * IDX_DIM;
+  float x[8];
+  pool8(A.w, grp, r, tid, x, &k);
+  *reinterpret_cast<uint2*>(A.pooled + ((size_t)pg * PAGE_GRP + g % PAGE_GRP) * IDX_DIM + tid * 8) = quant8(x, scale);
+}
+
+isa_status launch_append(const BatchArgs& a, const uint16_t* key_new, const uint16_t* latent_new, const float w4[4],
+                         const int32_t* bt, const float* scales, uint16_t* keys, uint16_t* latent, int8_t* pooled,
+                         uint32_t* err, hipStream_t stream) {
+  AppendPtrs A{key_new, latent_new, bt, scales, keys, latent, pooled, err, {w4[0], w4[1], w4[2], w4[3]}};
+  hipLaunchKernelGGL(k_append, dim3(a.batch), dim3(64), 0, stream, a, A);
+  return hipGetLastError() == hipSuccess ? ISA_OK : ISA_ERR_HIP;
 }
 
 isa_status launch_indexpool(const BatchArgs& a, const uint16_t* keys, const float w4[4], const int32_t* bt,

@@ -186,6 +186,32 @@ def test_shared_attention_rejects(m, case):
     assert rc == (m.ISA_ERR_WORKSPACE if case == "ws_small" else m.ISA_ERR_INVALID_ARG)
 
 
+@pytest.mark.parametrize("case", ["null_key", "latent_mismatch", "misaligned", "nan_w", "ws_small", "zero_len",
+                                  "pages_short"])
+def test_append_token_rejects(m, case):
+    lens, mp = [257, 1024, 5], None
+    key, lat_new, lat, wsb = P, P, P, 256
+    w = (ctypes.c_float * 4)(0.25, 0.25, 0.25, 0.25)
+    if case == "null_key":
+        key = None
+    elif case == "latent_mismatch":
+        lat = None
+    elif case == "misaligned":
+        key = P + 2
+    elif case == "nan_w":
+        w[2] = float("nan")
+    elif case == "ws_small":
+        wsb = 128
+    elif case == "zero_len":
+        lens = [257, 0, 5]
+    elif case == "pages_short":
+        mp = 1  # 257 tokens need two pages
+    s = FakeSeqs(m, lens, max_pages=mp)
+    rc = m.lib.isa_append_token(key, lat_new, ctypes.cast(w, ctypes.c_void_p), s.c, P, P, lat, P, P, wsb, None)
+    assert rc == (m.ISA_ERR_WORKSPACE if case == "ws_small" else m.ISA_ERR_INVALID_ARG)
+    assert m.lib.isa_workspace_size(m.ISA_OP_APPEND_TOKEN, FakeSeqs(m, [5]).c, 0, 0) == 256
+
+
 @pytest.mark.parametrize("case", ["batch2", "q0", "ld_small", "null_pos"])
 def test_prefill_scores_rejects(m, case):
     s = FakeSeqs(m, [1 << 20] if case != "batch2" else [1000, 1000])

@@ -218,6 +218,69 @@ def test_index_share_layers():
     assert np.array_equal(one[0][0], out1) and np.array_equal(one[0][1], lse1)
 
 
+def test_append_tokens_match_repool():
+    """Decode-time appends: nine tokens appended one call at a time to every
+    sequence (tails of each length, group completions, page crossings), with a
+    fixed scale per sequence.  After each call the group holding the new token
+    matches the oracle's pooling of the extended sequence at that scale; at the
+    end the key and latent pools hold the appended rows and the pooled cache is
+    bit-identical to a full isa_indexpool at the same scales."""
+    m = H.isa()
+    L0 = np.array([1, 255, 254, 1021, 2048, 4996, 3])
+    n_app = 9
+    wl = custom("append", 23, list(L0 + n_app), paged_random=True)
+    B, to = wl.batch, wl.token_offsets
+    keys, lat = wl.keys_logical(), wl.latent_logical()
+    w4 = wl.pool_weights()
+    scale = np.array([oracle.pool(keys[to[b]: to[b + 1]], w4)[1] for b in range(B)], np.float32)
+    scale[2] *= np.float32(0.5)  # values clamp at +-127
+    # pools holding only the first L0 tokens of each sequence (NaN bits after)
+    kh, lh = keys.copy(), lat.copy()
+    for b in range(B):
+        kh[to[b] + L0[b]: to[b + 1]] = H.NAN_BF16
+        lh[to[b] + L0[b]: to[b + 1]] = H.NAN_BF16
+    kd = H.pool_from_logical(wl, kh, 256, H.NAN_BF16)
+    ld = H.pool_from_logical(wl, lh, 256, H.NAN_BF16)
+    bt = torch.from_numpy(wl.block_table()).cuda()
+    pooled = torch.zeros((wl.num_pages, 64, IDX_DIM), dtype=torch.int8, device="cuda")
+    sc = torch.from_numpy(scale).cuda()
+    ws = m.alloc_workspace(m.workspace_size(m.ISA_OP_INDEXPOOL, m.Seqs(list(L0 + n_app), bt, wl.num_pages)))
+    m.isa_indexpool(kd, w4, m.Seqs(list(L0), bt, wl.num_pages), sc, pooled, 1, ws)
+    wsa = m.alloc_workspace(m.workspace_size(m.ISA_OP_APPEND_TOKEN, None))
+    for j in range(n_app):
+        lens = L0 + j + 1
+        seqs = m.Seqs(list(lens), bt, wl.num_pages)
+        knew = torch.from_numpy(np.stack([keys[to[b] + lens[b] - 1] for b in range(B)]).view(np.int16)).cuda()
+        lnew = torch.from_numpy(np.stack([lat[to[b] + lens[b] - 1] for b in range(B)]).view(np.int16)).cuda()
+        m.isa_append_token(knew, lnew, w4, seqs, sc, kd, ld, pooled, wsa)
+        torch.cuda.synchronize()
+        for b in range(B):
+            g = (lens[b] - 1) // 4
+            pg = int(wl.block_table()[b, g // 64])
+            got = pooled[pg, g % 64].cpu().numpy().astype(int)
+            ref = oracle.pool_given_scale(keys[to[b]: to[b] + lens[b]], w4, float(scale[b]))[g].astype(int)
+            assert np.max(np.abs(got - ref)) <= 1, f"sequence {b}, length {lens[b]}"
+    assert m.isa_device_error(wsa) == 0
+    # the appended rows landed in the key and latent pools
+    btn = wl.block_table()
+    for b in range(B):
+        for t in range(L0[b], L0[b] + n_app):
+            pg, row = int(btn[b, t // 256]), t % 256
+            assert np.array_equal(kd[pg, row].cpu().numpy().view(np.uint16), keys[to[b] + t])
+            assert np.array_equal(ld[pg, row].cpu().numpy().view(np.uint16), lat[to[b] + t])
+    # the same cache as a full pooling of the extended sequences at the same scales
+    full = torch.zeros_like(pooled)
+    m.isa_indexpool(kd, w4, m.Seqs(list(L0 + n_app), bt, wl.num_pages), sc, full, 1, ws)
+    torch.cuda.synchronize()
+    assert m.isa_device_error(ws) == 0
+    for b in range(B):
+        G = (L0[b] + n_app + 3) // 4
+        pages = bt[b, : (G + 63) // 64].long()
+        a_ = pooled[pages].reshape(-1, IDX_DIM)[:G]
+        f_ = full[pages].reshape(-1, IDX_DIM)[:G]
+        assert torch.equal(a_, f_), f"sequence {b}"
+
+
 def test_attention_rows_with_positions(ragged_batch):
     """Rows that map to sequences with an earlier last-visible position (prefill rows)."""
     db = ragged_batch
