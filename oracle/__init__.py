@@ -57,6 +57,14 @@ def _load():
             lib.oracle_topk.restype = ctypes.c_int
             lib.oracle_attention.argtypes = [vp, vp, i64, i64, vp, i32, ctypes.c_double, vp, vp]
             lib.oracle_attention.restype = ctypes.c_int
+            lib.oracle_fp8_decode.argtypes = [ctypes.c_uint8]
+            lib.oracle_fp8_decode.restype = ctypes.c_double
+            lib.oracle_fp8_encode.argtypes = [ctypes.c_float]
+            lib.oracle_fp8_encode.restype = ctypes.c_uint8
+            lib.oracle_latent_fp8.argtypes = [vp, i64, vp, vp]
+            lib.oracle_latent_fp8.restype = ctypes.c_int
+            lib.oracle_attention_fp8.argtypes = [vp, vp, vp, i64, i64, vp, i32, ctypes.c_double, vp, vp]
+            lib.oracle_attention_fp8.restype = ctypes.c_int
             _lib = lib
     return _lib
 
@@ -194,6 +202,45 @@ def attention(q: np.ndarray, lat: np.ndarray, L: int, pos: int, sel: np.ndarray,
                                   _ptr(out), _ptr(lse))
     if rc != 0:
         raise ValueError(f"oracle_attention rc={rc}")
+    return out, lse
+
+
+# ------------------------------------------------------------------ FP8 latent cache
+def fp8_decode(code: int) -> float:
+    """Value of an OCP E4M3 code (NaN for 0x7F / 0xFF)."""
+    return float(_load().oracle_fp8_decode(int(code)))
+
+
+def fp8_encode(x: float) -> int:
+    """Nearest E4M3 code of an fp32 value (ties to even; past 464 in magnitude: NaN)."""
+    return int(_load().oracle_fp8_encode(float(x)))
+
+
+def latent_fp8(lat: np.ndarray):
+    """bf16 bits [n,512] -> (codes uint8 [n,512], scales fp32 [n]): per-row amax/448 scale."""
+    lat = _c(lat, np.uint16)
+    n = lat.shape[0]
+    codes = np.empty((n, LAT_DIM), np.uint8)
+    scales = np.empty(n, np.float32)
+    rc = _load().oracle_latent_fp8(_ptr(lat), int(n), _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError(f"oracle_latent_fp8 rc={rc}")
+    return codes, scales
+
+
+def attention_fp8(q: np.ndarray, codes: np.ndarray, scales: np.ndarray, L: int, pos: int, sel: np.ndarray,
+                  count: int, scale: float):
+    """attention() over an FP8 cache: latent value of token t = scales[t] * decode(codes[t])."""
+    q = _c(q, np.uint16)
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.float32)
+    sel = _c(sel, np.int32)
+    out = np.empty((ATT_HEADS, LAT_DIM), np.float64)
+    lse = np.empty(ATT_HEADS, np.float64)
+    rc = _load().oracle_attention_fp8(_ptr(q), _ptr(codes), _ptr(scales), int(L), int(pos), _ptr(sel), int(count),
+                                      float(scale), _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise ValueError(f"oracle_attention_fp8 rc={rc}")
     return out, lse
 
 

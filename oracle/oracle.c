@@ -137,8 +137,20 @@ int oracle_topk(const int64_t* S, int64_t G, int32_t K, int32_t* idx, int32_t* c
   return 0;
 }
 
-int oracle_attention(const uint16_t* q, const uint16_t* lat, int64_t L, int64_t pos, const int32_t* sel,
-                     int32_t count, double scale, double* out, double* lse) {
+/* Latent value of token t, channel d, from one of the two cache formats. */
+typedef struct {
+  const uint16_t* bf16; /* [L,512] bf16 bits, or NULL */
+  const uint8_t* codes; /* [L,512] fp8 E4M3 codes (when bf16 is NULL) */
+  const float* scales;  /* [L] per-row scales of the codes */
+} latent_rows;
+
+static double latent_value(const latent_rows* c, int64_t t, int d) {
+  if (c->bf16) return bf16_value(c->bf16[t * OR_LAT_DIM + d]);
+  return (double)c->scales[t] * oracle_fp8_decode(c->codes[t * OR_LAT_DIM + d]);
+}
+
+static int attention_rows(const uint16_t* q, const latent_rows* lat, int64_t L, int64_t pos, const int32_t* sel,
+                          int32_t count, double scale, double* out, double* lse) {
   if (L < 1 || count < 0) return -1;
   /* the visible tokens of the selected groups */
   int64_t* tok = (int64_t*)malloc(sizeof(int64_t) * (size_t)(count > 0 ? count : 1) * OR_GROUP);
@@ -167,7 +179,7 @@ int oracle_attention(const uint16_t* q, const uint16_t* lat, int64_t L, int64_t 
     for (int64_t i = 0; i < T; ++i) {
       double dot = 0.0;
       for (int d = 0; d < OR_LAT_DIM; ++d)
-        dot += bf16_value(q[h * OR_LAT_DIM + d]) * bf16_value(lat[tok[i] * OR_LAT_DIM + d]);
+        dot += bf16_value(q[h * OR_LAT_DIM + d]) * latent_value(lat, tok[i], d);
       s[i] = dot * scale;
       if (s[i] > m) m = s[i];
     }
@@ -175,7 +187,7 @@ int oracle_attention(const uint16_t* q, const uint16_t* lat, int64_t L, int64_t 
     for (int64_t i = 0; i < T; ++i) {
       double e = exp(s[i] - m);
       l += e;
-      for (int d = 0; d < OR_LAT_DIM; ++d) o[d] += e * bf16_value(lat[tok[i] * OR_LAT_DIM + d]);
+      for (int d = 0; d < OR_LAT_DIM; ++d) o[d] += e * latent_value(lat, tok[i], d);
     }
     for (int d = 0; d < OR_LAT_DIM; ++d) o[d] /= l;
     lse[h] = m + log(l);
@@ -183,4 +195,69 @@ int oracle_attention(const uint16_t* q, const uint16_t* lat, int64_t L, int64_t 
   free(tok);
   free(s);
   return 0;
+}
+
+int oracle_attention(const uint16_t* q, const uint16_t* lat, int64_t L, int64_t pos, const int32_t* sel,
+                     int32_t count, double scale, double* out, double* lse) {
+  latent_rows c = {lat, NULL, NULL};
+  return attention_rows(q, &c, L, pos, sel, count, scale, out, lse);
+}
+
+/* ---- FP8 latent cache ([WIKI] quantisation section: the recent cache in FP8) ----
+ * OCP 8-bit E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent 0
+ * holds subnormals m/8 * 2^-6; S.1111.111 is NaN and there are no infinities, so
+ * the largest value is 1.75 * 2^8 = 448. */
+double oracle_fp8_decode(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9); /* m/8 * 2^-6 */
+  else
+    v = ldexp(8.0 + m, e - 10); /* (1 + m/8) * 2^(e-7) */
+  return s ? -v : v;
+}
+
+uint8_t oracle_fp8_encode(float x) {
+  if (isnan(x)) return 0x7F;
+  uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  double a = fabs((double)x);
+  if (a > 464.0) return sign | 0x7F;  /* rounds past the largest value: NaN (no saturation) */
+  if (a >= 448.0) return sign | 0x7E; /* [448, 464] -> 448 (464 is a tie: to the even mantissa) */
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e); /* a = f * 2^e, f in [0.5, 1): the leading bit is 2^(e-1) */
+  int ub = e - 1;
+  if (ub < -6) ub = -6; /* below the smallest normal the spacing stays 2^-9 */
+  double q = nearbyint(ldexp(a, 3 - ub)); /* units of the spacing 2^(ub-3); ties to even */
+  if (q >= 16.0) { /* rounded up into the next binade */
+    ub += 1;
+    q = 8.0;
+  }
+  if (ub == -6 && q < 8.0) return sign | (uint8_t)q; /* subnormal (or zero) */
+  return sign | (uint8_t)(((ub + 7) << 3) | ((int)q - 8));
+}
+
+int oracle_latent_fp8(const uint16_t* lat, int64_t n, uint8_t* codes, float* scales) {
+  for (int64_t t = 0; t < n; ++t) {
+    float amax = 0.f;
+    for (int d = 0; d < OR_LAT_DIM; ++d) {
+      float v = (float)bf16_value(lat[t * OR_LAT_DIM + d]);
+      if (isnan(v) || isinf(v)) return -1;
+      if (fabsf(v) > amax) amax = fabsf(v);
+    }
+    float s = amax > 0.f ? amax / 448.f : 1.f;
+    scales[t] = s;
+    for (int d = 0; d < OR_LAT_DIM; ++d) {
+      float v = (float)bf16_value(lat[t * OR_LAT_DIM + d]);
+      codes[t * OR_LAT_DIM + d] = oracle_fp8_encode(v / s);
+    }
+  }
+  return 0;
+}
+
+int oracle_attention_fp8(const uint16_t* q, const uint8_t* codes, const float* scales, int64_t L, int64_t pos,
+                         const int32_t* sel, int32_t count, double scale, double* out, double* lse) {
+  latent_rows c = {NULL, codes, scales};
+  return attention_rows(q, &c, L, pos, sel, count, scale, out, lse);
 }

@@ -88,6 +88,23 @@ int oracle_topk(const int64_t* S, int64_t G, int32_t K, int32_t* idx, int32_t* c
 int oracle_attention(const uint16_t* q, const uint16_t* lat, int64_t L, int64_t pos, const int32_t* sel,
                      int32_t count, double scale, double* out, double* lse);
 
+/* FP8 latent cache ([WIKI] quantisation section: the recent, high-importance
+ * cache is kept in FP8).  The pages name no FP8 format or scaling; this oracle
+ * follows the library's contract: OCP E4M3 (bias 7, subnormals, S.1111.111 =
+ * NaN, no infinities, largest value 448) with one fp32 scale per latent row.
+ *   decode: the value of a code (NaN for the two NaN codes)
+ *   encode: nearest value, ties to the even mantissa; a value that rounds past
+ *           448 (|x| > 464) becomes NaN (no saturation); NaN -> 0x7F
+ *   oracle_latent_fp8: per row, amax over its 512 bf16 values (as fp32),
+ *           scale = amax / 448 in fp32 (1 when amax == 0), code = encode(x / scale)
+ *           with the division in fp32.  Returns -1 for a non-finite value.
+ *   oracle_attention_fp8: oracle_attention with latent value scales[t] * decode(code). */
+double oracle_fp8_decode(uint8_t c);
+uint8_t oracle_fp8_encode(float x);
+int oracle_latent_fp8(const uint16_t* lat, int64_t n, uint8_t* codes, float* scales);
+int oracle_attention_fp8(const uint16_t* q, const uint8_t* codes, const float* scales, int64_t L, int64_t pos,
+                         const int32_t* sel, int32_t count, double scale, double* out, double* lse);
+
 #ifdef __cplusplus
 }
 #endif

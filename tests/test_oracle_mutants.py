@@ -42,6 +42,14 @@ MUTANTS = {
                               [lambda rng: pins.test_attention_dense_fallback_is_textbook_attention(rng, 100)]),
     "reads_past_sequence_end": ("if (t < L && t <= pos)", "if (t <= pos)",
                                 [pins.test_attention_order_invariance_and_causality]),
+    "fp8_bias_8": ("v = ldexp(8.0 + m, e - 10);", "v = ldexp(8.0 + m, e - 11);",
+                   [lambda rng: pins.test_fp8_decode_table()]),
+    "fp8_ties_away": ("double q = nearbyint(ldexp(a, 3 - ub));", "double q = round(ldexp(a, 3 - ub));",
+                      [lambda rng: pins.test_fp8_encode_round_trip_and_nearest()]),
+    "fp8_scale_int8_range": ("float s = amax > 0.f ? amax / 448.f : 1.f;", "float s = amax > 0.f ? amax / 127.f : 1.f;",
+                             [pins.test_latent_fp8_rows]),
+    "fp8_row_scale_ignored": ("return (double)c->scales[t] * oracle_fp8_decode", "return oracle_fp8_decode",
+                              [pins.test_attention_fp8_equals_bf16_attention_on_exact_values]),
 }
 
 

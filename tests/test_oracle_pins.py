@@ -441,3 +441,82 @@ def test_attention_empty_selection():
     out, lse = oracle.attention(np.zeros((64, 512), np.uint16), np.zeros((8, 512), np.uint16), 8, 7,
                                 np.array([-1], np.int32), 0, SCALE)
     assert not np.any(out) and np.all(np.isneginf(lse))
+
+
+# ---------------------------------------------------------------------- FP8 latent cache
+# OCP E4M3 facts: bias 7, 3 mantissa bits, subnormals m/8 * 2^-6, S.1111.111 = NaN,
+# no infinities, so the largest finite value is 1.75 * 2^8 = 448.
+
+def test_fp8_decode_table():
+    assert oracle.fp8_decode(0x00) == 0.0 and math.copysign(1.0, oracle.fp8_decode(0x80)) == -1.0
+    assert oracle.fp8_decode(0x01) == 2.0 ** -9 and oracle.fp8_decode(0x07) == 7 * 2.0 ** -9
+    assert oracle.fp8_decode(0x08) == 2.0 ** -6 and oracle.fp8_decode(0x38) == 1.0
+    assert oracle.fp8_decode(0x39) == 1.125 and oracle.fp8_decode(0x40) == 2.0
+    assert oracle.fp8_decode(0x7E) == 448.0 and oracle.fp8_decode(0xFE) == -448.0
+    assert math.isnan(oracle.fp8_decode(0x7F)) and math.isnan(oracle.fp8_decode(0xFF))
+    pos = [oracle.fp8_decode(c) for c in range(0x7F)]
+    assert all(a < b for a, b in zip(pos, pos[1:]))  # strictly increasing codes 0x00..0x7E
+    for c in range(0x7F):
+        assert oracle.fp8_decode(c | 0x80) == -pos[c]
+
+
+def test_fp8_encode_round_trip_and_nearest():
+    for c in range(256):
+        if c in (0x7F, 0xFF):
+            continue
+        assert oracle.fp8_encode(oracle.fp8_decode(c)) == c
+    pos = [oracle.fp8_decode(c) for c in range(0x7F)]
+    for c in range(0x7E):
+        lo, hi = pos[c], pos[c + 1]
+        mid = (lo + hi) / 2  # exact in fp32 for these values
+        assert oracle.fp8_encode(mid) == (c if c % 2 == 0 else c + 1), hex(c)  # ties to the even mantissa
+        gap = hi - lo
+        assert oracle.fp8_encode(lo + 0.25 * gap) == c and oracle.fp8_encode(hi - 0.25 * gap) == c + 1
+        assert oracle.fp8_encode(-(lo + 0.25 * gap)) == (c | 0x80 if c else 0x80)
+
+
+def test_fp8_encode_overflow_is_nan():
+    assert oracle.fp8_encode(448.0) == 0x7E and oracle.fp8_encode(464.0) == 0x7E
+    assert oracle.fp8_encode(464.5) == 0x7F and oracle.fp8_encode(-1e9) == 0xFF
+    assert oracle.fp8_encode(float("nan")) == 0x7F
+
+
+def test_latent_fp8_rows(rng):
+    lat = synth.normal_bf16(31, 5, (40, 512))
+    lat[3] = 0  # a zero row
+    lat[5, 17] = bf16_bits([-96.0])[0]  # a row whose amax is a negative outlier
+    codes, scales = oracle.latent_fp8(lat)
+    x = f32(lat)
+    for t in range(40):
+        amax = np.float32(np.max(np.abs(x[t])))
+        if amax == 0:
+            assert scales[t] == 1.0 and not np.any(codes[t])
+            continue
+        assert scales[t] == np.float32(amax / np.float32(448.0))
+        j = int(np.argmax(np.abs(x[t])))
+        assert codes[t, j] == (0x7E if x[t, j] > 0 else 0xFE)  # the amax element maps to +-448
+        v = np.array([oracle.fp8_decode(c) for c in codes[t]])
+        y = (x[t].astype(np.float32) / scales[t]).astype(np.float64)
+        # within half a spacing of the nearest code (spacing 2^(e-3), at least 2^-9)
+        e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -6)))
+        assert np.all(np.abs(y - v) <= 2.0 ** (e - 3) / 2 + 1e-12)
+        assert np.all(np.sign(v) * np.sign(y) >= 0)
+
+
+def test_attention_fp8_equals_bf16_attention_on_exact_values(rng):
+    """Codes with power-of-two row scales are exact bf16 values, so the FP8 cache
+    and the bf16 cache of the same values must give identical attention."""
+    L = 300
+    codes = rng.integers(0, 0x7F, size=(L, 512)).astype(np.uint8)
+    codes[codes == 0x7F] = 0x7E
+    codes |= (rng.integers(0, 2, size=(L, 512)) * 0x80).astype(np.uint8)
+    scales = (2.0 ** rng.integers(-6, 3, size=L)).astype(np.float32)
+    vals = np.array([[oracle.fp8_decode(c) for c in row] for row in codes]) * scales[:, None]
+    lat = bf16_bits(vals.astype(np.float32))
+    q = synth.normal_bf16(32, 6, (64, 512))
+    sel = np.sort(rng.choice(L // 4, size=40, replace=False)).astype(np.int32)
+    a = oracle.attention(q, lat, L, L - 1, sel, len(sel), SCALE)
+    b = oracle.attention_fp8(q, codes, scales, L, L - 1, sel, len(sel), SCALE)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    c = oracle.attention_fp8(q, codes, scales * np.float32(2.0), L, L - 1, sel, len(sel), SCALE)
+    assert not np.allclose(c[0], a[0])  # the row scales enter the result
