@@ -233,6 +233,52 @@ def bench_index_share(dec, n_layers=4, steps=100, warmup=10):
     return res
 
 
+def bench_fp8(dec, steps=100, warmup=10):
+    """FP8 latent cache on the headline workload: the whole latent pool quantised
+    once (isa_latent_to_fp8, timed), then decode steps with the attention over the
+    FP8 cache (512 B + a 4 B scale per token instead of 1 KiB)."""
+    import torch
+
+    import harness as H
+    from synth.configs import SM_SCALE
+
+    m, wl = dec.m, dec.wl
+    B = wl.batch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    codes, scales = H.latent_fp8(dec.db)
+    t_q = time.perf_counter() - t0
+
+    def step(j):
+        dec.topk(j)
+        m.isa_sparse_mla_decode_fp8(dec.qa[j % len(dec.qa)], codes, scales, dec.db.seqs, None, None, B, dec.idx,
+                                    dec.cnt, dec.k, SM_SCALE, dec.out, dec.lse, dec.ws_att)
+
+    for j in range(warmup):
+        step(j)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(steps):
+        step(j)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for j in range(20):
+        m.isa_sparse_mla_decode_fp8(dec.qa[j % len(dec.qa)], codes, scales, dec.db.seqs, None, None, B, dec.idx,
+                                    dec.cnt, dec.k, SM_SCALE, dec.out, dec.lse, dec.ws_att)
+    ev[1].record()
+    torch.cuda.synchronize()
+    t_att = ev[0].elapsed_time(ev[1]) / 20 * 1e3
+    tokens = sum(wl.lens)
+    del codes, scales
+    torch.cuda.empty_cache()
+    res = {"steps_per_s": round(1 / sec, 1), "ms_per_step": round(sec * 1e3, 4), "sparse_mla_us": round(t_att, 2),
+           "quantise_ms": round(t_q * 1e3, 2), "quantise_GBps": round(tokens * (1024 + 512 + 4) / t_q / 1e9, 1)}
+    log(f"{wl.name}: FP8 latent cache: {res['steps_per_s']} steps/s, attention call {t_att:.1f} us")
+    return res
+
+
 def bench_append(batch=8, length=1 << 20, reps=200):
     """Decode-time cache maintenance: isa_append_token for a batch of
     `batch` sequences at `length` tokens (one new key and latent row each, the
@@ -528,6 +574,7 @@ def main():
         secondary["indexpool"] = bench_pool(dec)
         secondary["index_share"] = bench_index_share(dec)
         secondary["append_token"] = bench_append()
+        secondary["fp8_latent"] = bench_fp8(dec)
     dec.free()
     if not args.primary_only:
         for i in (1, 4):

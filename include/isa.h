@@ -95,7 +95,8 @@ enum {
   ISA_OP_INDEXER_TOPK = 2,
   ISA_OP_SPARSE_MLA = 3,
   ISA_OP_PREFILL_SCORES = 4,
-  ISA_OP_APPEND_TOKEN = 5
+  ISA_OP_APPEND_TOKEN = 5,
+  ISA_OP_LATENT_FP8 = 6
 };
 
 /* Workspace bytes (a multiple of 256) that `op` needs for these sequences.
@@ -266,6 +267,36 @@ isa_status isa_indexer_prefill_scores(const int8_t* q, const int8_t* head_w, con
 isa_status isa_append_token(const uint16_t* key_new, const uint16_t* latent_new, const float* w4, const isa_seqs* s,
                             const float* scales, uint16_t* keys, uint16_t* latent, int8_t* pooled, void* ws,
                             size_t ws_bytes, isa_stream_t stream);
+
+/*
+ * (7) FP8 latent cache ([WIKI] quantisation section: the recent, high-importance
+ * cache is kept in FP8).  The pages name no format; this library's contract:
+ * OCP E4M3 codes (bias 7, subnormals, S.1111.111 = NaN, largest value 448) with
+ * one fp32 scale per latent row.
+ *
+ * isa_latent_to_fp8 quantises every row t < L_b of the batch's sequences:
+ * scale = amax / 448 over the row's 512 bf16 values (1 for a zero row), code =
+ * nearest E4M3 value of x / scale (ties to even; the division in fp32).
+ *   latent     [dev] bf16 bits [num_pages, 256, 512]
+ *   codes      [dev] uint8 [num_pages, 256, 512] (rows of the sequences written)
+ *   row_scales [dev] fp32 [num_pages, 256]
+ * Workspace: isa_workspace_size(ISA_OP_LATENT_FP8, ...) bytes.  A non-finite
+ * latent value sets ISA_DERR_NONFINITE.
+ *
+ * isa_sparse_mla_decode_fp8 is isa_sparse_mla_decode over such a cache: the
+ * latent value of token t is row_scales[t] * decode(codes[t]).  Arithmetic:
+ * codes decoded exactly to fp16, the query converted to fp16, fp16 products with
+ * fp32 accumulation; the row scale multiplies the fp32 score and is folded into
+ * the fp16 probability of the P.V product.  Row scales must be positive, finite
+ * and at most 128.  Arguments, results and errors otherwise as
+ * isa_sparse_mla_decode (same workspace size).
+ */
+isa_status isa_latent_to_fp8(const uint16_t* latent, const isa_seqs* s, uint8_t* codes, float* row_scales, void* ws,
+                             size_t ws_bytes, isa_stream_t stream);
+isa_status isa_sparse_mla_decode_fp8(const uint16_t* q, const uint8_t* codes, const float* row_scales,
+                                     const isa_seqs* s, const int32_t* row_seq, const int32_t* row_pos, int32_t rows,
+                                     const int32_t* idx, const int32_t* count, int32_t k, float sm_scale, float* out,
+                                     float* lse, void* ws, size_t ws_bytes, isa_stream_t stream);
 
 #ifdef __cplusplus
 }

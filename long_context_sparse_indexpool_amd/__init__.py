@@ -26,6 +26,7 @@ MAX_BATCH, MAX_SEQ_LEN, MAX_K = 256, 1 << 22, 512
 
 ISA_OK, ISA_ERR_INVALID_ARG, ISA_ERR_UNSUPPORTED, ISA_ERR_WORKSPACE, ISA_ERR_HIP = range(5)
 ISA_OP_INDEXPOOL, ISA_OP_INDEXER_TOPK, ISA_OP_SPARSE_MLA, ISA_OP_PREFILL_SCORES, ISA_OP_APPEND_TOKEN = 1, 2, 3, 4, 5
+ISA_OP_LATENT_FP8 = 6
 ISA_SCALE_DYNAMIC, ISA_SCALE_GIVEN = 0, 1
 ISA_MAX_LAYERS = 8  # layers sharing one selection (isa_sparse_mla_decode_shared)
 DERR_PAGE_OOB, DERR_HEADW_RANGE, DERR_SCORE_OVERFLOW, DERR_ROW_RANGE, DERR_NONFINITE = 1, 2, 4, 8, 16
@@ -34,7 +35,8 @@ ISA_TIMER_INDEXER_SCORE, ISA_TIMER_MLA_SPLIT = 1, 2
 
 EXPORTS = ("isa_workspace_size", "isa_workspace_init", "isa_device_error", "isa_status_string", "isa_version",
            "isa_set_kernel_timer", "isa_indexpool", "isa_indexer_topk", "isa_sparse_mla_decode",
-           "isa_sparse_mla_decode_shared", "isa_indexer_prefill_scores", "isa_append_token")
+           "isa_sparse_mla_decode_shared", "isa_indexer_prefill_scores", "isa_append_token", "isa_latent_to_fp8",
+           "isa_sparse_mla_decode_fp8")
 
 
 class IsaError(RuntimeError):
@@ -70,9 +72,12 @@ def _load() -> ctypes.CDLL:
                                                  vp, sz, vp]
     lib.isa_indexer_prefill_scores.argtypes = [vp, vp, vp, i32, vp, sp, vp, i32, vp, sz, vp]
     lib.isa_append_token.argtypes = [vp, vp, vp, sp, vp, vp, vp, vp, vp, sz, vp]
+    lib.isa_latent_to_fp8.argtypes = [vp, sp, vp, vp, vp, sz, vp]
+    lib.isa_sparse_mla_decode_fp8.argtypes = [vp, vp, vp, sp, vp, vp, i32, vp, vp, i32, ctypes.c_float, vp, vp, vp,
+                                              sz, vp]
     for f in ("isa_workspace_init", "isa_device_error", "isa_set_kernel_timer", "isa_indexpool", "isa_indexer_topk",
               "isa_sparse_mla_decode", "isa_sparse_mla_decode_shared", "isa_indexer_prefill_scores",
-              "isa_append_token"):
+              "isa_append_token", "isa_latent_to_fp8", "isa_sparse_mla_decode_fp8"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -185,6 +190,28 @@ def isa_append_token(key_new: torch.Tensor, latent_new: Optional[torch.Tensor], 
         ctypes.cast(w, ctypes.c_void_p), seqs.c, _ptr(scales, torch.float32, "scales"),
         _ptr(v16(keys), torch.int16, "keys"), _ptr(v16(latent), torch.int16, "latent"),
         _ptr(pooled, torch.int8, "pooled"), _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
+
+
+def isa_latent_to_fp8(latent: torch.Tensor, seqs: Seqs, codes: torch.Tensor, row_scales: torch.Tensor,
+                      ws: torch.Tensor, stream=None) -> None:
+    """bf16 latent pool [pages,256,512] -> E4M3 codes uint8 [pages,256,512] and fp32 row scales [pages,256]."""
+    lat = latent if latent.dtype == torch.int16 else latent.view(torch.int16)
+    _check("isa_latent_to_fp8", lib.isa_latent_to_fp8(
+        _ptr(lat, torch.int16, "latent"), seqs.c, _ptr(codes, torch.uint8, "codes"),
+        _ptr(row_scales, torch.float32, "row_scales"), _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
+
+
+def isa_sparse_mla_decode_fp8(q: torch.Tensor, codes: torch.Tensor, row_scales: torch.Tensor, seqs: Seqs,
+                              row_seq: Optional[torch.Tensor], row_pos: Optional[torch.Tensor], rows: int,
+                              idx: torch.Tensor, count: torch.Tensor, k: int, sm_scale: float, out: torch.Tensor,
+                              lse: Optional[torch.Tensor], ws: torch.Tensor, stream=None) -> None:
+    qq = q if q.dtype == torch.int16 else q.view(torch.int16)
+    _check("isa_sparse_mla_decode_fp8", lib.isa_sparse_mla_decode_fp8(
+        _ptr(qq, torch.int16, "q"), _ptr(codes, torch.uint8, "codes"), _ptr(row_scales, torch.float32, "row_scales"),
+        seqs.c, _ptr(row_seq, torch.int32, "row_seq"), _ptr(row_pos, torch.int32, "row_pos"), rows,
+        _ptr(idx, torch.int32, "idx"), _ptr(count, torch.int32, "count"), k, float(sm_scale),
+        _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"), _ptr(ws, torch.uint8, "ws"), ws.numel(),
+        _stream(stream)))
 
 
 def isa_indexer_topk(q: Optional[torch.Tensor], head_w: Optional[torch.Tensor], pooled: Optional[torch.Tensor],

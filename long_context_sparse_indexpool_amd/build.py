@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libisa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.hip", "pool.hip", "indexer_decode.hip", "topk_rows.hip", "mla_decode.hip", "score_prefill.hip"]
+SOURCES = ["api.hip", "pool.hip", "indexer_decode.hip", "topk_rows.hip", "mla_decode.hip", "score_prefill.hip",
+           "latent_fp8.hip"]
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
          # packed fp32 instructions are kept out of every kernel
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

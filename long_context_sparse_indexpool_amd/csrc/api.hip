@@ -138,6 +138,7 @@ size_t isa_workspace_size(int op, const isa_seqs* s, int32_t rows, int32_t cols)
     }
     case ISA_OP_PREFILL_SCORES:
     case ISA_OP_APPEND_TOKEN:
+    case ISA_OP_LATENT_FP8:
       return HDR;
   }
   return 0;
@@ -214,14 +215,17 @@ isa_status isa_indexer_topk(const int8_t* q, const int8_t* head_w, const int8_t*
                                (hipStream_t)stream);
 }
 
-static isa_status sparse_mla(int32_t n_layers, const uint16_t* const* q, const uint16_t* const* latent,
-                             const isa_seqs* s, const int32_t* row_seq, const int32_t* row_pos, int32_t rows,
-                             const int32_t* idx, const int32_t* count, int32_t k, float sm_scale, float* const* out,
-                             float* const* lse, void* ws, size_t ws_bytes, isa_stream_t stream) {
+static isa_status sparse_mla(int32_t n_layers, const uint16_t* const* q, const void* const* latent,
+                             const float* const* lat_scale, const isa_seqs* s, const int32_t* row_seq,
+                             const int32_t* row_pos, int32_t rows, const int32_t* idx, const int32_t* count,
+                             int32_t k, float sm_scale, float* const* out, float* const* lse, void* ws,
+                             size_t ws_bytes, isa_stream_t stream) {
   if (n_layers < 1 || n_layers > ISA_MAX_LAYERS || !q || !latent || !out) return ISA_ERR_INVALID_ARG;
   for (int l = 0; l < n_layers; ++l) {
-    if (!q[l] || !latent[l] || !out[l] || (lse && !lse[l])) return ISA_ERR_INVALID_ARG;
-    if (!aligned16(q[l]) || !aligned16(latent[l]) || !aligned16(out[l]) || (lse && !aligned16(lse[l])))
+    if (!q[l] || !latent[l] || !out[l] || (lse && !lse[l]) || (lat_scale && !lat_scale[l]))
+      return ISA_ERR_INVALID_ARG;
+    if (!aligned16(q[l]) || !aligned16(latent[l]) || !aligned16(out[l]) || (lse && !aligned16(lse[l])) ||
+        (lat_scale && !aligned16(lat_scale[l])))
       return ISA_ERR_INVALID_ARG;
   }
   if (!idx || !count || !ws) return ISA_ERR_INVALID_ARG;
@@ -239,8 +243,8 @@ static isa_status sparse_mla(int32_t n_layers, const uint16_t* const* q, const u
   char* base = (char*)ws;
   MlaWs w{(uint32_t*)base, (float*)(base + HDR),
           (float*)(base + HDR + up256((size_t)n_layers * rows * p.splits * ATT_HEADS * LAT_DIM * 4))};
-  return launch_sparse_mla(a, p, n_layers, q, latent, s->block_table, row_seq, row_pos, idx, count, k, sm_scale,
-                           out, lse, w, (hipStream_t)stream);
+  return launch_sparse_mla(a, p, n_layers, q, latent, lat_scale, s->block_table, row_seq, row_pos, idx, count, k,
+                           sm_scale, out, lse, w, (hipStream_t)stream);
 }
 
 isa_status isa_sparse_mla_decode(const uint16_t* q, const uint16_t* latent, const isa_seqs* s,
@@ -248,8 +252,19 @@ isa_status isa_sparse_mla_decode(const uint16_t* q, const uint16_t* latent, cons
                                  const int32_t* count, int32_t k, float sm_scale, float* out, float* lse, void* ws,
                                  size_t ws_bytes, isa_stream_t stream) {
   if (!q || !latent || !out) return ISA_ERR_INVALID_ARG;
-  return sparse_mla(1, &q, &latent, s, row_seq, row_pos, rows, idx, count, k, sm_scale, &out, lse ? &lse : nullptr,
-                    ws, ws_bytes, stream);
+  const void* lat = latent;
+  return sparse_mla(1, &q, &lat, nullptr, s, row_seq, row_pos, rows, idx, count, k, sm_scale, &out,
+                    lse ? &lse : nullptr, ws, ws_bytes, stream);
+}
+
+isa_status isa_sparse_mla_decode_fp8(const uint16_t* q, const uint8_t* codes, const float* row_scales,
+                                     const isa_seqs* s, const int32_t* row_seq, const int32_t* row_pos, int32_t rows,
+                                     const int32_t* idx, const int32_t* count, int32_t k, float sm_scale, float* out,
+                                     float* lse, void* ws, size_t ws_bytes, isa_stream_t stream) {
+  if (!q || !codes || !row_scales || !out) return ISA_ERR_INVALID_ARG;
+  const void* lat = codes;
+  return sparse_mla(1, &q, &lat, &row_scales, s, row_seq, row_pos, rows, idx, count, k, sm_scale, &out,
+                    lse ? &lse : nullptr, ws, ws_bytes, stream);
 }
 
 isa_status isa_sparse_mla_decode_shared(int32_t n_layers, const uint16_t* const* q, const uint16_t* const* latent,
@@ -257,8 +272,11 @@ isa_status isa_sparse_mla_decode_shared(int32_t n_layers, const uint16_t* const*
                                         int32_t rows, const int32_t* idx, const int32_t* count, int32_t k,
                                         float sm_scale, float* const* out, float* const* lse, void* ws,
                                         size_t ws_bytes, isa_stream_t stream) {
-  return sparse_mla(n_layers, q, latent, s, row_seq, row_pos, rows, idx, count, k, sm_scale, out, lse, ws, ws_bytes,
-                    stream);
+  if (!latent || n_layers < 1 || n_layers > ISA_MAX_LAYERS) return ISA_ERR_INVALID_ARG;
+  const void* lat[ISA_MAX_LAYERS];
+  for (int l = 0; l < n_layers; ++l) lat[l] = latent[l];
+  return sparse_mla(n_layers, q, lat, nullptr, s, row_seq, row_pos, rows, idx, count, k, sm_scale, out, lse, ws,
+                    ws_bytes, stream);
 }
 
 isa_status isa_append_token(const uint16_t* key_new, const uint16_t* latent_new, const float* w4, const isa_seqs* s,
@@ -277,6 +295,23 @@ isa_status isa_append_token(const uint16_t* key_new, const uint16_t* latent_new,
   fill_batch(s, &a, MAX_K);
   return launch_append(a, key_new, latent_new, w4, s->block_table, scales, keys, latent, pooled, (uint32_t*)ws,
                        (hipStream_t)stream);
+}
+
+isa_status isa_latent_to_fp8(const uint16_t* latent, const isa_seqs* s, uint8_t* codes, float* row_scales, void* ws,
+                             size_t ws_bytes, isa_stream_t stream) {
+  if (!latent || !codes || !row_scales || !ws) return ISA_ERR_INVALID_ARG;
+  if (!aligned16(latent) || !aligned16(codes) || !aligned16(row_scales) || !aligned16(ws)) return ISA_ERR_INVALID_ARG;
+  if (!valid_seqs(s)) return ISA_ERR_INVALID_ARG;
+  if (ws_bytes < HDR) return ISA_ERR_WORKSPACE;
+  BatchArgs a;
+  fill_batch(s, &a, MAX_K);
+  int t = 0;
+  for (int b = 0; b < s->batch; ++b) {
+    a.tile_start[b] = t;
+    t += (s->seq_lens_host[b] + PAGE_TOK - 1) / PAGE_TOK;  // one workgroup per page
+  }
+  a.tile_start[s->batch] = t;
+  return launch_latent_fp8(a, latent, s->block_table, codes, row_scales, (uint32_t*)ws, (hipStream_t)stream);
 }
 
 isa_status isa_indexer_prefill_scores(const int8_t* q, const int8_t* head_w, const int32_t* q_pos, int32_t Q,

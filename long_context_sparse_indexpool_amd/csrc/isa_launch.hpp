@@ -50,11 +50,17 @@ struct MlaWs {
 MlaPlan plan_mla(int32_t rows, int32_t k, int32_t layers);
 // n_layers (1..ISA_MAX_LAYERS) attentions that share one selection; q, latent,
 // out are host arrays of n_layers device pointers, lse null or such an array.
+// lat_scale null: latent rows are bf16; otherwise the rows are FP8 E4M3 codes
+// and lat_scale an array of n_layers per-row scale pools.
 isa_status launch_sparse_mla(const BatchArgs& a, const MlaPlan& p, int32_t n_layers, const uint16_t* const* q,
-                             const uint16_t* const* latent, const int32_t* bt, const int32_t* row_seq,
+                             const void* const* latent, const float* const* lat_scale, const int32_t* bt,
+                             const int32_t* row_seq,
                              const int32_t* row_pos, const int32_t* idx, const int32_t* count, int32_t k,
                              float sm_scale, float* const* out, float* const* lse, const MlaWs& w,
                              hipStream_t stream);
+
+isa_status launch_latent_fp8(const BatchArgs& a, const uint16_t* latent, const int32_t* bt, uint8_t* codes,
+                             float* scales, uint32_t* err, hipStream_t stream);
 
 isa_status launch_prefill_scores(const BatchArgs& a, const int8_t* q, const int8_t* hw, const int32_t* q_pos,
                                  int32_t Q, const int8_t* pooled, const int32_t* bt, int32_t* scores,

@@ -36,6 +36,8 @@
 // With one split the workgroup normalises and writes the output; otherwise it
 // writes its unnormalised partial (O, reference, sum) and k_mla_combine merges
 // the splits by log-sum-exp weights.
+#include <type_traits>
+
 #include "isa_launch.hpp"
 
 namespace isa {
@@ -86,7 +88,8 @@ __device__ __forceinline__ int sp_slot(int lane) { return lane + 8 * (lane >> 4)
 
 struct MlaPtrs {
   const uint16_t* q[ISA_MAX_LAYERS];       // per layer sharing the selection
-  const uint16_t* latent[ISA_MAX_LAYERS];
+  const void* latent[ISA_MAX_LAYERS];      // bf16 rows, or FP8 E4M3 codes
+  const float* lat_scale[ISA_MAX_LAYERS];  // FP8: per-row scales
   float* out[ISA_MAX_LAYERS];
   float* lse[ISA_MAX_LAYERS];              // all null when not requested
   int32_t n_layers;
@@ -105,7 +108,28 @@ struct MlaPtrs {
   int32_t gps;  // groups per split
 };
 
+// FP8 E4M3 codes of 8 channels to fp16 (exact: every E4M3 value is an fp16
+// value), low byte first.
+__device__ __forceinline__ v8h fp8x8_to_f16x8(v2i w) {
+  typedef _Float16 v2h_ __attribute__((ext_vector_type(2)));
+  const v2h_ a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)w.x, 1.0f, false);
+  const v2h_ b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)w.x, 1.0f, true);
+  const v2h_ c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)w.y, 1.0f, false);
+  const v2h_ d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)w.y, 1.0f, true);
+  return v8h{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+// FP8 selects the cache format: bf16 rows (1 KiB per token), or E4M3 codes
+// (512 B per token) with one fp32 scale per row.  The FP8 path decodes the
+// codes to fp16 exactly and uses fp16 MFMA for both products, with the query
+// converted to fp16 once; a token's scale multiplies its scores and is folded
+// into its probability for the P.V product (the normalising sum stays unscaled).
+// MULTI: several layers share the selection (the layer is part of the grid);
+// a single-layer launch keeps every pointer a static kernel argument.
+template <bool FP8, bool MULTI>
 __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, const MlaPtrs P) {
+  using LoadT = typename std::conditional<FP8, v2i, v4i>::type;  // one lane's 8 channels of a row
+  using QOpT = typename std::conditional<FP8, v8h, v8bf>::type;
   __shared__ __attribute__((aligned(16))) _Float16 vt[2][TILE_TOK * V_STRIDE];  // 2 x 33 KiB: fp16 V of a tile, double-buffered
   __shared__ v4f sp[2][4][HBLK][SP_LANES];                // 48 KiB: partial S^T [half][group][head block][lane]
   __shared__ _Float16 pb[ATT_HEADS * P_STRIDE];           // 5 KiB: P of the tile [head][token]
@@ -117,11 +141,14 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cg = wave & 3, th = wave >> 2;   // channels 128cg.., tokens 16th.. of each tile
-  const int layer = blockIdx.x / (P.rows * P.splits);  // layers sharing the selection: one launch
-  const int r = (blockIdx.x / P.splits) % P.rows;
-  const int split = blockIdx.x % P.splits;
+  const int layer = MULTI ? (int)blockIdx.x / (P.rows * P.splits) : 0;  // layers sharing the selection
+  const int rs = MULTI ? (int)blockIdx.x % (P.rows * P.splits) : (int)blockIdx.x;
+  const int r = rs / P.splits;
+  const int split = rs % P.splits;
   const uint16_t* const q = P.q[layer];
-  const uint16_t* const latent = P.latent[layer];
+  const char* const latent = static_cast<const char*>(P.latent[layer]);
+  const float* const lscale = P.lat_scale[layer];
+  constexpr int ROW_BYTES = FP8 ? LAT_DIM : LAT_DIM * 2;
   const int lq = lane & 15, lg = lane >> 4;  // column / row-group of the 16x16 layouts
 
   // row description, read by every thread (no barrier); the split's group ids
@@ -138,6 +165,17 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
   for (int e = 0; e < MAX_GPS / MLA_THREADS + 1; ++e) {
     const int j = tid + e * MLA_THREADS;
     gid[e] = (j < P.gps && jbeg0 + j < P.k) ? P.idx[(size_t)r * P.k + jbeg0 + j] : -1;
+  }
+  // query operand (B = Q^T), fetched in the same round as the group ids:
+  // lane -> head 16hb + lq, channels 128cg + 32c + 8lg .. +7 (bf16 bits; the
+  // FP8 path converts it to fp16 once the token table is built)
+  v4i qraw[HBLK][KSTEPS];
+  {
+    const uint16_t* qp = q + ((size_t)r * ATT_HEADS + lq) * LAT_DIM + cg * CG_DIM + lg * 8;
+#pragma unroll
+    for (int hb = 0; hb < HBLK; ++hb)
+#pragma unroll
+      for (int c = 0; c < KSTEPS; ++c) qraw[hb][c] = *reinterpret_cast<const v4i*>(qp + (size_t)hb * 16 * LAT_DIM + c * 32);
   }
   // the row's block-table entries, fetched in the same round as the group ids
   // (one dependent global round trip less before the first latent load)
@@ -187,16 +225,18 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
 
   const int nslot = ng * GROUP;
   const int ntile = (nslot + TILE_TOK - 1) / TILE_TOK;
-  // query operand (B = Q^T): lane -> head 16hb + lq, channels 128cg + 32c + 8lg .. +7
-  v8bf qop[HBLK][KSTEPS];
-  {
-    const uint16_t* qp = q + ((size_t)r * ATT_HEADS + lq) * LAT_DIM + cg * CG_DIM + lg * 8;
+  QOpT qop[HBLK][KSTEPS];
 #pragma unroll
-    for (int hb = 0; hb < HBLK; ++hb)
+  for (int hb = 0; hb < HBLK; ++hb)
 #pragma unroll
-      for (int c = 0; c < KSTEPS; ++c)
-        qop[hb][c] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qp + (size_t)hb * 16 * LAT_DIM + c * 32));
-  }
+    for (int c = 0; c < KSTEPS; ++c) {
+      const v4i w = qraw[hb][c];
+      if constexpr (FP8)
+        qop[hb][c] = __builtin_bit_cast(v8h, v4i{(int)bf16x2_to_f16x2((uint32_t)w[0]), (int)bf16x2_to_f16x2((uint32_t)w[1]),
+                                                 (int)bf16x2_to_f16x2((uint32_t)w[2]), (int)bf16x2_to_f16x2((uint32_t)w[3])});
+      else
+        qop[hb][c] = __builtin_bit_cast(v8bf, w);
+    }
   v4f o[HBLK][NBLK];
 #pragma unroll
   for (int hb = 0; hb < HBLK; ++hb)
@@ -208,33 +248,49 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
   // Loads are unconditional (an invisible token reads row 0 of the pool and is
   // zeroed by its mask), so no branch separates a load from its use and the
   // compiler waits for exactly the loads it consumes.
-  auto row_of = [&](int t, int& mask) -> const v4i* {
+  auto row_of = [&](int t, int& mask) -> const LoadT* {
     const int slot = t * TILE_TOK + th * 16 + lq;
     const uint32_t tr = trow[min(slot, MAX_GPS * GROUP - 1)];  // always in range; masked below
     const bool vis = t < ntile && slot < nslot && tr != 0xFFFFFFFFu;
     mask = vis ? -1 : 0;
     const uint32_t row = vis ? tr : 0u;
-    return reinterpret_cast<const v4i*>(latent + (size_t)row * LAT_DIM + cg * CG_DIM + lg * 8);
+    return reinterpret_cast<const LoadT*>(latent + (size_t)row * ROW_BYTES + (cg * CG_DIM + lg * 8) * (ROW_BYTES / LAT_DIM));
+  };
+  // FP8: the row scales of the 4 tokens of this lane's softmax group in tile t
+  // (row 0's when the group is not visible; masked at use)
+  auto scales_of = [&](int t) -> const float4* {
+    const int sbase = t * TILE_TOK + 4 * own_tq;
+    const uint32_t tr = trow[min(sbase, MAX_GPS * GROUP - 4)];
+    const bool vis = t < ntile && sbase < nslot && tr != 0xFFFFFFFFu;
+    return reinterpret_cast<const float4*>(lscale + (vis ? tr : 0u));
   };
 
   // one tile: partial scores, V, softmax of the owned heads, P.V
-  auto tile_step = [&](int t, v4i (&buf)[KSTEPS], int& bmask) {
+  auto tile_step = [&](int t, LoadT (&buf)[KSTEPS], int& bmask, float4& sbuf) {
     const int vb = t & 1;
     _Float16* vtb = vt[vb];
     v4f acc[HBLK];
 #pragma unroll
     for (int hb = 0; hb < HBLK; ++hb) acc[hb] = v4f{0.f, 0.f, 0.f, 0.f};
     int nmask;
-    const v4i* nsrc = row_of(t + 2, nmask);
+    const LoadT* nsrc = row_of(t + 2, nmask);
 #pragma unroll
     for (int c = 0; c < KSTEPS; ++c) {
-      const v4i kv = buf[c] & bmask;
+      v4i vh;  // V in fp16, token-major: this lane's 8 channels of token 16th + lq
+      if constexpr (FP8) {
+        const v8h kh = fp8x8_to_f16x8(buf[c] & bmask);
 #pragma unroll
-      for (int hb = 0; hb < HBLK; ++hb)
-        acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kv), qop[hb][c], acc[hb], 0, 0, 0);
-      // V in fp16, token-major: this lane's 8 channels of token 16th + lq
-      const v4i vh = {(int)bf16x2_to_f16x2((uint32_t)kv[0]), (int)bf16x2_to_f16x2((uint32_t)kv[1]),
-                      (int)bf16x2_to_f16x2((uint32_t)kv[2]), (int)bf16x2_to_f16x2((uint32_t)kv[3])};
+        for (int hb = 0; hb < HBLK; ++hb)
+          acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, qop[hb][c], acc[hb], 0, 0, 0);
+        vh = __builtin_bit_cast(v4i, kh);
+      } else {
+        const v4i kv = buf[c] & bmask;
+#pragma unroll
+        for (int hb = 0; hb < HBLK; ++hb)
+          acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kv), qop[hb][c], acc[hb], 0, 0, 0);
+        vh = v4i{(int)bf16x2_to_f16x2((uint32_t)kv[0]), (int)bf16x2_to_f16x2((uint32_t)kv[1]),
+                 (int)bf16x2_to_f16x2((uint32_t)kv[2]), (int)bf16x2_to_f16x2((uint32_t)kv[3])};
+      }
       *reinterpret_cast<v4i*>(&vtb[vrow(th * 16 + lq) * V_STRIDE + cg * CG_DIM + c * 32 + lg * 8]) = vh;
       buf[c] = nsrc[c * 4];  // refill with tile t + 2
     }
@@ -253,12 +309,17 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
       const int sbase = t * TILE_TOK + 4 * tq;
       const uint4 tr = *reinterpret_cast<const uint4*>(&trow[min(sbase, MAX_GPS * GROUP - 4)]);
       const uint32_t trv[4] = {tr.x, tr.y, tr.z, tr.w};
-      float x[4];
+      float x[4], st[4];
       float mt = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool vis = sbase + i < nslot && trv[i] != 0xFFFFFFFFu;
-        x[i] = vis ? s[i] * P.c2 : -INFINITY;
+        if constexpr (FP8) {
+          st[i] = vis ? (&sbuf.x)[i] : 0.f;
+          x[i] = vis ? s[i] * st[i] * P.c2 : -INFINITY;
+        } else {
+          x[i] = vis ? s[i] * P.c2 : -INFINITY;
+        }
         mt = fmaxf(mt, x[i]);
       }
       const bool moved = __any(mt > m_ref + RESCALE_LOG2);
@@ -282,10 +343,14 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
       for (int i = 0; i < 4; ++i) {
         const float pr = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[i] - m_ref);
         ps += pr;
-        ph[i] = (_Float16)pr;
+        if constexpr (FP8)
+          ph[i] = (_Float16)(pr * st[i]);  // the row scale enters P.V through P
+        else
+          ph[i] = (_Float16)pr;
       }
       l_run += ps;
       *reinterpret_cast<v4h*>(&pb[own_h * P_STRIDE + 4 * tq]) = ph;
+      if constexpr (FP8) sbuf = *scales_of(t + 2);  // refill with tile t + 2, after the latent rows
     }
     lds_barrier();  // P, reference moves complete
 
@@ -328,25 +393,34 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
   // entry with the back edge, so any other order would make each K step wait
   // for every load in flight.  The loop is unrolled by two (a register buffer
   // per parity); an odd last tile is followed by an all-masked one.
-  v4i buf0[KSTEPS], buf1[KSTEPS];
+  LoadT buf0[KSTEPS], buf1[KSTEPS];
   int bm0, bm1;
+  float4 sc0 = make_float4(0.f, 0.f, 0.f, 0.f), sc1 = sc0;  // FP8 row scales per parity
   {
-    const v4i* s0 = row_of(0, bm0);
+    const LoadT* s0 = row_of(0, bm0);
 #pragma unroll
     for (int c = 0; c < KSTEPS; ++c) {
       buf0[c] = s0[c * 4];
       __builtin_amdgcn_sched_barrier(0);
     }
-    const v4i* s1 = row_of(1, bm1);
+    if constexpr (FP8) {
+      sc0 = *scales_of(0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const LoadT* s1 = row_of(1, bm1);
 #pragma unroll
     for (int c = 0; c < KSTEPS; ++c) {
       buf1[c] = s1[c * 4];
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (FP8) {
+      sc1 = *scales_of(1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   for (int t = 0; t < ntile; t += 2) {
-    tile_step(t, buf0, bm0);
-    tile_step(t + 1, buf1, bm1);
+    tile_step(t, buf0, bm0, sc0);
+    tile_step(t + 1, buf1, bm1, sc1);
   }
 
   // ---- finish: per-head sums of the owned heads, then every wave's channels ----
@@ -397,11 +471,13 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
 
 // Merge the splits of one (row, head): weights 2^(m_s - M), then a weighted
 // sum of the partial outputs (128 threads x 4 channels, loads unrolled).
+template <bool MULTI>
 __global__ __launch_bounds__(128) void k_mla_combine(const MlaPtrs P, int32_t rows) {
   __shared__ float wsh[MAX_SPLITS];
   __shared__ float stat[2];
-  const int layer = blockIdx.x / (rows * ATT_HEADS);
-  const int r = (blockIdx.x / ATT_HEADS) % rows, h = blockIdx.x % ATT_HEADS;
+  const int rl = blockIdx.x / ATT_HEADS, h = blockIdx.x % ATT_HEADS;
+  const int layer = MULTI ? rl / rows : 0;
+  const int r = MULTI ? rl % rows : rl;
   const int S = P.splits;
   const size_t part0 = ((size_t)layer * rows + r) * S;  // (layer, row, split 0)
   const float* ml = P.ml_part + (part0 * ATT_HEADS + h) * 2;
@@ -454,7 +530,8 @@ MlaPlan plan_mla(int32_t rows, int32_t k, int32_t layers) {
 }
 
 isa_status launch_sparse_mla(const BatchArgs& a, const MlaPlan& p, int32_t n_layers, const uint16_t* const* q,
-                             const uint16_t* const* latent, const int32_t* bt, const int32_t* row_seq,
+                             const void* const* latent, const float* const* lat_scale, const int32_t* bt,
+                             const int32_t* row_seq,
                              const int32_t* row_pos, const int32_t* idx, const int32_t* count, int32_t k,
                              float sm_scale, float* const* out, float* const* lse, const MlaWs& w,
                              hipStream_t stream) {
@@ -462,6 +539,7 @@ isa_status launch_sparse_mla(const BatchArgs& a, const MlaPlan& p, int32_t n_lay
   for (int l = 0; l < n_layers; ++l) {
     P.q[l] = q[l];
     P.latent[l] = latent[l];
+    P.lat_scale[l] = lat_scale ? lat_scale[l] : nullptr;
     P.out[l] = out[l];
     P.lse[l] = lse ? lse[l] : nullptr;
   }
@@ -479,12 +557,20 @@ isa_status launch_sparse_mla(const BatchArgs& a, const MlaPlan& p, int32_t n_lay
   P.c2 = sm_scale * LOG2E;
   P.splits = p.splits;
   P.gps = p.groups_per_split;
-  if (launch_timed(ISA_TIMER_MLA_SPLIT, k_mla_split, dim3(n_layers * p.rows * p.splits), dim3(MLA_THREADS), stream,
-                   a, P) !=
-      hipSuccess)
-    return ISA_ERR_HIP;
+  const dim3 grid(n_layers * p.rows * p.splits), block(MLA_THREADS);
+  hipError_t e;
+  if (lat_scale)
+    e = n_layers > 1 ? launch_timed(ISA_TIMER_MLA_SPLIT, k_mla_split<true, true>, grid, block, stream, a, P)
+                     : launch_timed(ISA_TIMER_MLA_SPLIT, k_mla_split<true, false>, grid, block, stream, a, P);
+  else
+    e = n_layers > 1 ? launch_timed(ISA_TIMER_MLA_SPLIT, k_mla_split<false, true>, grid, block, stream, a, P)
+                     : launch_timed(ISA_TIMER_MLA_SPLIT, k_mla_split<false, false>, grid, block, stream, a, P);
+  if (e != hipSuccess) return ISA_ERR_HIP;
   if (p.splits > 1) {
-    hipLaunchKernelGGL(k_mla_combine, dim3(n_layers * p.rows * ATT_HEADS), dim3(128), 0, stream, P, p.rows);
+    if (n_layers > 1)
+      hipLaunchKernelGGL(k_mla_combine<true>, dim3(n_layers * p.rows * ATT_HEADS), dim3(128), 0, stream, P, p.rows);
+    else
+      hipLaunchKernelGGL(k_mla_combine<false>, dim3(p.rows * ATT_HEADS), dim3(128), 0, stream, P, p.rows);
     if (hipGetLastError() != hipSuccess) return ISA_ERR_HIP;
   }
   return ISA_OK;

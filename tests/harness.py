@@ -169,6 +169,44 @@ def run_attention_shared(db: DeviceBatch, idx: torch.Tensor, cnt: torch.Tensor, 
     return [(o.cpu().numpy(), l.cpu().numpy()) for o, l in zip(outs, lses)]
 
 
+def latent_fp8(db: DeviceBatch):
+    """isa_latent_to_fp8 of the batch's latent pool -> (codes, row_scales) device pools."""
+    m = isa()
+    wl = db.wl
+    codes = torch.zeros((wl.num_pages, PAGE_TOKENS, LAT_DIM), dtype=torch.uint8, device="cuda")
+    scales = torch.full((wl.num_pages, PAGE_TOKENS), float("nan"), dtype=torch.float32, device="cuda")
+    ws = m.alloc_workspace(m.workspace_size(m.ISA_OP_LATENT_FP8, db.seqs))
+    m.isa_latent_to_fp8(db.latent, db.seqs, codes, scales, ws)
+    torch.cuda.synchronize()
+    err = m.isa_device_error(ws)
+    assert err == 0, f"device error word {err:#x}"
+    return codes, scales
+
+
+def logical_rows(db: DeviceBatch, pool: torch.Tensor, b: int, tokens: np.ndarray) -> np.ndarray:
+    """Rows of a token-paged device pool for the given tokens of sequence b (host)."""
+    bt = db.bt[b].long()
+    t = torch.from_numpy(np.asarray(tokens, np.int64)).cuda()
+    return pool[bt[t // PAGE_TOKENS], t % PAGE_TOKENS].cpu().numpy()
+
+
+def run_attention_fp8(db: DeviceBatch, codes, scales, idx: torch.Tensor, cnt: torch.Tensor, k: int, q=None,
+                      rows=None):
+    m = isa()
+    wl = db.wl
+    rows = wl.batch if rows is None else rows
+    qh = wl.q_attn(0, rows) if q is None else q
+    qd = torch.from_numpy(qh.view(np.int16)).cuda()
+    out = torch.full((rows, ATT_HEADS, LAT_DIM), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((rows, ATT_HEADS), float("nan"), dtype=torch.float32, device="cuda")
+    ws = m.alloc_workspace(m.workspace_size(m.ISA_OP_SPARSE_MLA, db.seqs, rows))
+    m.isa_sparse_mla_decode_fp8(qd, codes, scales, db.seqs, None, None, rows, idx, cnt, k, SM_SCALE, out, lse, ws)
+    torch.cuda.synchronize()
+    err = m.isa_device_error(ws)
+    assert err == 0, f"device error word {err:#x}"
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
 # ------------------------------------------------------------------ comparisons
 def check_pool(db: DeviceBatch, bs=None):
     """GPU pooled keys within 1 LSB of the oracle's, scale within 1e-6 relative."""

@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "isa.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(isa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(isa_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -210,6 +210,37 @@ def test_append_token_rejects(m, case):
     rc = m.lib.isa_append_token(key, lat_new, ctypes.cast(w, ctypes.c_void_p), s.c, P, P, lat, P, P, wsb, None)
     assert rc == (m.ISA_ERR_WORKSPACE if case == "ws_small" else m.ISA_ERR_INVALID_ARG)
     assert m.lib.isa_workspace_size(m.ISA_OP_APPEND_TOKEN, FakeSeqs(m, [5]).c, 0, 0) == 256
+
+
+@pytest.mark.parametrize("case", ["null_codes", "misaligned_scales", "ws_small"])
+def test_fp8_latent_rejects(m, case):
+    s = FakeSeqs(m, [8192] * 4)
+    codes, scl, wsb = P, P, 256
+    if case == "null_codes":
+        codes = None
+    elif case == "misaligned_scales":
+        scl = P + 4
+    elif case == "ws_small":
+        wsb = 100
+    rc = m.lib.isa_latent_to_fp8(P, s.c, codes, scl, P, wsb, None)
+    assert rc == (m.ISA_ERR_WORKSPACE if case == "ws_small" else m.ISA_ERR_INVALID_ARG)
+    assert m.lib.isa_workspace_size(m.ISA_OP_LATENT_FP8, s.c, 0, 0) == 256
+
+
+@pytest.mark.parametrize("case", ["null_scales", "misaligned_codes", "k0", "ws_small"])
+def test_sparse_mla_fp8_rejects(m, case):
+    s = FakeSeqs(m, [8192] * 8)
+    codes, scl, k, wsb = P, P, 512, 1 << 30
+    if case == "null_scales":
+        scl = None
+    elif case == "misaligned_codes":
+        codes = P + 8
+    elif case == "k0":
+        k = 0
+    elif case == "ws_small":
+        wsb = 1000
+    rc = m.lib.isa_sparse_mla_decode_fp8(P, codes, scl, s.c, None, None, 8, P, P, k, 0.044, P, None, P, wsb, None)
+    assert rc == (m.ISA_ERR_WORKSPACE if case == "ws_small" else m.ISA_ERR_INVALID_ARG)
 
 
 @pytest.mark.parametrize("case", ["batch2", "q0", "ld_small", "null_pos"])

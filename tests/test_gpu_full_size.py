@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from synth.configs import SM_SCALE, TOPK_GROUPS, workload
+from synth.configs import GROUP, SM_SCALE, TOPK_GROUPS, workload
 
 import harness as H
 
@@ -62,7 +62,43 @@ def _decode_full(i: int, share_layers: int = 0):
         H.attention_tolerance(out[b], ref_att[b][0], lse[b], ref_att[b][1])
     if share_layers:
         _index_share_full(db, idx, cnt, idx_d, cnt_d, ref_att, share_layers)
+        _fp8_full(db, idx, cnt, idx_d, cnt_d)
     H.log(f"{wl.name}: done")
+
+
+def _fp8_full(db, idx, cnt, idx_d, cnt_d):
+    """FP8 latent cache at full size: the whole pool quantised on the GPU, the
+    selected rows' codes and scales bit-exact against the oracle's quantiser, and
+    attention over the FP8 cache against the oracle's FP8 attention for every row
+    (the oracle runs on the selected rows only: every sequence length is a
+    multiple of 4, so each selected group is complete and visible)."""
+    wl = db.wl
+    B = wl.batch
+    H.log(f"{wl.name}: FP8 latent cache")
+    codes, scales = H.latent_fp8(db)
+    out, lse = H.run_attention_fp8(db, codes, scales, idx_d, cnt_d, TOPK_GROUPS, q=wl.q_attn(0, B))
+    lat, to = db.host["latent"], wl.token_offsets
+    qa = wl.q_attn(0, B)
+    toks, gc, gs = [], [], []
+    for b in range(B):
+        assert wl.lens[b] % GROUP == 0
+        n = int(cnt[b])
+        tok = (idx[b, :n].astype(np.int64)[:, None] * GROUP + np.arange(GROUP)).reshape(-1)
+        toks.append(tok)
+        gc.append(H.logical_rows(db, codes, b, tok))
+        gs.append(H.logical_rows(db, scales, b, tok))
+    del codes, scales
+
+    def one(b):
+        rc, rs = oracle.latent_fp8(lat[to[b] + toks[b]])
+        assert np.array_equal(gc[b], rc) and np.array_equal(gs[b], rs), f"codes of sequence {b}"
+        n = int(cnt[b])
+        return oracle.attention_fp8(qa[b], rc, rs, GROUP * n, GROUP * n - 1, np.arange(n, dtype=np.int32), n,
+                                    SM_SCALE)
+
+    ref = oracle.map_rows(one, range(B))
+    for b in range(B):
+        H.attention_tolerance(out[b], ref[b][0], lse[b], ref[b][1])
 
 
 def _index_share_full(db, idx, cnt, idx_d, cnt_d, ref0, n):

@@ -281,6 +281,37 @@ def test_append_tokens_match_repool():
         assert torch.equal(a_, f_), f"sequence {b}"
 
 
+def test_fp8_latent_cache():
+    """FP8 latent cache: every code and row scale of isa_latent_to_fp8 bit-exact
+    against the oracle's quantiser (a zero row and a large outlier included), and
+    attention over the FP8 cache against the oracle's attention over the same
+    codes within the attention tolerance."""
+    wl = custom("fp8", 19, [9000, 3000, 20003, 700, 131075], paged_random=True)
+    lat = wl.latent_logical()
+    to = wl.token_offsets
+    lat[to[1] + 5] = 0                                   # a zero row: scale 1, codes 0
+    lat[to[2] + 77, 300] = np.uint16(0xC2C0)             # -96: a large outlier sets the row scale
+    db = H.make_batch(wl, with_latent=False)
+    db.host["latent"] = lat
+    db.latent = H.pool_from_logical(wl, lat, 256, H.NAN_BF16)
+    H.run_pool(db)
+    codes, scales = H.latent_fp8(db)
+    ref_c, ref_s = oracle.latent_fp8(lat)
+    for b in range(wl.batch):
+        t = np.arange(wl.lens[b])
+        assert np.array_equal(H.logical_rows(db, codes, b, t), ref_c[to[b]: to[b + 1]]), f"codes of sequence {b}"
+        assert np.array_equal(H.logical_rows(db, scales, b, t), ref_s[to[b]: to[b + 1]]), f"scales of sequence {b}"
+    assert ref_s[to[1] + 5] == 1.0 and not ref_c[to[1] + 5].any()
+    idx, cnt, _, _ = H.run_topk(db, with_scores=False)
+    out, lse = H.run_attention_fp8(db, codes, scales, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), 512)
+    q = wl.q_attn(0, wl.batch)
+    for b in range(wl.batch):
+        L = wl.lens[b]
+        ref, ref_lse = oracle.attention_fp8(q[b], ref_c[to[b]: to[b + 1]], ref_s[to[b]: to[b + 1]], L, L - 1, idx[b],
+                                            int(cnt[b]), SM_SCALE)
+        H.attention_tolerance(out[b], ref, lse[b], ref_lse)
+
+
 def test_attention_rows_with_positions(ragged_batch):
     """Rows that map to sequences with an earlier last-visible position (prefill rows)."""
     db = ragged_batch
