@@ -65,6 +65,10 @@ def _load():
             lib.oracle_latent_fp8.restype = ctypes.c_int
             lib.oracle_attention_fp8.argtypes = [vp, vp, vp, i64, i64, vp, i32, ctypes.c_double, vp, vp]
             lib.oracle_attention_fp8.restype = ctypes.c_int
+            lib.oracle_kda_step.argtypes = [vp, vp, vp, vp, ctypes.c_float, vp, vp]
+            lib.oracle_kda_step.restype = ctypes.c_int
+            lib.oracle_bf16_round.argtypes = [ctypes.c_double]
+            lib.oracle_bf16_round.restype = ctypes.c_uint16
             _lib = lib
     return _lib
 
@@ -242,6 +246,28 @@ def attention_fp8(q: np.ndarray, codes: np.ndarray, scales: np.ndarray, L: int, 
     if rc != 0:
         raise ValueError(f"oracle_attention_fp8 rc={rc}")
     return out, lse
+
+
+# ------------------------------------------------------------------ linear-attention (KDA) layers
+KDA_DIM = 128
+
+
+def kda_step(q: np.ndarray, k: np.ndarray, v: np.ndarray, alpha: np.ndarray, beta: float, S: np.ndarray):
+    """One KDA decode step of one head: q, k, v bf16 bits [128]; alpha fp32 [128];
+    S bf16 bits [128,128] (row = key channel).  Returns (new S bits, o [128] f64)."""
+    q, k, v = _c(q, np.uint16), _c(k, np.uint16), _c(v, np.uint16)
+    alpha = _c(alpha, np.float32)
+    S = np.array(S, dtype=np.uint16, copy=True, order="C")
+    o = np.empty(KDA_DIM, np.float64)
+    rc = _load().oracle_kda_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), float(beta), _ptr(S), _ptr(o))
+    if rc != 0:
+        raise ValueError(f"oracle_kda_step rc={rc}")
+    return S, o
+
+
+def bf16_round(x: float) -> int:
+    """Nearest bf16 (ties to even) of a double, as bits."""
+    return int(_load().oracle_bf16_round(float(x)))
 
 
 def map_rows(fn, items, threads: int | None = None):

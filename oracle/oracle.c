@@ -261,3 +261,58 @@ int oracle_attention_fp8(const uint16_t* q, const uint8_t* codes, const float* s
   latent_rows c = {NULL, codes, scales};
   return attention_rows(q, &c, L, pos, sel, count, scale, out, lse);
 }
+
+
+/* ---- linear-attention layers: one KDA decode step ----
+ * [WIKI] linear attention section: the state matrix takes the delta update
+ * S_t = S_{t-1} - beta k (k^T S_{t-1}) + beta k v^T; [TREND] section on why the
+ * linear layers are the majority: KDA gates the decay channel by channel.
+ * Reading (the pages give no more): the decay alpha multiplies the key-channel
+ * rows of the state before the delta update, the output is o = S_t^T q, and
+ * the state is stored in bf16 ([WIKI] quantisation section: the shared state
+ * matrix stays BF16), rounded to nearest even after the step. */
+static uint16_t bf16_round(double x) {
+  /* nearest bf16 value of x (8 significant bits), ties to even, straight from
+   * the double (no intermediate fp32 rounding) */
+  if (x == 0.0) return signbit(x) ? 0x8000 : 0x0000;
+  int e;
+  frexp(x, &e);                       /* |x| = f 2^e, f in [0.5, 1) */
+  if (e < -125) e = -125;             /* bf16 subnormals: fixed spacing 2^-133 */
+  double m = nearbyint(ldexp(x, 8 - e)); /* 8 significant bits */
+  double r = ldexp(m, e - 8);
+  float f = (float)r;                 /* exact: r has at most 8 significant bits */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(u >> 16);
+}
+
+int oracle_kda_step(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* alpha, float beta,
+                    uint16_t* S, double* o) {
+  enum { D = OR_KDA_DIM };
+  double* Sp = (double*)malloc(sizeof(double) * D * D);
+  if (!Sp) return -2;
+  /* decay, channel by channel over the key dimension */
+  for (int i = 0; i < D; ++i)
+    for (int j = 0; j < D; ++j) Sp[i * D + j] = (double)alpha[i] * bf16_value(S[i * D + j]);
+  /* delta update: erase what the key retrieves (u = S'^T k), write the value */
+  for (int j = 0; j < D; ++j) {
+    double u = 0.0;
+    for (int i = 0; i < D; ++i) u += bf16_value(k[i]) * Sp[i * D + j];
+    for (int i = 0; i < D; ++i) Sp[i * D + j] += (double)beta * bf16_value(k[i]) * (bf16_value(v[j]) - u);
+  }
+  /* read-out and the stored state */
+  for (int j = 0; j < D; ++j) {
+    double acc = 0.0;
+    for (int i = 0; i < D; ++i) acc += bf16_value(q[i]) * Sp[i * D + j];
+    o[j] = acc;
+  }
+  int bad = 0;
+  for (int i = 0; i < D * D; ++i) {
+    if (!isfinite(Sp[i])) bad = 1;
+    S[i] = bf16_round(Sp[i]);
+  }
+  free(Sp);
+  return bad ? -1 : 0;
+}
+
+uint16_t oracle_bf16_round(double x) { return bf16_round(x); }

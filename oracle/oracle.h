@@ -36,6 +36,7 @@
 #define OR_GROUP 4
 #define OR_ATT_HEADS 64
 #define OR_LAT_DIM 512
+#define OR_KDA_DIM 128
 
 #ifdef __cplusplus
 extern "C" {
@@ -104,6 +105,20 @@ uint8_t oracle_fp8_encode(float x);
 int oracle_latent_fp8(const uint16_t* lat, int64_t n, uint8_t* codes, float* scales);
 int oracle_attention_fp8(const uint16_t* q, const uint8_t* codes, const float* scales, int64_t L, int64_t pos,
                          const int32_t* sel, int32_t count, double scale, double* out, double* lse);
+
+/* One decode step of one head of a linear-attention (KDA) layer ([WIKI] linear
+ * attention section: the delta update of the state matrix; [TREND] section on
+ * the linear layers: KDA's channel-wise decay).  Reading: with S [128][128]
+ * (row i = key channel, column j = value channel),
+ *   S' = diag(alpha) S;  u = S'^T k;  S'' = S' + beta k (v - u)^T;  o = S''^T q;
+ *   S := bf16(S'') rounded to nearest even.  With alpha = 1 this is the pages'
+ *   S - beta k (k^T S) + beta k v^T.
+ *   q, k, v  bf16 bits [128]; alpha fp32 [128]; beta fp32; S bf16 bits [128*128]
+ *   (in/out); o double [128].  Returns -1 if the new state is not finite. */
+int oracle_kda_step(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* alpha, float beta,
+                    uint16_t* S, double* o);
+/* Nearest bf16 of a double (ties to even), as bits. */
+uint16_t oracle_bf16_round(double x);
 
 #ifdef __cplusplus
 }

@@ -48,6 +48,14 @@ MUTANTS = {
                       [lambda rng: pins.test_fp8_encode_round_trip_and_nearest()]),
     "fp8_scale_int8_range": ("float s = amax > 0.f ? amax / 448.f : 1.f;", "float s = amax > 0.f ? amax / 127.f : 1.f;",
                              [pins.test_latent_fp8_rows]),
+    "kda_decay_dropped": ("Sp[i * D + j] = (double)alpha[i] * bf16_value(S[i * D + j]);",
+                          "Sp[i * D + j] = bf16_value(S[i * D + j]);", [pins.test_kda_decay_scales_key_rows]),
+    "kda_erase_sign": ("(bf16_value(v[j]) - u)", "(bf16_value(v[j]) + u)",
+                       [pins.test_kda_delta_rule_is_the_pages_equation]),
+    "kda_readout_transposed": ("acc += bf16_value(q[i]) * Sp[i * D + j];", "acc += bf16_value(q[i]) * Sp[j * D + i];",
+                               [pins.test_kda_no_erase_no_decay_keeps_state]),
+    "kda_readout_of_old_state": ("acc += bf16_value(q[i]) * Sp[i * D + j];", "acc += bf16_value(q[i]) * bf16_value(S[i * D + j]);",
+                                 [pins.test_kda_writes_the_value_at_a_unit_key]),
     "fp8_row_scale_ignored": ("return (double)c->scales[t] * oracle_fp8_decode", "return oracle_fp8_decode",
                               [pins.test_attention_fp8_equals_bf16_attention_on_exact_values]),
 }

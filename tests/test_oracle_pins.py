@@ -520,3 +520,63 @@ def test_attention_fp8_equals_bf16_attention_on_exact_values(rng):
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
     c = oracle.attention_fp8(q, codes, scales * np.float32(2.0), L, L - 1, sel, len(sel), SCALE)
     assert not np.allclose(c[0], a[0])  # the row scales enter the result
+
+
+# ---------------------------------------------------------------------- KDA decode step
+def _kda_inputs(rng, unit_k=True):
+    D = 128
+    q = synth.normal_bf16(41, 1, (D,))
+    k = synth.normal_bf16(41, 2, (D,))
+    if unit_k:
+        kf = f32(k)
+        k = bf16_bits((kf / np.linalg.norm(kf)).astype(np.float32).view(np.uint32).__and__(0xFFFF0000).view(np.float32))
+    v = synth.normal_bf16(41, 3, (D,))
+    S = synth.normal_bf16(41, 4, (D, D))
+    return q, k, v, S
+
+
+def _ulp_ok(got_bits, ref):
+    """got (bf16 bits) is the nearest bf16 of ref: within half a bf16 spacing."""
+    got = f32(got_bits)
+    e = np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126)))
+    return np.all(np.abs(got - ref) <= 2.0 ** (e - 8) + 1e-300)
+
+
+def test_kda_no_erase_no_decay_keeps_state(rng):
+    q, k, v, S = _kda_inputs(rng)
+    S2, o = oracle.kda_step(q, k, v, np.ones(128, np.float32), 0.0, S)
+    assert np.array_equal(S2, S)
+    assert np.allclose(o, f32(S).T @ f32(q), rtol=1e-12, atol=1e-12)  # o = S^T q
+
+
+def test_kda_delta_rule_is_the_pages_equation(rng):
+    q, k, v, S = _kda_inputs(rng)
+    for beta in (0.3, 1.0):
+        S2, o = oracle.kda_step(q, k, v, np.ones(128, np.float32), beta, S)
+        Sf, kf, vf = f32(S), f32(k), f32(v)
+        b = float(np.float32(beta))  # the gate is an fp32 argument
+        ref = Sf - b * np.outer(kf, kf @ Sf) + b * np.outer(kf, vf)
+        assert _ulp_ok(S2, ref)
+        assert np.allclose(o, ref.T @ f32(q), rtol=1e-10, atol=1e-10)
+
+
+def test_kda_writes_the_value_at_a_unit_key(rng):
+    q, k, v, S = _kda_inputs(rng)
+    # a key of exactly unit norm (four channels of +-1/2) and beta = 1: the
+    # delta rule replaces what the key retrieves by v, so reading the new state
+    # with q = k returns v
+    kb = np.zeros(128, np.float32)
+    kb[[3, 17, 64, 100]] = [0.5, -0.5, 0.5, -0.5]
+    k = bf16_bits(kb)
+    _, o = oracle.kda_step(k, k, v, np.ones(128, np.float32), 1.0, S)
+    assert np.allclose(o, f32(v), rtol=1e-12, atol=1e-12)
+
+
+def test_kda_decay_scales_key_rows(rng):
+    q, k, v, S = _kda_inputs(rng)
+    alpha = rng.uniform(0.0, 1.0, 128).astype(np.float32)
+    alpha[5] = 0.0
+    S2, o = oracle.kda_step(q, k, v, alpha, 0.0, S)
+    ref = alpha[:, None].astype(np.float64) * f32(S)
+    assert _ulp_ok(S2, ref) and not np.any(f32(S2)[5])
+    assert np.allclose(o, ref.T @ f32(q), rtol=1e-12, atol=1e-12)
