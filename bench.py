@@ -279,6 +279,38 @@ def bench_fp8(dec, steps=100, warmup=10):
     return res
 
 
+def bench_kda(batch=8, heads=32, reps=200):
+    """Linear-attention (KDA) decode step of one layer for `batch` sequences x
+    `heads` heads: 32 KiB of bf16 state read and written per head, plus the
+    per-token vectors.  Reported as us per step and algorithmic GB/s."""
+    import numpy as np
+    import torch
+
+    import long_context_sparse_indexpool_amd as m
+    from synth.configs import kda_inputs, kda_state
+    n = batch * heads
+    st = torch.from_numpy(kda_state(7, n).view(np.int16)).cuda()
+    q, k, v, alpha, beta = [torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).cuda()
+                            for x in kda_inputs(7, n, 0)]
+    out = torch.empty((n, 128), dtype=torch.float32, device="cuda")
+    ws = m.alloc_workspace(m.workspace_size(m.ISA_OP_KDA_STEP, None))
+    for _ in range(10):
+        m.isa_kda_decode_step(q, k, v, alpha, beta, st, out, ws)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(reps):
+        m.isa_kda_decode_step(q, k, v, alpha, beta, st, out, ws)
+    ev[1].record()
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) / reps * 1e3
+    nbytes = n * (2 * 128 * 128 * 2 + 3 * 128 * 2 + 128 * 4 + 4 + 128 * 4)
+    assert m.isa_device_error(ws) == 0
+    log(f"KDA decode step: {n} heads in {us:.2f} us, {nbytes / us / 1e3:.1f} GB/s")
+    return {"units": n, "batch": batch, "heads": heads, "us_per_step": round(us, 2),
+            "alg_bytes_per_step": nbytes, "alg_GBps": round(nbytes / us / 1e3, 1)}
+
+
 def bench_append(batch=8, length=1 << 20, reps=200):
     """Decode-time cache maintenance: isa_append_token for a batch of
     `batch` sequences at `length` tokens (one new key and latent row each, the
@@ -575,6 +607,7 @@ def main():
         secondary["index_share"] = bench_index_share(dec)
         secondary["append_token"] = bench_append()
         secondary["fp8_latent"] = bench_fp8(dec)
+        secondary["kda_decode"] = bench_kda()
     dec.free()
     if not args.primary_only:
         for i in (1, 4):

@@ -96,7 +96,8 @@ enum {
   ISA_OP_SPARSE_MLA = 3,
   ISA_OP_PREFILL_SCORES = 4,
   ISA_OP_APPEND_TOKEN = 5,
-  ISA_OP_LATENT_FP8 = 6
+  ISA_OP_LATENT_FP8 = 6,
+  ISA_OP_KDA_STEP = 7
 };
 
 /* Workspace bytes (a multiple of 256) that `op` needs for these sequences.
@@ -297,6 +298,25 @@ isa_status isa_sparse_mla_decode_fp8(const uint16_t* q, const uint8_t* codes, co
                                      const isa_seqs* s, const int32_t* row_seq, const int32_t* row_pos, int32_t rows,
                                      const int32_t* idx, const int32_t* count, int32_t k, float sm_scale, float* out,
                                      float* lse, void* ws, size_t ws_bytes, isa_stream_t stream);
+
+/*
+ * (8) One decode step of a linear-attention (KDA) layer for n (sequence, head)
+ * units ([WIKI] linear attention section: the state matrix's delta update
+ * S_t = S_{t-1} - beta k (k^T S_{t-1}) + beta k v^T, and quantisation section:
+ * the state stays BF16; [TREND] section on the linear layers: KDA's decay gate
+ * is channel-wise).  Contract (the pages give no more): per unit, with the
+ * state S [128][128] (row = key channel, column = value channel)
+ *   S' = diag(alpha) S;  u = S'^T k;  S'' = S' + beta k (v - u)^T;  out = S''^T q
+ * and S is replaced by S'' rounded to bf16 (nearest even).
+ *   q, k, v [dev] bf16 bits [n, 128]; alpha [dev] fp32 [n, 128] decay per key
+ *   channel; beta [dev] fp32 [n]; state [dev] bf16 bits [n, 128, 128], updated in
+ *   place; out [dev] fp32 [n, 128].  No normalisation of k is applied.
+ * Arithmetic in fp32.  Workspace: isa_workspace_size(ISA_OP_KDA_STEP, ...)
+ * bytes.  A non-finite new state sets ISA_DERR_NONFINITE.
+ */
+isa_status isa_kda_decode_step(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* alpha,
+                               const float* beta, uint16_t* state, float* out, int32_t n, void* ws, size_t ws_bytes,
+                               isa_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -26,7 +26,7 @@ MAX_BATCH, MAX_SEQ_LEN, MAX_K = 256, 1 << 22, 512
 
 ISA_OK, ISA_ERR_INVALID_ARG, ISA_ERR_UNSUPPORTED, ISA_ERR_WORKSPACE, ISA_ERR_HIP = range(5)
 ISA_OP_INDEXPOOL, ISA_OP_INDEXER_TOPK, ISA_OP_SPARSE_MLA, ISA_OP_PREFILL_SCORES, ISA_OP_APPEND_TOKEN = 1, 2, 3, 4, 5
-ISA_OP_LATENT_FP8 = 6
+ISA_OP_LATENT_FP8, ISA_OP_KDA_STEP = 6, 7
 ISA_SCALE_DYNAMIC, ISA_SCALE_GIVEN = 0, 1
 ISA_MAX_LAYERS = 8  # layers sharing one selection (isa_sparse_mla_decode_shared)
 DERR_PAGE_OOB, DERR_HEADW_RANGE, DERR_SCORE_OVERFLOW, DERR_ROW_RANGE, DERR_NONFINITE = 1, 2, 4, 8, 16
@@ -36,7 +36,7 @@ ISA_TIMER_INDEXER_SCORE, ISA_TIMER_MLA_SPLIT = 1, 2
 EXPORTS = ("isa_workspace_size", "isa_workspace_init", "isa_device_error", "isa_status_string", "isa_version",
            "isa_set_kernel_timer", "isa_indexpool", "isa_indexer_topk", "isa_sparse_mla_decode",
            "isa_sparse_mla_decode_shared", "isa_indexer_prefill_scores", "isa_append_token", "isa_latent_to_fp8",
-           "isa_sparse_mla_decode_fp8")
+           "isa_sparse_mla_decode_fp8", "isa_kda_decode_step")
 
 
 class IsaError(RuntimeError):
@@ -73,11 +73,12 @@ def _load() -> ctypes.CDLL:
     lib.isa_indexer_prefill_scores.argtypes = [vp, vp, vp, i32, vp, sp, vp, i32, vp, sz, vp]
     lib.isa_append_token.argtypes = [vp, vp, vp, sp, vp, vp, vp, vp, vp, sz, vp]
     lib.isa_latent_to_fp8.argtypes = [vp, sp, vp, vp, vp, sz, vp]
+    lib.isa_kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.isa_sparse_mla_decode_fp8.argtypes = [vp, vp, vp, sp, vp, vp, i32, vp, vp, i32, ctypes.c_float, vp, vp, vp,
                                               sz, vp]
     for f in ("isa_workspace_init", "isa_device_error", "isa_set_kernel_timer", "isa_indexpool", "isa_indexer_topk",
               "isa_sparse_mla_decode", "isa_sparse_mla_decode_shared", "isa_indexer_prefill_scores",
-              "isa_append_token", "isa_latent_to_fp8", "isa_sparse_mla_decode_fp8"):
+              "isa_append_token", "isa_latent_to_fp8", "isa_sparse_mla_decode_fp8", "isa_kda_decode_step"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -212,6 +213,18 @@ def isa_sparse_mla_decode_fp8(q: torch.Tensor, codes: torch.Tensor, row_scales: 
         _ptr(idx, torch.int32, "idx"), _ptr(count, torch.int32, "count"), k, float(sm_scale),
         _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"), _ptr(ws, torch.uint8, "ws"), ws.numel(),
         _stream(stream)))
+
+
+def isa_kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
+                        state: torch.Tensor, out: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
+    """One KDA decode step for n units: q, k, v bf16 bits [n,128]; alpha fp32 [n,128];
+    beta fp32 [n]; state bf16 bits [n,128,128] (in place); out fp32 [n,128]."""
+    v16 = lambda t: t if t.dtype == torch.int16 else t.view(torch.int16)
+    n = int(beta.numel())
+    _check("isa_kda_decode_step", lib.isa_kda_decode_step(
+        _ptr(v16(q), torch.int16, "q"), _ptr(v16(k), torch.int16, "k"), _ptr(v16(v), torch.int16, "v"),
+        _ptr(alpha, torch.float32, "alpha"), _ptr(beta, torch.float32, "beta"), _ptr(v16(state), torch.int16, "state"),
+        _ptr(out, torch.float32, "out"), n, _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
 
 
 def isa_indexer_topk(q: Optional[torch.Tensor], head_w: Optional[torch.Tensor], pooled: Optional[torch.Tensor],

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libisa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["api.hip", "pool.hip", "indexer_decode.hip", "topk_rows.hip", "mla_decode.hip", "score_prefill.hip",
-           "latent_fp8.hip"]
+           "latent_fp8.hip", "kda.hip"]
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
          # packed fp32 instructions are kept out of every kernel
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -139,6 +139,7 @@ size_t isa_workspace_size(int op, const isa_seqs* s, int32_t rows, int32_t cols)
     case ISA_OP_PREFILL_SCORES:
     case ISA_OP_APPEND_TOKEN:
     case ISA_OP_LATENT_FP8:
+    case ISA_OP_KDA_STEP:
       return HDR;
   }
   return 0;
@@ -312,6 +313,18 @@ isa_status isa_latent_to_fp8(const uint16_t* latent, const isa_seqs* s, uint8_t*
   }
   a.tile_start[s->batch] = t;
   return launch_latent_fp8(a, latent, s->block_table, codes, row_scales, (uint32_t*)ws, (hipStream_t)stream);
+}
+
+isa_status isa_kda_decode_step(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* alpha,
+                               const float* beta, uint16_t* state, float* out, int32_t n, void* ws, size_t ws_bytes,
+                               isa_stream_t stream) {
+  if (!q || !k || !v || !alpha || !beta || !state || !out || !ws) return ISA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(alpha) || !aligned16(beta) ||
+      !aligned16(state) || !aligned16(out) || !aligned16(ws))
+    return ISA_ERR_INVALID_ARG;
+  if (n < 1) return ISA_ERR_INVALID_ARG;
+  if (ws_bytes < HDR) return ISA_ERR_WORKSPACE;
+  return launch_kda_step(q, k, v, alpha, beta, state, out, n, (uint32_t*)ws, (hipStream_t)stream);
 }
 
 isa_status isa_indexer_prefill_scores(const int8_t* q, const int8_t* head_w, const int32_t* q_pos, int32_t Q,

@@ -62,6 +62,10 @@ isa_status launch_sparse_mla(const BatchArgs& a, const MlaPlan& p, int32_t n_lay
 isa_status launch_latent_fp8(const BatchArgs& a, const uint16_t* latent, const int32_t* bt, uint8_t* codes,
                              float* scales, uint32_t* err, hipStream_t stream);
 
+isa_status launch_kda_step(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* alpha,
+                           const float* beta, uint16_t* state, float* out, int32_t n, uint32_t* err,
+                           hipStream_t stream);
+
 isa_status launch_prefill_scores(const BatchArgs& a, const int8_t* q, const int8_t* hw, const int32_t* q_pos,
                                  int32_t Q, const int8_t* pooled, const int32_t* bt, int32_t* scores,
                                  int32_t ld, uint32_t* err, hipStream_t stream);

@@ -26,6 +26,15 @@ Input recipe (tensor ids of the generator in parentheses):
   lengths (7)           uniform double u_b (workload 4 only)
   page permutation (8)  Fisher-Yates with j = draw_i mod (i + 1) (workload 4 only)
 
+Linear-attention (KDA) decode steps, n (sequence, head) units, step s (each
+tensor drawn at element offset s * its size per step):
+  query (32)            N(0,1) -> bf16, [n, 128]
+  key (33)              N(0,1) in double, scaled to unit length per unit, -> bf16 (nearest even)
+  value (34)            N(0,1) -> bf16, [n, 128]
+  decay (35)            0.9 + 0.1 u, fp32 [n, 128]
+  gate (36)             u, fp32 [n]
+  initial state (37)    N(0,1) -> bf16, [n, 128, 128] (step 0 only)
+
 Layers that share one selection (IndexShare): layer 0 uses the tensors above;
 layer l >= 1 has its own attention query (tensor id 16 + l, same layout) and a
 latent cache equal to layer 0's with the sign bit flipped on the channels whose
@@ -54,6 +63,35 @@ SM_SCALE = 1.0 / math.sqrt(LAT_DIM)
 
 T_KEYS, T_POOLW, T_QIDX, T_HEADW, T_LATENT, T_QATT, T_LENS, T_PERM = 1, 2, 3, 4, 5, 6, 7, 8
 T_QATT_LAYER = 16  # attention query of layer l >= 1: tensor id 16 + l
+
+
+T_KDA_Q, T_KDA_K, T_KDA_V, T_KDA_ALPHA, T_KDA_BETA, T_KDA_STATE = 32, 33, 34, 35, 36, 37
+KDA_DIM = 128
+
+
+def _to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Nearest bf16 (ties to even) of float32 values, as bits (input plumbing)."""
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def kda_inputs(seed: int, n: int, step: int):
+    """Per-step inputs of n KDA units: (q, k, v) bf16 bits [n,128], alpha fp32
+    [n,128], beta fp32 [n]."""
+    D = KDA_DIM
+    off = step * n * D
+    q = normal_bf16(seed, T_KDA_Q, (n, D), start=off)
+    kd = normal_f64(seed, T_KDA_K, (n, D), start=off)
+    k = _to_bf16_bits((kd / np.linalg.norm(kd, axis=1, keepdims=True)).astype(np.float32))
+    v = normal_bf16(seed, T_KDA_V, (n, D), start=off)
+    alpha = (0.9 + 0.1 * uniform_f64(seed, T_KDA_ALPHA, (n, D), start=off)).astype(np.float32)
+    beta = uniform_f64(seed, T_KDA_BETA, (n,), start=step * n).astype(np.float32)
+    return q, k, v, alpha, beta
+
+
+def kda_state(seed: int, n: int) -> np.ndarray:
+    """Initial bf16 state bits [n, 128, 128]."""
+    return normal_bf16(seed, T_KDA_STATE, (n, KDA_DIM, KDA_DIM))
 
 
 def layer_flip_view(bits, layer: int):

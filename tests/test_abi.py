@@ -243,6 +243,22 @@ def test_sparse_mla_fp8_rejects(m, case):
     assert rc == (m.ISA_ERR_WORKSPACE if case == "ws_small" else m.ISA_ERR_INVALID_ARG)
 
 
+@pytest.mark.parametrize("case", ["null_state", "misaligned_alpha", "n0", "ws_small"])
+def test_kda_step_rejects(m, case):
+    st, al, n, wsb = P, P, 256, 256
+    if case == "null_state":
+        st = None
+    elif case == "misaligned_alpha":
+        al = P + 4
+    elif case == "n0":
+        n = 0
+    elif case == "ws_small":
+        wsb = 64
+    rc = m.lib.isa_kda_decode_step(P, P, P, al, P, st, P, n, P, wsb, None)
+    assert rc == (m.ISA_ERR_WORKSPACE if case == "ws_small" else m.ISA_ERR_INVALID_ARG)
+    assert m.lib.isa_workspace_size(m.ISA_OP_KDA_STEP, None, 0, 0) == 256
+
+
 @pytest.mark.parametrize("case", ["batch2", "q0", "ld_small", "null_pos"])
 def test_prefill_scores_rejects(m, case):
     s = FakeSeqs(m, [1 << 20] if case != "batch2" else [1000, 1000])

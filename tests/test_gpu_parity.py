@@ -312,6 +312,59 @@ def test_fp8_latent_cache():
         H.attention_tolerance(out[b], ref, lse[b], ref_lse)
 
 
+def test_kda_decode_steps():
+    """Linear-attention (KDA) layer: six decode steps of 96 (sequence, head)
+    units on the GPU, the oracle stepping the same inputs from the same initial
+    state.  Bars, from the arithmetic: the kernel computes in fp32, so after one
+    step a state element may differ from the oracle's nearest bf16 by one bf16
+    step plus the fp32 error of u = S'^T k; later steps start from states that
+    differ by that much, and the bound carries the difference through the decay
+    and the update exactly (see below).  Outputs: rel-L2 1e-4, and per element
+    1e-3 plus what the entering state difference can move the read-out."""
+    from synth.configs import kda_inputs, kda_state
+    m = H.isa()
+    n, steps, seed = 96, 6, 29
+    st_host = kda_state(seed, n)
+    st_ref = st_host.copy()
+    st = torch.from_numpy(st_host.view(np.int16)).cuda()
+    out = torch.empty((n, 128), dtype=torch.float32, device="cuda")
+    ws = m.alloc_workspace(m.workspace_size(m.ISA_OP_KDA_STEP, None))
+    exact = 0
+    prev_bound = np.zeros((n, 128, 128))  # both sides start from the same state
+    for step in range(steps):
+        q, k, v, alpha, beta = kda_inputs(seed, n, step)
+        dev = [torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).cuda() for x in (q, k, v, alpha, beta)]
+        m.isa_kda_decode_step(*dev, st, out, ws)
+        torch.cuda.synchronize()
+        refs = oracle.map_rows(lambda u: oracle.kda_step(q[u], k[u], v[u], alpha[u], float(beta[u]), st_ref[u]),
+                               range(n))
+        st_ref = np.stack([r[0] for r in refs])
+        o_ref = np.stack([r[1] for r in refs])
+        got_bits = st.cpu().numpy().view(np.uint16)
+        got, ref = synth.bf16_to_f32(got_bits).astype(np.float64), synth.bf16_to_f32(st_ref).astype(np.float64)
+        # a state difference B entering the step moves S'' by at most
+        # alpha_i B_ij + beta |k_i| sum_l |k_l| alpha_l B_lj (through u); this
+        # step's own rounding adds one bf16 step (at most 2^-7 of the value: an
+        # fp32 result can land on a bf16 midpoint the exact value misses) and the
+        # fp32 error of u (~1e-6 for |S| ~ 1; 1e-5 allowed)
+        kf = np.abs(synth.bf16_to_f32(k).astype(np.float64))
+        prop = alpha.astype(np.float64)[:, :, None] * prev_bound
+        prop = prop + beta.astype(np.float64)[:, None, None] * kf[:, :, None] * np.einsum("ul,ulj->uj", kf, prop)[:, None, :]
+        bound = prop + 2.0 ** -7 * np.abs(ref) + 1e-5
+        assert np.all(np.abs(got - ref) <= bound), f"step {step}: state off by {np.max(np.abs(got - ref) - bound):.2e}"
+        if step == 0:
+            exact = np.mean(got_bits == st_ref)
+        qf = np.abs(synth.bf16_to_f32(q).astype(np.float64))
+        o_bound = np.einsum("ui,uij->uj", qf, prop) + 1e-3  # the read-out of the unrounded S''
+        prev_bound = bound
+        o = out.cpu().numpy().astype(np.float64)
+        rel = np.linalg.norm(o - o_ref) / np.linalg.norm(o_ref)
+        assert rel <= 1e-4, f"step {step}: out rel-L2 {rel:.2e}"
+        assert np.all(np.abs(o - o_ref) <= o_bound), f"step {step}: out off by {np.max(np.abs(o - o_ref) - o_bound):.2e}"
+    assert exact > 0.999, f"only {exact:.5f} of the first step's state elements equal the oracle's bf16"
+    assert m.isa_device_error(ws) == 0
+
+
 def test_attention_rows_with_positions(ragged_batch):
     """Rows that map to sequences with an earlier last-visible position (prefill rows)."""
     db = ragged_batch
