@@ -192,40 +192,60 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
   }
 
   // ---- local candidates: every score in a bin >= the bin of this tile's k-th best ----
+  // Thread t owns bins NBINS-2t-1 (higher) and NBINS-2t-2, so ascending threads
+  // walk the bins in descending order.  One packed prefix sum over the threads
+  // gives, for every bin, the candidates and the nonzero bins above it; the
+  // kept bins (>= the boundary) are a prefix of that order, so these are also
+  // their emission offsets and (bin, count) pair positions.
   constexpr int PER = TILE_G / DEC_THREADS;
-  int bt_local;
-  uint32_t n_gt_local, n_valid;
-  find_boundary(hist, K, &bt_local, &n_gt_local, &n_valid, scr);
-  const int blo = bt_local < 0 ? 0 : bt_local;  // all valid candidates when at most k
-  uint32_t* pairs = P.tile_pairs + (size_t)tile * PAIR_CAP;
-  {
-    // bins >= blo, descending: emission cursors and (bin, count) pairs
-    constexpr int per = NBINS / DEC_THREADS;
-    const int hi = NBINS - tid * per;
-    uint32_t local = 0, nz = 0;
-    for (int j = 0; j < per; ++j) {
-      int bin = hi - 1 - j;
-      if (bin >= blo) {
-        local += hist[bin];
-        nz += hist[bin] != 0;
-      }
-    }
-    uint32_t tot, npairs;
-    uint32_t run = block_exclusive_scan(local, scr, &tot);
-    uint32_t po = block_exclusive_scan(nz, scr, &npairs);
-    for (int j = 0; j < per; ++j) {
-      int bin = hi - 1 - j;
-      if (bin < blo) break;
-      uint32_t c = hist[bin];
-      if (c) {
-        pairs[po++] = ((uint32_t)bin << 16) | c;
-        atomicAdd(&P.seq_hist[(size_t)b * NBINS + bin], c);  // the sequence's candidate histogram
-      }
-      hist[bin] = run;
-      run += c;
-    }
-    if (tid == 0) P.tile_meta[tile] = make_uint2(tot, npairs);
+  static_assert(NBINS == 2 * DEC_THREADS, "two bins per thread");
+  static_assert(TILE_G < 65536 && NBINS < 65536, "counts and nonzero bins share one word");
+  const int hb = NBINS - 2 * tid;
+  const uint32_t c_hi = hist[hb - 1], c_lo = hist[hb - 2];
+  const uint32_t local = c_hi + c_lo, nzl = (c_hi != 0u) + (c_lo != 0u);
+  const uint32_t packed = local | (nzl << 16);
+  const uint32_t xin = wave_inclusive_scan(packed);
+  if (lane == 63) scr[wave] = xin;
+  __syncthreads();
+  uint32_t above = xin - packed, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t t_ = scr[w];
+    all += t_;
+    if (w < wave) above += t_;
   }
+  const uint32_t run_hi = above & 0xFFFFu, pz_hi = above >> 16;
+  const uint32_t total = all & 0xFFFFu;
+  if (tid == 0 && total < K) {  // at most k valid scores: keep them all
+    scr[SCR_RES] = 0;
+    scr[SCR_RES + 1] = total;
+    scr[SCR_RES + 2] = all >> 16;
+  }
+  if (total >= K && run_hi < K && run_hi + local >= K) {  // the boundary bin is one of this thread's
+    const bool in_hi = run_hi + c_hi >= K;
+    scr[SCR_RES] = (uint32_t)(in_hi ? hb - 1 : hb - 2);
+    scr[SCR_RES + 1] = in_hi ? run_hi + c_hi : run_hi + local;
+    scr[SCR_RES + 2] = in_hi ? pz_hi + 1u : pz_hi + nzl;
+  }
+  __syncthreads();
+  const int blo = (int)scr[SCR_RES];
+  uint32_t* pairs = P.tile_pairs + (size_t)tile * PAIR_CAP;
+  // kept bins, descending: (bin, count) pairs, the sequence histogram, emission cursors
+  if (hb - 1 >= blo) {
+    if (c_hi) {
+      pairs[pz_hi] = ((uint32_t)(hb - 1) << 16) | c_hi;
+      atomicAdd(&P.seq_hist[(size_t)b * NBINS + hb - 1], c_hi);
+    }
+    hist[hb - 1] = run_hi;
+  }
+  if (hb - 2 >= blo) {
+    if (c_lo) {
+      pairs[pz_hi + (c_hi != 0u)] = ((uint32_t)(hb - 2) << 16) | c_lo;
+      atomicAdd(&P.seq_hist[(size_t)b * NBINS + hb - 2], c_lo);
+    }
+    hist[hb - 2] = run_hi + c_hi;
+  }
+  if (tid == 0) P.tile_meta[tile] = make_uint2(scr[SCR_RES + 1], scr[SCR_RES + 2]);
   __syncthreads();
   uint64_t* list = P.tile_list + (size_t)tile * TILE_G;
 #pragma unroll
