@@ -68,7 +68,7 @@ size_t pool_ws(const isa_seqs* s) {
 size_t mla_ws(int32_t rows, int32_t k, int32_t layers) {
   MlaPlan p = plan_mla(rows, k, layers);
   if (p.splits <= 1) return HDR;
-  return HDR + up256((size_t)layers * rows * p.splits * ATT_HEADS * LAT_DIM * 4) +
+  return HDR + up256((size_t)layers * rows * p.splits * ATT_HEADS * LAT_DIM * 2) +
          up256((size_t)layers * rows * p.splits * ATT_HEADS * 2 * 4);
 }
 
@@ -242,8 +242,8 @@ static isa_status sparse_mla(int32_t n_layers, const uint16_t* const* q, const v
   BatchArgs a;
   fill_batch(s, &a, k);
   char* base = (char*)ws;
-  MlaWs w{(uint32_t*)base, (float*)(base + HDR),
-          (float*)(base + HDR + up256((size_t)n_layers * rows * p.splits * ATT_HEADS * LAT_DIM * 4))};
+  MlaWs w{(uint32_t*)base, (_Float16*)(base + HDR),
+          (float*)(base + HDR + up256((size_t)n_layers * rows * p.splits * ATT_HEADS * LAT_DIM * 2))};
   return launch_sparse_mla(a, p, n_layers, q, latent, lat_scale, s->block_table, row_seq, row_pos, idx, count, k,
                            sm_scale, out, lse, w, (hipStream_t)stream);
 }

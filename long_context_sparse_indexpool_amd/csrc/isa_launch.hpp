@@ -44,7 +44,7 @@ struct MlaPlan {
 };
 struct MlaWs {
   uint32_t* err;
-  float* o_part;    // [layers][rows][splits][64][512]
+  _Float16* o_part;  // [layers][rows][splits][64][512] fp16 O / l
   float* ml_part;   // [layers][rows][splits][64][2]  (running max in log2 units, sum)
 };
 MlaPlan plan_mla(int32_t rows, int32_t k, int32_t layers);

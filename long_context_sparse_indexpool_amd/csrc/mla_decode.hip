@@ -99,8 +99,8 @@ struct MlaPtrs {
   const int32_t* row_pos;
   const int32_t* idx;
   const int32_t* count;
-  float* o_part;   // [layers][rows][splits][64][512]
-  float* ml_part;  // [layers][rows][splits][64][2]
+  _Float16* o_part;  // [layers][rows][splits][64][512] normalised partials O / l
+  float* ml_part;    // [layers][rows][splits][64][2]
   uint32_t* err;
   int32_t k;
   float c2;  // sm_scale * log2(e)
@@ -452,15 +452,31 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
     if (P.lse[layer] && own_tq == 0)
       P.lse[layer][(size_t)r * ATT_HEADS + own_h] = l_tot > 0.f ? m_ref * LN2 + logf(l_tot) : -INFINITY;
   } else {
+    // the split's normalised output O / l in fp16 (a convex combination of
+    // latent rows, so within their range), staged in LDS -- the V tiles are
+    // free now -- and written with 16-B stores
     const size_t part = blockIdx.x;  // (layer, row, split)
-    float* op = P.o_part + part * ATT_HEADS * LAT_DIM;
+    _Float16* stage = &vt[0][0];
+    static_assert(2 * TILE_TOK * V_STRIDE >= ATT_HEADS * LAT_DIM, "staging fits in the V tiles");
 #pragma unroll
-    for (int hb = 0; hb < HBLK; ++hb)
+    for (int hb = 0; hb < HBLK; ++hb) {
+      float inv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float li = fin_s[1][hb * 16 + 4 * lg + i];
+        inv[i] = li > 0.f ? 1.f / li : 0.f;
+      }
 #pragma unroll
       for (int nb = 0; nb < NBLK; ++nb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          op[(size_t)(hb * 16 + 4 * lg + i) * LAT_DIM + d_base + nb * 16 + lq] = o[hb][nb][i];
+          stage[(hb * 16 + 4 * lg + i) * LAT_DIM + d_base + nb * 16 + lq] = (_Float16)(o[hb][nb][i] * inv[i]);
+    }
+    __syncthreads();
+    v4i* op = reinterpret_cast<v4i*>(P.o_part + part * ATT_HEADS * LAT_DIM);
+    constexpr int N16 = ATT_HEADS * LAT_DIM * 2 / 16;
+#pragma unroll
+    for (int k = 0; k < N16 / MLA_THREADS; ++k) op[tid + k * MLA_THREADS] = reinterpret_cast<const v4i*>(stage)[tid + k * MLA_THREADS];
     if (own_tq == 0) {
       float* mp = P.ml_part + (part * ATT_HEADS + own_h) * 2;
       mp[0] = l_tot > 0.f ? m_ref : -INFINITY;
@@ -469,8 +485,8 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
   }
 }
 
-// Merge the splits of one (row, head): weights 2^(m_s - M), then a weighted
-// sum of the partial outputs (128 threads x 4 channels, loads unrolled).
+// Merge the splits of one (row, head): split s weighs l_s 2^(m_s - M) / sum,
+// applied to its normalised partial (128 threads x 4 channels, loads unrolled).
 template <bool MULTI>
 __global__ __launch_bounds__(128) void k_mla_combine(const MlaPtrs P, int32_t rows) {
   __shared__ float wsh[MAX_SPLITS];
@@ -490,23 +506,23 @@ __global__ __launch_bounds__(128) void k_mla_combine(const MlaPtrs P, int32_t ro
     float w = (M == -INFINITY || m == -INFINITY) ? 0.f : exp2f(m - M);
     float ws = w * l;
     for (int o = 32; o > 0; o >>= 1) ws += __shfl_xor(ws, o, 64);
-    if (lane < S) wsh[lane] = ws > 0.f ? w / ws : 0.f;
+    if (lane < S) wsh[lane] = ws > 0.f ? w * l / ws : 0.f;  // weight of the normalised partial
     if (lane == 0) {
       stat[0] = M;
       stat[1] = ws;
     }
   }
   __syncthreads();
-  const float* op = P.o_part + (part0 * ATT_HEADS + h) * LAT_DIM + threadIdx.x * 4;
+  const _Float16* op = P.o_part + (part0 * ATT_HEADS + h) * LAT_DIM + threadIdx.x * 4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 8
   for (int s = 0; s < S; ++s) {
     float f = wsh[s];
-    float4 v = *reinterpret_cast<const float4*>(op + (size_t)s * ATT_HEADS * LAT_DIM);
-    acc.x = fmaf(f, v.x, acc.x);
-    acc.y = fmaf(f, v.y, acc.y);
-    acc.z = fmaf(f, v.z, acc.z);
-    acc.w = fmaf(f, v.w, acc.w);
+    const v4h v = *reinterpret_cast<const v4h*>(op + (size_t)s * ATT_HEADS * LAT_DIM);
+    acc.x = fmaf(f, (float)v[0], acc.x);
+    acc.y = fmaf(f, (float)v[1], acc.y);
+    acc.z = fmaf(f, (float)v[2], acc.z);
+    acc.w = fmaf(f, (float)v[3], acc.w);
   }
   *reinterpret_cast<float4*>(P.out[layer] + ((size_t)r * ATT_HEADS + h) * LAT_DIM + threadIdx.x * 4) = acc;
   if (P.lse[layer] && threadIdx.x == 0)
