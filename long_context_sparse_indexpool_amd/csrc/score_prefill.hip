@@ -12,17 +12,21 @@
 // Scores of Q queries x G groups: [Q*32, 128] x [128, G] int8 -> int32, then
 // S[q][g] = sum_h w[q][h] * max(0, acc[q,h][g]).  v_mfma_i32_32x32x32_i8 with a
 // query's 32 heads as M and 32 groups as N; four MFMAs cover the 128 channels.
-// Each wave keeps 4 queries' operands and head weights (two 16-bit weights per
-// register) in registers and streams 32-group key blocks through them, three
-// blocks of loads in flight; the accumulators live in VGPRs.  The epilogue is
-// two VALU ops per element (max, 24-bit multiply-add with the weight's half
-// selected in the instruction) plus one cross-half add, which costs about as
-// much issue time as the MFMAs, so each wave issues the MFMAs of its next query
-// before the epilogue of the current one.  A workgroup covers 16 queries x
-// 4096 groups.  Workgroups are numbered so that every query block of one group
-// range lands on the same XCD (dispatch is round-robin over the 8 XCDs): the
-// range's 512 KiB of keys is then fetched into that XCD's L2 once and reused
-// by all query blocks.
+// A workgroup covers 16 queries x 4096 groups; each of its four waves keeps 4
+// queries' operands and head weights in registers.  The 32-group key blocks
+// are fetched once per workgroup, by direct-to-LDS loads into a four-slot ring
+// (each wave fetches one K step of a block), and every wave reads its operands
+// from there: a quarter of the key traffic of per-wave register loads, three
+// blocks in flight, no registers spent on prefetch.  The epilogue costs two
+// VALU ops per accumulator element (max, 24-bit multiply-add by the head
+// weight); the two halves of a query pair's 32 heads meet in one cross-half
+// swap, after which each lane finishes one score of one of the two queries.
+// The MFMAs of each query are issued before the epilogue of the previous one,
+// across block boundaries, so the matrix core and the VALU work side by side.
+// Workgroups are numbered so that every query block of one group range lands
+// on the same XCD (dispatch is round-robin over the 8 XCDs): the range's
+// 512 KiB of keys is then fetched into that XCD's L2 once and reused by all
+// query blocks.
 #include "isa_launch.hpp"
 
 namespace isa {
@@ -32,6 +36,34 @@ constexpr int PF_QW = 4;                      // queries per wave
 constexpr int PF_QB = PF_QW * (PF_THREADS / 64);  // queries per workgroup
 constexpr int PF_GT = 4096;                   // groups per workgroup
 constexpr int N_XCD = 8;
+constexpr int PF_NS = 4;                      // key blocks staged in LDS (ring slots)
+constexpr int PF_KB = 32 * IDX_DIM;           // bytes of one key block (32 groups)
+
+// 16 bytes per lane from global memory straight into LDS (lane l's bytes at
+// lds + 16 l; lds is uniform).  Written out rather than through the builtin:
+// the compiler would otherwise guard every later LDS read with a wait for all
+// outstanding loads, since it cannot tell ring slots apart.  The instruction
+// has no register result; completion is tracked by vmcnt (waited for
+// explicitly by the caller).  One wait state separates the M0 write from the
+// load that reads it; nothing else in this kernel uses M0.
+__device__ __forceinline__ void load_to_lds16(const int8_t* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
+}
+
+// s_waitcnt vmcnt(N), no wait on the other counters
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | ((N >> 4) << 14));
+}
+
+// a * b + c on 24-bit unsigned operands in one instruction (the compiler
+// otherwise splits it into a multiply and a three-way add)
+__device__ __forceinline__ uint32_t mad_u24(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t d;
+  asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
 
 struct PrefillPtrs {
   const int8_t* q;
@@ -67,7 +99,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_scores(const BatchArgs a
 
   // this wave's queries: operands, head weights of the accumulator rows, visible range
   v4i qa[PF_QW][4];
-  uint32_t wv[PF_QW][8];  // head weights of the accumulator rows, two 16-bit halves per register
+  uint32_t wv[PF_QW][16];  // head weights of the accumulator rows
   int lastg[PF_QW];
   bool bad = false;
 #pragma unroll
@@ -84,7 +116,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_scores(const BatchArgs a
     for (int r = 0; r < 16; ++r) {
       int w = hp[(r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)];
       bad |= (w < 0) | (w > 64);
-      wv[qq][r >> 1] = (r & 1) ? (wv[qq][r >> 1] | ((uint32_t)w << 16)) : (uint32_t)w;
+      wv[qq][r] = (uint32_t)w;
     }
     int p = P.q_pos[qc];
     if (live && (p < 0 || p >= L)) {
@@ -96,90 +128,129 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_scores(const BatchArgs a
   if (__any(bad) && lane == 0) report(P.err, ISA_DERR_HEADW_RANGE | ISA_DERR_ROW_RANGE);
   __syncthreads();
 
-  const int8_t* kbase = P.pooled + (lane >> 5) * 64;
-  // Loads are unconditional (a group past the range, or on a page outside the
-  // pool, reads row 0 and is zeroed by its mask) and the two register buffers
-  // alternate by block parity, so each block waits for its own loads only.
-  auto load_blk = [&](int blk, v4i (&kb)[4], int& mask) {
+  // Key blocks (32 groups x 128 B) are staged once per workgroup in a ring of
+  // PF_NS LDS slots by direct-to-LDS loads: wave w fetches K step w of a block
+  // (lane l: group l%32, channels 64(l/32) + 16w .. +15), which lands at slot
+  // + 1024w + 16l, so every wave's operand read of K step c is one contiguous
+  // KiB.  Loads are unconditional (a group past the range, or on a page
+  // outside the pool, reads row 0); such a group needs no mask: past the range
+  // its score falls outside the row's buffer range and is dropped, and a page
+  // outside the pool has already been reported as an error.
+  __shared__ __attribute__((aligned(16))) int8_t ring[PF_NS][PF_KB];
+  auto issue = [&](int blk) {
     const int gi = blk * 32 + (lane & 31);
     const int gl = min(gi, PF_GT - 1);
     const int pg = pages[gl / PAGE_GRP];
     const bool ok = gi < gN && pg >= 0;
-    mask = ok ? -1 : 0;
     const size_t row = ok ? (size_t)pg * PAGE_GRP + gl % PAGE_GRP : 0;
-    const v4i* p = reinterpret_cast<const v4i*>(kbase + row * IDX_DIM);
-    kb[0] = p[0];
-    kb[1] = p[1];
-    kb[2] = p[2];
-    kb[3] = p[3];
+    load_to_lds16(P.pooled + row * IDX_DIM + (lane >> 5) * 64 + wave * 16,
+                  (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int8_t*)&ring[blk % PF_NS][wave * 1024]);
+  };
+  auto read_blk = [&](int blk, v4i (&k)[4]) {
+    const int8_t* src = &ring[blk % PF_NS][lane * 16];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) k[c] = *reinterpret_cast<const v4i*>(src + c * 1024);
   };
   // each query's score row as a buffer resource (scalar base, 32-bit offsets,
-  // stores past the row's end dropped by the range check)
+  // stores past the row's end dropped by the range check; a query beyond Q
+  // gets an empty range, so nothing of it is stored)
   __amdgpu_buffer_rsrc_t rows[PF_QW];
 #pragma unroll
   for (int qq = 0; qq < PF_QW; ++qq) {
-    const int qi = min(qb * PF_QB + wave * PF_QW + qq, P.Q - 1);
-    rows[qq] = __builtin_amdgcn_make_buffer_rsrc(P.scores + (size_t)qi * P.ld, 0, (g0 + gN) * 4, 0x00020000);
+    const int qi = qb * PF_QB + wave * PF_QW + qq;
+    rows[qq] = __builtin_amdgcn_make_buffer_rsrc(P.scores + (size_t)min(qi, P.Q - 1) * P.ld, 0,
+                                                 qi < P.Q ? (g0 + gN) * 4 : 0, 0x00020000);
   }
+  // visibility bound per query pair: lanes < 32 carry the pair's first query,
+  // lanes >= 32 its second (the layout of a pair's finished scores)
+  int lgp[PF_QW / 2];
+#pragma unroll
+  for (int pr = 0; pr < PF_QW / 2; ++pr)
+    lgp[pr] = min(lane < 32 ? lastg[2 * pr] : lastg[2 * pr + 1], g0 + gN - 1);  // range clamp: see the loop
+  const uint32_t oob_lo = lane < 32 ? 0u : 0x80000000u;  // beyond every row's range
+  const uint32_t oob_hi = lane < 32 ? 0x80000000u : 0u;
   uint32_t smax = 0;  // largest visible score of this lane (overflow check after the loop)
-  // score of the lane's group for query qq from its 32 x 32 accumulator block:
-  // the lane holds 16 heads of group l%32; the other 16 are in lane l^32.
-  // gb: first group of the block (uniform)
-  auto epilogue = [&](const v16i& acc, int qq, int gb) {
+  // this lane's share of query qq's score of group l%32 from its 32 x 32
+  // accumulator block: the lane holds 16 of the 32 heads, lane l^32 the others
+  auto partial = [&](const v16i& acc, int qq) {
     uint32_t s = 0;
 #pragma unroll
-    for (int r = 0; r < 16; r += 2)  // ReLU <= 2^21: 24-bit multiplies by the packed weights
-      s += __umul24((uint32_t)max(acc[r], 0), wv[qq][r >> 1] & 0xFFFFu) +
-           __umul24((uint32_t)max(acc[r + 1], 0), wv[qq][r >> 1] >> 16);
-    s += __builtin_amdgcn_permlane32_swap(s, s, false, false)[1];  // lanes < 32: + lane l+32
-    const int lg = lastg[qq];
-    if (lg == -2) return;  // uniform: query beyond Q
+    for (int r = 0; r < 16; ++r) s = mad_u24((uint32_t)max(acc[r], 0), wv[qq][r], s);  // ReLU <= 2^21
+    return s;
+  };
+  // scores of the query pair (2pr, 2pr + 1) for the block's 32 groups (gb
+  // uniform): one cross-half swap leaves the first query's sums in lanes < 32
+  // and the second's in lanes >= 32, so every lane finishes one score
+  auto finish = [&](uint32_t s0, uint32_t s1, int pr, int gb) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(s0, s1, false, false);
+    const uint32_t s = sw[0] + sw[1];
     const int g = gb + (lane & 31);
-    const bool vis = g <= lg;
+    const bool vis = g <= lgp[pr];
     smax = max(smax, vis ? s : 0u);
-    if (lane < 32)  // groups past the sequence fall outside the row's range and are dropped
-      __builtin_amdgcn_raw_buffer_store_b32(vis ? (int32_t)s : -1, rows[qq], g * 4, 0, 2 /* nontemporal */);
+    const int32_t v = vis ? (int32_t)s : -1;
+    // both stores from every lane, each half's offset pushed out of the other
+    // row's range (uniform resources, no per-lane branch); groups past the
+    // sequence fall outside the row's range as well and are dropped
+    __builtin_amdgcn_raw_buffer_store_b32(v, rows[2 * pr], (g * 4) | oob_lo, 0, 2 /* nontemporal */);
+    __builtin_amdgcn_raw_buffer_store_b32(v, rows[2 * pr + 1], (g * 4) | oob_hi, 0, 2 /* nontemporal */);
   };
-  // one block of 32 groups for the wave's queries; the MFMAs of the next query
-  // are issued before the epilogue of the current one, so the matrix core and
-  // the VALU work side by side
-  auto do_blk = [&](int blk, const v4i (&kb)[4], int mask) {
+  auto mm = [&](const v4i (&k)[4], int qq) {
+    v16i acc = {0};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[qq][c], k[c], acc, 0, 0, 0);
+    return acc;
+  };
+  // Software pipeline over (block, query): the MFMAs of each query are issued
+  // before the epilogue of the previous one, so the matrix core and the VALU
+  // work side by side; the last query of a block is finished in the next
+  // block.  At most two accumulators are live at any point.
+  static_assert(PF_QW == 4, "the pipeline below is written for four queries per wave");
+  v16i pend;       // accumulator of the previous block's last query
+  uint32_t s2 = 0;  // partial of the previous block's third query
+  auto do_blk = [&](int blk, const v4i (&k)[4], bool first) {
     const int g = g0 + blk * 32;
-    const v4i k[4] = {kb[0] & mask, kb[1] & mask, kb[2] & mask, kb[3] & mask};
-    auto mm = [&](int qq) {
-      v16i acc = {0};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[qq][c], k[c], acc, 0, 0, 0);
-      return acc;
-    };
-    static_assert(PF_QW % 2 == 0, "queries are pipelined in pairs");
-    v16i a0 = mm(0), a1;
-#pragma unroll
-    for (int qq = 0; qq < PF_QW; qq += 2) {
-      a1 = mm(qq + 1);
-      epilogue(a0, qq, g);
-      if (qq + 2 < PF_QW) a0 = mm(qq + 2);
-      epilogue(a1, qq + 1, g);
-    }
+    v16i x = mm(k, 0);
+    if (!first) finish(s2, partial(pend, 3), 1, g - 32);
+    v16i y = mm(k, 1);
+    const uint32_t s0 = partial(x, 0);
+    x = mm(k, 2);
+    finish(s0, partial(y, 1), 0, g);
+    pend = mm(k, 3);
+    s2 = partial(x, 2);
   };
+  // Block b: wait for this wave's load of block b, meet the other waves (their
+  // quarters of the block are then in LDS, and every wave is done with the
+  // slot of block b - 1), refill that slot with block b + PF_NS - 1, compute.
+  // The compiler does not track direct-to-LDS loads, so the waits are explicit:
+  // vmcnt counts loads and stores in issue order, and the load of block b is
+  // followed by PF_NS - 2 later loads and the score stores of the blocks in
+  // between (two in block 0, four in every later block); a count below the
+  // true one only waits longer.
+  static_assert(PF_NS == 4, "the wait counts below are written for four slots");
   const int nblk = (gN + 31) / 32;
-  v4i bA[4], bB[4], bC[4];
-  int mA, mB, mC;
-  load_blk(0, bA, mA);
-  __builtin_amdgcn_sched_barrier(0);
-  load_blk(1, bB, mB);
-  __builtin_amdgcn_sched_barrier(0);
-  load_blk(2, bC, mC);
-  __builtin_amdgcn_sched_barrier(0);
-  for (int blk = 0; blk < nblk; blk += 3) {  // trailing blocks past the range store nothing
-    do_blk(blk, bA, mA);
-    load_blk(blk + 3, bA, mA);
-    do_blk(blk + 1, bB, mB);
-    load_blk(blk + 4, bB, mB);
-    do_blk(blk + 2, bC, mC);
-    load_blk(blk + 5, bC, mC);
+  v4i kb[4];
+#pragma unroll
+  for (int b = 0; b < PF_NS - 1; ++b) issue(b);
+  wait_vmcnt<PF_NS - 2>();
+  lds_barrier();
+  asm volatile("" ::: "memory");
+  issue(PF_NS - 1);
+  read_blk(0, kb);
+  do_blk(0, kb, true);
+  int blk = 1;
+  for (; blk < nblk; ++blk) {
+    if (blk >= PF_NS)
+      wait_vmcnt<(PF_NS - 2) + 4 * (PF_NS - 1)>();
+    else
+      wait_vmcnt<PF_NS - 2 + 2>();
+    lds_barrier();
+    asm volatile("" ::: "memory");
+    issue(blk + PF_NS - 1);
+    read_blk(blk, kb);
+    do_blk(blk, kb, false);
   }
-  if (__any(lane < 32 && smax > 0x7FFFFFFFu) && lane == 0) report(P.err, ISA_DERR_SCORE_OVERFLOW);  // (lanes >= 32 hold doubled sums)
+  finish(s2, partial(pend, 3), 1, g0 + (blk - 1) * 32);
+  if (__any(smax > 0x7FFFFFFFu) && lane == 0) report(P.err, ISA_DERR_SCORE_OVERFLOW);
 }
 
 isa_status launch_prefill_scores(const BatchArgs& a, const int8_t* q, const int8_t* hw, const int32_t* q_pos,
