@@ -198,7 +198,9 @@ isa_status isa_indexer_topk(const int8_t* q, const int8_t* head_w, const int8_t*
  * A row with no visible token gets out = 0 and lse = -inf.
  * Arithmetic: bf16 products with fp32 accumulation for q.c; fp32 softmax;
  * probabilities rounded to fp16 and latents converted exactly to fp16 for the
- * weighted sum, fp32 accumulation.
+ * weighted sum, fp32 accumulation.  When a row's selection is split over
+ * several workgroups, each split's normalised output is held in fp16 (a convex
+ * combination of latent rows) and the splits are merged with fp32 weights.
  */
 isa_status isa_sparse_mla_decode(const uint16_t* q, const uint16_t* latent, const isa_seqs* s,
                                  const int32_t* row_seq, const int32_t* row_pos, int32_t rows,
