@@ -106,6 +106,7 @@ struct MlaPtrs {
   float c2;  // sm_scale * log2(e)
   int32_t splits;
   int32_t gps;  // groups per split
+  int32_t n_units;  // (layer, row, split) units of the launch
 };
 
 // FP8 E4M3 codes of 8 channels to fp16 (exact: every E4M3 value is an fp16
@@ -126,23 +127,37 @@ __device__ __forceinline__ v8h fp8x8_to_f16x8(v2i w) {
 // into its probability for the P.V product (the normalising sum stays unscaled).
 // MULTI: several layers share the selection (the layer is part of the grid);
 // a single-layer launch keeps every pointer a static kernel argument.
-template <bool FP8, bool MULTI>
+// NH: heads per workgroup.  With 32, two workgroups share a (row, split) unit,
+// one per half of the heads, numbered so that both land on the same XCD (the
+// second fetch of a latent row comes from its L2): half the MFMA and softmax
+// work per tile, for launches that would otherwise leave CUs idle.
+template <bool FP8, bool MULTI, int NH>
 __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, const MlaPtrs P) {
+  constexpr int HB = NH / 16;            // 16-head blocks of the workgroup
+  constexpr int NSW = NH / OWN_HEADS;    // waves that own softmax heads
   using LoadT = typename std::conditional<FP8, v2i, v4i>::type;  // one lane's 8 channels of a row
   using QOpT = typename std::conditional<FP8, v8h, v8bf>::type;
   __shared__ __attribute__((aligned(16))) _Float16 vt[2][TILE_TOK * V_STRIDE];  // 2 x 33 KiB: fp16 V of a tile, double-buffered
-  __shared__ v4f sp[2][4][HBLK][SP_LANES];                // 48 KiB: partial S^T [half][group][head block][lane]
-  __shared__ _Float16 pb[ATT_HEADS * P_STRIDE];           // 5 KiB: P of the tile [head][token]
-  __shared__ __attribute__((aligned(16))) float alpha_s[ATT_HEADS];
+  __shared__ v4f sp[2][4][HB][SP_LANES];                  // 48 KiB (64 heads): partial S^T [half][group][head block][lane]
+  __shared__ _Float16 pb[NH * P_STRIDE];                  // 5 KiB (64 heads): P of the tile [head][token]
+  __shared__ __attribute__((aligned(16))) float alpha_s[NH];
   __shared__ __attribute__((aligned(16))) uint32_t flag_s[8];
-  __shared__ float fin_s[2][ATT_HEADS];
+  __shared__ float fin_s[2][NH];
   __shared__ __attribute__((aligned(16))) uint32_t trow[MAX_GPS * GROUP];  // latent row of each token slot, ~0 if not visible
   __shared__ int32_t bt_s[BT_LDS];                        // 4 KiB: the row's block-table entries
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cg = wave & 3, th = wave >> 2;   // channels 128cg.., tokens 16th.. of each tile
-  const int layer = MULTI ? (int)blockIdx.x / (P.rows * P.splits) : 0;  // layers sharing the selection
-  const int rs = MULTI ? (int)blockIdx.x % (P.rows * P.splits) : (int)blockIdx.x;
+  int unit = (int)blockIdx.x, hh = 0;  // (layer, row, split) unit and half of the heads
+  if constexpr (NH < ATT_HEADS) {
+    const int slot = (int)blockIdx.x / 8;  // dispatch is round-robin over the 8 XCDs
+    hh = slot & 1;
+    unit = (slot >> 1) * 8 + (int)blockIdx.x % 8;
+    if (unit >= P.n_units) return;  // the whole workgroup
+  }
+  const int h0 = hh * NH;  // first head of this workgroup
+  const int layer = MULTI ? unit / (P.rows * P.splits) : 0;  // layers sharing the selection
+  const int rs = MULTI ? unit % (P.rows * P.splits) : unit;
   const int r = rs / P.splits;
   const int split = rs % P.splits;
   const uint16_t* const q = P.q[layer];
@@ -169,11 +184,11 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
   // query operand (B = Q^T), fetched in the same round as the group ids:
   // lane -> head 16hb + lq, channels 128cg + 32c + 8lg .. +7 (bf16 bits; the
   // FP8 path converts it to fp16 once the token table is built)
-  v4i qraw[HBLK][KSTEPS];
+  v4i qraw[HB][KSTEPS];
   {
-    const uint16_t* qp = q + ((size_t)r * ATT_HEADS + lq) * LAT_DIM + cg * CG_DIM + lg * 8;
+    const uint16_t* qp = q + ((size_t)r * ATT_HEADS + h0 + lq) * LAT_DIM + cg * CG_DIM + lg * 8;
 #pragma unroll
-    for (int hb = 0; hb < HBLK; ++hb)
+    for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
       for (int c = 0; c < KSTEPS; ++c) qraw[hb][c] = *reinterpret_cast<const v4i*>(qp + (size_t)hb * 16 * LAT_DIM + c * 32);
   }
@@ -221,13 +236,14 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
   // eight lanes of a head; l_run is this lane's share of the sum)
   const int own_h = OWN_HEADS * wave + (lane & 7);
   const int own_tq = lane >> 3;  // tokens 4 own_tq .. +3 of the tile
+  if (tid < 8) flag_s[tid] = 0u;  // waves without softmax heads never set theirs
   lds_barrier();  // token table complete
 
   const int nslot = ng * GROUP;
   const int ntile = (nslot + TILE_TOK - 1) / TILE_TOK;
-  QOpT qop[HBLK][KSTEPS];
+  QOpT qop[HB][KSTEPS];
 #pragma unroll
-  for (int hb = 0; hb < HBLK; ++hb)
+  for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
     for (int c = 0; c < KSTEPS; ++c) {
       const v4i w = qraw[hb][c];
@@ -237,9 +253,9 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
       else
         qop[hb][c] = __builtin_bit_cast(v8bf, w);
     }
-  v4f o[HBLK][NBLK];
+  v4f o[HB][NBLK];
 #pragma unroll
-  for (int hb = 0; hb < HBLK; ++hb)
+  for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
     for (int nb = 0; nb < NBLK; ++nb) o[hb][nb] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY, l_run = 0.f;
@@ -269,9 +285,9 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
   auto tile_step = [&](int t, LoadT (&buf)[KSTEPS], int& bmask, float4& sbuf) {
     const int vb = t & 1;
     _Float16* vtb = vt[vb];
-    v4f acc[HBLK];
+    v4f acc[HB];
 #pragma unroll
-    for (int hb = 0; hb < HBLK; ++hb) acc[hb] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int hb = 0; hb < HB; ++hb) acc[hb] = v4f{0.f, 0.f, 0.f, 0.f};
     int nmask;
     const LoadT* nsrc = row_of(t + 2, nmask);
 #pragma unroll
@@ -280,13 +296,13 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
       if constexpr (FP8) {
         const v8h kh = fp8x8_to_f16x8(buf[c] & bmask);
 #pragma unroll
-        for (int hb = 0; hb < HBLK; ++hb)
+        for (int hb = 0; hb < HB; ++hb)
           acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, qop[hb][c], acc[hb], 0, 0, 0);
         vh = __builtin_bit_cast(v4i, kh);
       } else {
         const v4i kv = buf[c] & bmask;
 #pragma unroll
-        for (int hb = 0; hb < HBLK; ++hb)
+        for (int hb = 0; hb < HB; ++hb)
           acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kv), qop[hb][c], acc[hb], 0, 0, 0);
         vh = v4i{(int)bf16x2_to_f16x2((uint32_t)kv[0]), (int)bf16x2_to_f16x2((uint32_t)kv[1]),
                  (int)bf16x2_to_f16x2((uint32_t)kv[2]), (int)bf16x2_to_f16x2((uint32_t)kv[3])};
@@ -296,11 +312,11 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
     }
     bmask = nmask;
 #pragma unroll
-    for (int hb = 0; hb < HBLK; ++hb) sp[th][cg][hb][sp_slot(lane)] = acc[hb];
+    for (int hb = 0; hb < HB; ++hb) sp[th][cg][hb][sp_slot(lane)] = acc[hb];
     lds_barrier();  // partial scores and V of this tile complete
 
     // ---- softmax of the owned heads over the tile's 32 tokens ----
-    {
+    if (wave < NSW) {
       const int hb = own_h >> 4, hl = own_h & 15;
       const int tq = own_tq, th2 = tq >> 2;
       v4f s = sp[th2][0][hb][sp_slot(hl + 16 * (tq & 3))];
@@ -360,7 +376,7 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
     // the flags are the same in every lane: a scalar branch
     if (__builtin_amdgcn_readfirstlane(f0.x | f0.y | f0.z | f0.w | f1.x | f1.y | f1.z | f1.w) != 0u) {
 #pragma unroll
-      for (int hb = 0; hb < HBLK; ++hb) {
+      for (int hb = 0; hb < HB; ++hb) {
         const float4 al = *reinterpret_cast<const float4*>(&alpha_s[hb * 16 + 4 * lg]);
 #pragma unroll
         for (int nb = 0; nb < NBLK; ++nb) {
@@ -371,9 +387,9 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
         }
       }
     }
-    v8h pv[HBLK];
+    v8h pv[HB];
 #pragma unroll
-    for (int hb = 0; hb < HBLK; ++hb)
+    for (int hb = 0; hb < HB; ++hb)
       pv[hb] = __builtin_bit_cast(v8h, *reinterpret_cast<const v4i*>(&pb[(hb * 16 + lq) * P_STRIDE + lg * 8]));
     // V operand: lane (lq, lg) gets channel 16nb + lq of tokens 8lg .. 8lg+7
     const _Float16* vr0 = &vtb[vrow(8 * lg + (lq >> 2)) * V_STRIDE + wave * OUT_DIM + 4 * (lq & 3)];
@@ -384,7 +400,7 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
       const v8h vv = __builtin_bit_cast(v8h, v4i{__builtin_bit_cast(v2i, v0).x, __builtin_bit_cast(v2i, v0).y,
                                                   __builtin_bit_cast(v2i, v1).x, __builtin_bit_cast(v2i, v1).y});
 #pragma unroll
-      for (int hb = 0; hb < HBLK; ++hb) o[hb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pv[hb], vv, o[hb][nb], 0, 0, 0);
+      for (int hb = 0; hb < HB; ++hb) o[hb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pv[hb], vv, o[hb][nb], 0, 0, 0);
     }
   };
 
@@ -427,16 +443,16 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
   float l_tot = l_run + __shfl_xor(l_run, 8, 64);
   l_tot += __shfl_xor(l_tot, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
-  if (own_tq == 0) {
+  if (own_tq == 0 && wave < NSW) {
     fin_s[0][own_h] = l_tot > 0.f ? m_ref : -INFINITY;
     fin_s[1][own_h] = l_tot;
   }
   __syncthreads();
   const int d_base = wave * OUT_DIM;
   if (P.splits == 1) {
-    float* orow = P.out[layer] + (size_t)r * ATT_HEADS * LAT_DIM;
+    float* orow = P.out[layer] + ((size_t)r * ATT_HEADS + h0) * LAT_DIM;
 #pragma unroll
-    for (int hb = 0; hb < HBLK; ++hb) {
+    for (int hb = 0; hb < HB; ++hb) {
       float inv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -449,17 +465,17 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
         for (int i = 0; i < 4; ++i)
           orow[(size_t)(hb * 16 + 4 * lg + i) * LAT_DIM + d_base + nb * 16 + lq] = o[hb][nb][i] * inv[i];
     }
-    if (P.lse[layer] && own_tq == 0)
-      P.lse[layer][(size_t)r * ATT_HEADS + own_h] = l_tot > 0.f ? m_ref * LN2 + logf(l_tot) : -INFINITY;
+    if (P.lse[layer] && own_tq == 0 && wave < NSW)
+      P.lse[layer][(size_t)r * ATT_HEADS + h0 + own_h] = l_tot > 0.f ? m_ref * LN2 + logf(l_tot) : -INFINITY;
   } else {
     // the split's normalised output O / l in fp16 (a convex combination of
     // latent rows, so within their range), staged in LDS -- the V tiles are
     // free now -- and written with 16-B stores
-    const size_t part = blockIdx.x;  // (layer, row, split)
+    const size_t part = unit;  // (layer, row, split)
     _Float16* stage = &vt[0][0];
-    static_assert(2 * TILE_TOK * V_STRIDE >= ATT_HEADS * LAT_DIM, "staging fits in the V tiles");
+    static_assert(2 * TILE_TOK * V_STRIDE >= NH * LAT_DIM, "staging fits in the V tiles");
 #pragma unroll
-    for (int hb = 0; hb < HBLK; ++hb) {
+    for (int hb = 0; hb < HB; ++hb) {
       float inv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -473,12 +489,12 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
           stage[(hb * 16 + 4 * lg + i) * LAT_DIM + d_base + nb * 16 + lq] = (_Float16)(o[hb][nb][i] * inv[i]);
     }
     __syncthreads();
-    v4i* op = reinterpret_cast<v4i*>(P.o_part + part * ATT_HEADS * LAT_DIM);
-    constexpr int N16 = ATT_HEADS * LAT_DIM * 2 / 16;
+    v4i* op = reinterpret_cast<v4i*>(P.o_part + (part * ATT_HEADS + h0) * LAT_DIM);
+    constexpr int N16 = NH * LAT_DIM * 2 / 16;
 #pragma unroll
     for (int k = 0; k < N16 / MLA_THREADS; ++k) op[tid + k * MLA_THREADS] = reinterpret_cast<const v4i*>(stage)[tid + k * MLA_THREADS];
-    if (own_tq == 0) {
-      float* mp = P.ml_part + (part * ATT_HEADS + own_h) * 2;
+    if (own_tq == 0 && wave < NSW) {
+      float* mp = P.ml_part + (part * ATT_HEADS + h0 + own_h) * 2;
       mp[0] = l_tot > 0.f ? m_ref : -INFINITY;
       mp[1] = l_tot;
     }
@@ -573,14 +589,20 @@ isa_status launch_sparse_mla(const BatchArgs& a, const MlaPlan& p, int32_t n_lay
   P.c2 = sm_scale * LOG2E;
   P.splits = p.splits;
   P.gps = p.groups_per_split;
-  const dim3 grid(n_layers * p.rows * p.splits), block(MLA_THREADS);
+  const int units = n_layers * p.rows * p.splits;
+  P.n_units = units;
+  // a launch of at most 128 units would fill half the CUs: split the heads
+  const bool hsplit = units <= 128;
+  const dim3 grid(hsplit ? (unsigned)((units + 7) / 8 * 16) : (unsigned)units), block(MLA_THREADS);
   hipError_t e;
+#define ISA_MLA_LAUNCH(FP8_, MULTI_)                                                                         \
+  (hsplit ? launch_timed(ISA_TIMER_MLA_SPLIT, k_mla_split<FP8_, MULTI_, ATT_HEADS / 2>, grid, block, stream, a, P) \
+          : launch_timed(ISA_TIMER_MLA_SPLIT, k_mla_split<FP8_, MULTI_, ATT_HEADS>, grid, block, stream, a, P))
   if (lat_scale)
-    e = n_layers > 1 ? launch_timed(ISA_TIMER_MLA_SPLIT, k_mla_split<true, true>, grid, block, stream, a, P)
-                     : launch_timed(ISA_TIMER_MLA_SPLIT, k_mla_split<true, false>, grid, block, stream, a, P);
+    e = n_layers > 1 ? ISA_MLA_LAUNCH(true, true) : ISA_MLA_LAUNCH(true, false);
   else
-    e = n_layers > 1 ? launch_timed(ISA_TIMER_MLA_SPLIT, k_mla_split<false, true>, grid, block, stream, a, P)
-                     : launch_timed(ISA_TIMER_MLA_SPLIT, k_mla_split<false, false>, grid, block, stream, a, P);
+    e = n_layers > 1 ? ISA_MLA_LAUNCH(false, true) : ISA_MLA_LAUNCH(false, false);
+#undef ISA_MLA_LAUNCH
   if (e != hipSuccess) return ISA_ERR_HIP;
   if (p.splits > 1) {
     if (n_layers > 1)
