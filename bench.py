@@ -547,6 +547,8 @@ def main():
     ap.add_argument("--primary-only", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-run", action="store_true", help="workload for the rocprofv3 counter passes")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the prefill scoring measurement (for profiling that kernel alone)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_k_indexer_score_*.json from two counter CSVs (no GPU)")
     args = ap.parse_args()
@@ -568,6 +570,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     import long_context_sparse_indexpool_amd as m  # noqa: F401  (fails loudly when libisa.so is missing)
+    if args.prefill_only:
+        print(json.dumps({"prefill_scores": bench_prefill(args)}), flush=True)
+        return
 
     wl = workload(2)
     dec = Decode(wl, N_POOL_COPIES, N_QSETS, keep_host=not args.no_cpu_baseline)
