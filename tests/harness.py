@@ -240,14 +240,20 @@ def check_topk_row(S: np.ndarray, k: int, idx_row: np.ndarray, cnt: int):
     assert np.array_equal(idx_row, ridx), "selected ids differ from the oracle"
 
 
-def attention_tolerance(out: np.ndarray, ref: np.ndarray, lse=None, ref_lse=None):
-    """max-abs <= 2e-2 and relative L2 <= 1e-3 (and |d lse| <= 1e-3 where finite)."""
+def attention_tolerance(out: np.ndarray, ref: np.ndarray, lse=None, ref_lse=None, vmax: float = 0.0):
+    """max-abs <= 2e-2 and relative L2 <= 1e-3 (and |d lse| <= 1e-3 where finite).
+
+    vmax: the largest |latent value| among the attended tokens, when a test plants
+    values far outside the N(0,1) workload.  The probabilities of the P.V product
+    are fp16, off by at most 2^-11 relative each, so an output element can be off
+    by about 2^-11 * vmax: the 2e-2 bound covers |v| <= 40 and grows in
+    proportion beyond that (the relative bounds are unchanged)."""
     d = out.astype(np.float64) - ref
     mx = float(np.max(np.abs(d))) if d.size else 0.0
     nrm = float(np.linalg.norm(ref))
     rel = float(np.linalg.norm(d) / nrm) if nrm > 0 else float(np.linalg.norm(d))
     assert np.all(np.isfinite(out)), "non-finite attention output"
-    assert mx <= 2e-2, f"max-abs error {mx}"
+    assert mx <= 2e-2 * max(1.0, vmax / 40.0), f"max-abs error {mx}"
     assert rel <= 1e-3, f"relative L2 error {rel}"
     dl = 0.0
     if lse is not None:
