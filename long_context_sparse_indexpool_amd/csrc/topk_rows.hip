@@ -6,7 +6,8 @@
 // 것": keep the top-k positions; with no more than k candidates nothing is
 // dropped.  Ties (unspecified on the pages): higher score first, then lower id.
 //
-// One 1024-thread workgroup per row, no workspace.  Pass 1 streams the row into
+// One 1024-thread workgroup per row, no workspace; rows are streamed with 16-B
+// loads, several in flight per thread.  Pass 1 streams the row into
 // an LDS histogram over the 11-bit monotone score key and finds the bin holding
 // the k-th best.  Pass 2 streams it again: ids above that bin are selected
 // outright, ids in it become (score, -id) keys in LDS (or, when they do not
@@ -19,6 +20,37 @@ namespace isa {
 
 constexpr int ROW_THREADS = 1024;
 constexpr int ROW_CAND = 2048;
+constexpr int ROW_UNROLL = 4;  // 16-B loads of a thread in flight per round
+
+// f(score, id) for every entry of the row, in any order.  A 16-B aligned row
+// (the usual case: ld a multiple of 4) is read with 16-B loads, ROW_UNROLL of
+// them issued by each thread before any is used (entries past the row read as
+// -1, which every caller skips); otherwise entry by entry.
+template <class F>
+__device__ __forceinline__ void for_each_entry(const int32_t* __restrict__ row, int32_t cols, bool aligned, F&& f) {
+  const int tid = threadIdx.x;
+  if (aligned) {
+    const int4* row4 = reinterpret_cast<const int4*>(row);
+    const int n4 = cols >> 2;
+    for (int i0 = 0; i0 < n4; i0 += ROW_UNROLL * ROW_THREADS) {
+      int4 v[ROW_UNROLL];
+#pragma unroll
+      for (int u = 0; u < ROW_UNROLL; ++u) v[u] = row4[min(i0 + u * ROW_THREADS + tid, n4 - 1)];
+#pragma unroll
+      for (int u = 0; u < ROW_UNROLL; ++u) {
+        const int i = i0 + u * ROW_THREADS + tid;
+        const int4 w = i < n4 ? v[u] : make_int4(-1, -1, -1, -1);  // masked at use, not at load
+        f(w.x, 4 * i);
+        f(w.y, 4 * i + 1);
+        f(w.z, 4 * i + 2);
+        f(w.w, 4 * i + 3);
+      }
+    }
+    for (int e = 4 * n4 + tid; e < cols; e += ROW_THREADS) f(row[e], e);
+  } else {
+    for (int e = tid; e < cols; e += ROW_THREADS) f(row[e], e);
+  }
+}
 
 __global__ __launch_bounds__(ROW_THREADS) void k_topk_rows(const int32_t* __restrict__ scores, int32_t cols,
                                                            int32_t ld, int32_t k, int32_t* __restrict__ out_idx,
@@ -34,12 +66,12 @@ __global__ __launch_bounds__(ROW_THREADS) void k_topk_rows(const int32_t* __rest
   const int32_t* row = scores + (size_t)r * ld;
   int32_t* orow = out_idx + (size_t)r * k;
 
+  const bool aligned = ((uintptr_t)row & 15u) == 0;  // uniform
   for (int i = tid; i < NBINS; i += ROW_THREADS) hist[i] = 0;
   __syncthreads();
-  for (int e = tid; e < cols; e += ROW_THREADS) {
-    int32_t s = row[e];
+  for_each_entry(row, cols, aligned, [&](int32_t s, int) {
     if (s >= 0) atomicAdd(&hist[score_bin((uint32_t)s)], 1u);
-  }
+  });
   __syncthreads();
   int bstar;
   uint32_t n_gt, total;
@@ -66,9 +98,8 @@ __global__ __launch_bounds__(ROW_THREADS) void k_topk_rows(const int32_t* __rest
     scr[SCR_RES + 11] = 0;
   }
   __syncthreads();
-  for (int e = tid; e < cols; e += ROW_THREADS) {
-    int32_t s = row[e];
-    if (s < 0) continue;
+  for_each_entry(row, cols, aligned, [&](int32_t s, int e) {
+    if (s < 0) return;
     int bin = score_bin((uint32_t)s);
     if (bin > bstar) {
       uint32_t p = atomicAdd(&scr[SCR_RES + 10], 1u);
@@ -77,7 +108,7 @@ __global__ __launch_bounds__(ROW_THREADS) void k_topk_rows(const int32_t* __rest
       uint32_t p = atomicAdd(&scr[SCR_RES + 11], 1u);
       if (p < ROW_CAND) cand[p] = rank_key((uint32_t)s, (uint32_t)e);
     }
-  }
+  });
   __syncthreads();
   const uint32_t nb = scr[SCR_RES + 11];
   const bool in_lds = nb <= ROW_CAND;
