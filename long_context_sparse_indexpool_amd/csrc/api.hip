@@ -62,7 +62,7 @@ DecodeLayout decode_layout(const isa_seqs* s, int32_t k) {
 size_t pool_ws(const isa_seqs* s) {
   int nt = 0;
   for (int b = 0; b < s->batch; ++b) nt += pool_tiles(s->seq_lens_host[b]);
-  return HDR + up256((size_t)nt * 4 + (size_t)s->batch * 4);
+  return HDR + up256((size_t)nt * 4);  // per-tile maxima of the dynamic scale
 }
 
 size_t mla_ws(int32_t rows, int32_t k, int32_t layers) {

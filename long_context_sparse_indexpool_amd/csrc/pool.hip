@@ -12,9 +12,12 @@
 // HBM-bound stream: 1 KiB of bf16 keys in, 128 B of int8 out per group.  A
 // workgroup handles 256 groups (4 key pages) of one sequence; 16 threads per
 // group, 8 channels each, 16-byte loads and 8-byte stores.  The dynamic scale
-// needs the sequence's amax first: a first launch reduces per-tile maxima and
-// the last tile of each sequence (atomic ticket) publishes the scale; the
-// second launch pools again and quantises.  A given scale skips the first pass.
+// needs the sequence's amax first: a first launch writes per-tile maxima, and
+// every workgroup of the second launch reduces its sequence's maxima (a few
+// KiB, from L2) before it pools again and quantises; the kernel boundary
+// makes the maxima visible, with no fence or ticket (on this 8-XCD part a
+// device-scope release per workgroup writes back the L2 and costs more than
+// the stream).  A given scale skips the first pass.
 #include "isa_launch.hpp"
 
 namespace isa {
@@ -28,10 +31,13 @@ struct PoolPtrs {
   float* scales;
   int8_t* pooled;
   float* amax_part;   // [ntiles]
-  uint32_t* tickets;  // [B], zero between calls
   uint32_t* err;
   float w[4];
 };
+
+// k_pool passes: per-tile maxima; quantise with the given scales; quantise
+// with the scales of the maxima (and write them)
+enum PoolMode { POOL_AMAX = 0, POOL_GIVEN = 1, POOL_DYNAMIC = 2 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
@@ -78,11 +84,11 @@ __device__ __forceinline__ uint2 quant8(const float (&x)[8], float scale) {
   return make_uint2(packed[0], packed[1]);
 }
 
-template <bool QUANT>
+template <int MODE>
 __global__ __launch_bounds__(POOL_THREADS) void k_pool(const BatchArgs a, const PoolPtrs P) {
+  constexpr bool QUANT = MODE != POOL_AMAX;
   __shared__ int32_t pages[POOL_TILE_G / PAGE_GRP];
   __shared__ float red[POOL_THREADS / 64];
-  __shared__ uint32_t ticket;
   const int tid = threadIdx.x;
   const int tile = blockIdx.x;
   const int b = tile_owner(a, tile);
@@ -94,10 +100,24 @@ __global__ __launch_bounds__(POOL_THREADS) void k_pool(const BatchArgs a, const 
     int j = g0 / PAGE_GRP + tid;
     pages[tid] = (g0 + tid * PAGE_GRP < G) ? phys_page(P.bt, a.max_pages, a.num_pages, b, j, P.err) : -1;
   }
+  float scale = 1.f;
+  if (MODE == POOL_DYNAMIC) {  // the sequence's amax from the first launch's per-tile maxima
+    const int ntiles = a.tile_start[b + 1] - t0;
+    float m = 0.f;
+    for (int i = tid; i < ntiles; i += POOL_THREADS) m = fmaxf(m, P.amax_part[t0 + i]);
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+  }
   __syncthreads();
   const int c = tid & 15;  // channel block
-  float inv = 1.f, scale = 1.f;
-  if (QUANT) {
+  if (MODE == POOL_DYNAMIC) {
+    float m = red[0];
+#pragma unroll
+    for (int i = 1; i < POOL_THREADS / 64; ++i) m = fmaxf(m, red[i]);
+    scale = m > 0.f ? m / 127.f : 1.f;
+    if (tile == t0 && tid == 0) P.scales[b] = scale;
+    if (!isfinite(scale)) scale = 1.f;  // an infinite key: already reported by the first pass
+  } else if (MODE == POOL_GIVEN) {
     scale = P.scales[b];
     if (!(scale > 0.f) || !isfinite(scale)) {
       if (tid == 0) report(P.err, ISA_DERR_NONFINITE);
@@ -129,34 +149,16 @@ __global__ __launch_bounds__(POOL_THREADS) void k_pool(const BatchArgs a, const 
   }
   if (QUANT) return;
 
-  // ---- per-tile amax; the last tile of the sequence publishes the scale ----
+  // ---- per-tile amax ----
   if (__any(nonfinite) && (tid & 63) == 0) report(P.err, ISA_DERR_NONFINITE);
   for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
   if ((tid & 63) == 0) red[tid >> 6] = amax;
   __syncthreads();
   if (tid == 0) {
     float m = red[0];
+#pragma unroll
     for (int i = 1; i < POOL_THREADS / 64; ++i) m = fmaxf(m, red[i]);
     P.amax_part[tile] = m;
-    __threadfence();
-    ticket = atomicAdd(&P.tickets[b], 1u);
-  }
-  __syncthreads();
-  const int ntiles = a.tile_start[b + 1] - t0;
-  if ((int)ticket != ntiles - 1) return;
-  __threadfence();
-  float m = 0.f;
-  for (int i = tid; i < ntiles; i += POOL_THREADS)
-    m = fmaxf(m, __hip_atomic_load(&P.amax_part[t0 + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  __syncthreads();
-  if ((tid & 63) == 0) red[tid >> 6] = m;
-  __syncthreads();
-  if (tid == 0) {
-    float mm = red[0];
-    for (int i = 1; i < POOL_THREADS / 64; ++i) mm = fmaxf(mm, red[i]);
-    P.scales[b] = mm > 0.f ? mm / 127.f : 1.f;
-    __hip_atomic_store(&P.tickets[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -215,14 +217,14 @@ isa_status launch_indexpool(const BatchArgs& a, const uint16_t* keys, const floa
                             float* scales, int8_t* pooled, bool dynamic, float* amax_part, uint32_t* err,
                             hipStream_t stream) {
   const int ntiles = a.tile_start[a.batch];
-  // per-tile maxima, then one ticket counter per sequence
-  PoolPtrs P{keys, bt, scales, pooled, amax_part, reinterpret_cast<uint32_t*>(amax_part + ntiles), err,
-             {w4[0], w4[1], w4[2], w4[3]}};
+  PoolPtrs P{keys, bt, scales, pooled, amax_part, err, {w4[0], w4[1], w4[2], w4[3]}};
   if (dynamic) {
-    hipLaunchKernelGGL(k_pool<false>, dim3(ntiles), dim3(POOL_THREADS), 0, stream, a, P);
+    hipLaunchKernelGGL(k_pool<POOL_AMAX>, dim3(ntiles), dim3(POOL_THREADS), 0, stream, a, P);
     if (hipGetLastError() != hipSuccess) return ISA_ERR_HIP;
+    hipLaunchKernelGGL(k_pool<POOL_DYNAMIC>, dim3(ntiles), dim3(POOL_THREADS), 0, stream, a, P);
+  } else {
+    hipLaunchKernelGGL(k_pool<POOL_GIVEN>, dim3(ntiles), dim3(POOL_THREADS), 0, stream, a, P);
   }
-  hipLaunchKernelGGL(k_pool<true>, dim3(ntiles), dim3(POOL_THREADS), 0, stream, a, P);
   return hipGetLastError() == hipSuccess ? ISA_OK : ISA_ERR_HIP;
 }
 
