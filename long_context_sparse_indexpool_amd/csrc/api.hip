@@ -34,12 +34,32 @@ void fill_batch(const isa_seqs* s, BatchArgs* a, int32_t k) {
   a->max_pages = s->max_pages;
   a->num_pages = s->num_pages;
   a->k = k;
+  a->tile_g = TILE_G;
   for (int b = 0; b < s->batch; ++b) a->lens[b] = s->seq_lens_host[b];
 }
 
-int decode_tiles(int32_t L, int32_t k) {
+int decode_tiles(int32_t L, int32_t k, int32_t tg) {
   int64_t G = groups_of(L);
-  return G <= k ? 1 : (int)((G + TILE_G - 1) / TILE_G);
+  return G <= k ? 1 : (int)((G + tg - 1) / tg);
+}
+
+// Pooled groups per decode scoring tile: the largest of 8192, 4096, 2048 that
+// gives at least one tile per CU, keeping every sequence within the tiles
+// per sequence the selection handles.  The tile count does not depend on k
+// (every tile holds more than MAX_K groups), so the workspace query and the
+// call agree.
+int32_t decode_tile_g(const isa_seqs* s) {
+  constexpr int N_CU = 256;
+  int32_t tg = TILE_G;
+  for (;;) {
+    int nt = 0;
+    for (int b = 0; b < s->batch; ++b) nt += decode_tiles(s->seq_lens_host[b], MAX_K, tg);
+    if (nt >= N_CU || tg <= TILE_G_MIN) return tg;
+    const int32_t half = tg / 2;
+    for (int b = 0; b < s->batch; ++b)
+      if (decode_tiles(s->seq_lens_host[b], MAX_K, half) > TILE_MAX_PER_SEQ) return tg;
+    tg = half;
+  }
 }
 
 int pool_tiles(int32_t L) { return (int)((groups_of(L) + POOL_TILE_G - 1) / POOL_TILE_G); }
@@ -49,8 +69,9 @@ struct DecodeLayout {
 };
 DecodeLayout decode_layout(const isa_seqs* s, int32_t k) {
   DecodeLayout d;
+  const int32_t tg = decode_tile_g(s);
   int nt = 0;
-  for (int b = 0; b < s->batch; ++b) nt += decode_tiles(s->seq_lens_host[b], k);
+  for (int b = 0; b < s->batch; ++b) nt += decode_tiles(s->seq_lens_host[b], k, tg);
   d.tile_meta = HDR;
   d.tile_pairs = d.tile_meta + up256((size_t)nt * 8);
   d.tile_list = d.tile_pairs + up256((size_t)nt * PAIR_CAP * 4);
@@ -203,10 +224,11 @@ isa_status isa_indexer_topk(const int8_t* q, const int8_t* head_w, const int8_t*
   if (ws_bytes < d.total) return ISA_ERR_WORKSPACE;
   BatchArgs a;
   fill_batch(s, &a, k);
+  a.tile_g = decode_tile_g(s);
   int t = 0;
   for (int b = 0; b < s->batch; ++b) {
     a.tile_start[b] = t;
-    t += decode_tiles(s->seq_lens_host[b], k);
+    t += decode_tiles(s->seq_lens_host[b], k, a.tile_g);
   }
   a.tile_start[s->batch] = t;
   char* base = (char*)ws;

@@ -14,7 +14,8 @@
 // than the streaming itself; the kernel boundary gives coherence for free).
 //
 // k_indexer_score: one workgroup per work tile of 8192 pooled groups (128
-// pages) of one sequence, one workgroup per CU.  Its sixteen waves stream the
+// pages) of one sequence, one workgroup per CU; a batch that would make fewer
+// tiles than CUs uses tiles of 4096 or 2048 groups.  Its sixteen waves stream the
 // tile's int8 keys straight from HBM into v_mfma_i32_32x32x32_i8 operands --
 // the 32 indexer heads are M (the query stays in registers), 32 groups are N,
 // four MFMAs span the 128 channels, each lane loading 64 contiguous bytes of
@@ -72,8 +73,9 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
   const int L = a.lens[b];
   const int G = (L + GROUP - 1) / GROUP;
   const uint32_t K = (uint32_t)a.k;
-  const int g0 = (tile - a.tile_start[b]) * TILE_G;
-  const int gN = min(G - g0, TILE_G);
+  const int tg = a.tile_g;  // groups per tile of this call (2048 .. 8192)
+  const int g0 = (tile - a.tile_start[b]) * tg;
+  const int gN = min(G - g0, tg);
   const bool dense = G <= (int)K;
 
   if (dense && P.scores_out == nullptr) {  // at most k groups: select them all
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
 
   for (int i = tid; i < NBINS; i += DEC_THREADS) hist[i] = 0;
   if (tid == 0) chunk_ctr = 2 * (DEC_THREADS / 64);
-  if (tid < TILE_G / PAGE_GRP) {
+  if (tid < tg / PAGE_GRP) {
     int j = (g0 / PAGE_GRP) + tid;
     pages[tid] = (tid * PAGE_GRP < gN) ? phys_page(P.bt, a.max_pages, a.num_pages, b, j, P.err) : -1;
   }
@@ -115,16 +117,16 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
   __syncthreads();
 
   // ---- stream the tile: waves take 32-group chunks from an LDS counter ----
-  constexpr int NCH = TILE_G / 32;
+  const int nch = tg / 32;  // chunks of the tile (at least 2 per wave)
   constexpr int NW = DEC_THREADS / 64;
   const int8_t* kbase = P.pooled + (lane >> 5) * 64;
   // Loads are unconditional (a group past the end, or on a page outside the
   // pool, reads row 0 and is zeroed by its mask), so the compiler waits for
   // exactly the chunk it consumes.
   auto load_chunk = [&](int c, v4i (&kb)[4], int& mask) {
-    const int gl = min(c, NCH - 1) * 32 + (lane & 31);
+    const int gl = min(c, nch - 1) * 32 + (lane & 31);
     const int pg = pages[gl / PAGE_GRP];
-    const bool ok = c < NCH && gl < gN && pg >= 0;
+    const bool ok = c < nch && gl < gN && pg >= 0;
     mask = ok ? -1 : 0;
     const size_t row = ok ? (size_t)pg * PAGE_GRP + (gl % PAGE_GRP) : 0;
     const v4i* p = reinterpret_cast<const v4i*>(kbase + row * IDX_DIM);
@@ -167,14 +169,14 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
   load_chunk(cB, bB, mB);
   __builtin_amdgcn_sched_barrier(0);
   for (;;) {
-    if (cA >= NCH) break;
+    if (cA >= nch) break;
     {
       const int nA = grab();
       compute(cA, bA, mA);
       cA = nA;
       load_chunk(cA, bA, mA);
     }
-    if (cB >= NCH) break;
+    if (cB >= nch) break;
     {
       const int nB = grab();
       compute(cB, bB, mB);
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
   // gives, for every bin, the candidates and the nonzero bins above it; the
   // kept bins (>= the boundary) are a prefix of that order, so these are also
   // their emission offsets and (bin, count) pair positions.
-  constexpr int PER = TILE_G / DEC_THREADS;
+  constexpr int PER = TILE_G / DEC_THREADS;  // scores per thread of the largest tile
   static_assert(NBINS == 2 * DEC_THREADS, "two bins per thread");
   static_assert(TILE_G < 65536 && NBINS < 65536, "counts and nonzero bins share one word");
   const int hb = NBINS - 2 * tid;
@@ -251,6 +253,7 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     int e = tid + j * DEC_THREADS;
+    if (e >= tg) break;  // uniform
     uint32_t s = sc[e];
     if (s == INVALID_SCORE) continue;
     int bin = score_bin(s);

@@ -46,6 +46,7 @@ struct BatchArgs {
   int32_t max_pages;
   int32_t num_pages;
   int32_t k;
+  int32_t tile_g;  // pooled groups per decode scoring tile (2048, 4096 or 8192)
   int32_t lens[ISA_MAX_BATCH];
   int32_t tile_start[ISA_MAX_BATCH + 1];  // first work tile of each sequence
 };

@@ -7,7 +7,8 @@
 
 namespace isa {
 
-constexpr int TILE_G = 8192;  // pooled groups per decode work tile (128 pages)
+constexpr int TILE_G = 8192;      // pooled groups of the largest decode work tile (128 pages); list stride
+constexpr int TILE_G_MIN = 2048;  // smallest tile, for batches that would not fill the chip
 constexpr int TILE_MAX_PER_SEQ = (ISA_MAX_SEQ_LEN / GROUP + TILE_G - 1) / TILE_G;
 
 constexpr int PAIR_CAP = NBINS;  // (bin, count) pairs a decode tile can emit

@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from synth.configs import GROUP, SM_SCALE, TOPK_GROUPS, workload
+from synth.configs import GROUP, SM_SCALE, TOPK_GROUPS, custom, workload
 
 import harness as H
 
@@ -64,6 +64,25 @@ def _decode_full(i: int, share_layers: int = 0):
         _index_share_full(db, idx, cnt, idx_d, cnt_d, ref_att, share_layers)
         _fp8_full(db, idx, cnt, idx_d, cnt_d)
     H.log(f"{wl.name}: done")
+
+
+def test_decode_tiles_of_4096_groups():
+    """A batch that makes fewer scoring tiles than CUs at 8192 groups per tile
+    and enough at 4096 (8 x 600,000 tokens: 152 tiles of 8192, 296 of 4096), so
+    the scoring runs with 4096-group tiles: every score and every selected id
+    bit-exact against the oracle, with and without the score output."""
+    wl = custom("tile4096", 23, [600000] * 8, paged_random=True)
+    B = wl.batch
+    db = H.make_batch(wl, with_latent=False)
+    H.run_pool(db)
+    idx, cnt, sc, _ = H.run_topk(db, with_scores=True)
+    idx2, cnt2, _, _ = H.run_topk(db, with_scores=False)
+    assert np.array_equal(idx, idx2) and np.array_equal(cnt, cnt2), "selection differs with the score output"
+    refs = oracle.map_rows(lambda b: H.oracle_scores_for(db, b), range(B))
+    for b in range(B):
+        G = wl.groups(b)
+        assert np.array_equal(sc[b, :G].astype(np.int64), refs[b]), f"scores of sequence {b}"
+        H.check_topk_row(refs[b], TOPK_GROUPS, idx[b], int(cnt[b]))
 
 
 def _fp8_full(db, idx, cnt, idx_d, cnt_d):
