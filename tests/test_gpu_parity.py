@@ -445,6 +445,31 @@ def test_prefill_scores_topk_attention():
         H.attention_tolerance(out[i], ref, lse[i], ref_lse)
 
 
+@pytest.mark.parametrize("L,qpos", [(77, [0, 3, 4, 40, 76]), (130, [129, 64, 1])], ids=["L77", "L130"])
+def test_prefill_scores_short_sequence(L, qpos):
+    """Prefill scores of a sequence shorter than one 32-group key block, or
+    just over it: the blocks past the range are fetched and discarded, and the
+    last query pair is finished after the block loop."""
+    m = H.isa()
+    wl = custom("prefill_short", 37, [L], kind="prefill", q_pos=qpos)
+    db = H.make_batch(wl, with_latent=False)
+    H.run_pool(db)
+    Q, G = wl.rows, wl.groups(0)
+    qh, hwh = wl.q_idx(), wl.head_w()
+    sc = torch.full((Q, G + 4), -7, dtype=torch.int32, device="cuda")
+    ws = m.alloc_workspace(256)
+    m.isa_indexer_prefill_scores(torch.from_numpy(qh).cuda(), torch.from_numpy(hwh).cuda(),
+                                 torch.from_numpy(wl.row_pos()).cuda(), Q, db.pooled, db.seqs, sc, G + 4, ws)
+    torch.cuda.synchronize()
+    assert m.isa_device_error(ws) == 0
+    S = sc.cpu().numpy()
+    k8 = H.pooled_logical(db, 0)
+    for i in range(Q):
+        ref = oracle.prefill_scores(qh[i], hwh[i], int(qpos[i]), k8)
+        assert np.array_equal(S[i, :G].astype(np.int64), ref), f"query {i} (pos {qpos[i]})"
+        assert np.all(S[i, G:] == -7), "columns beyond the sequence were written"
+
+
 def test_paging_is_invisible():
     """The same logical data at two physical placements gives bit-identical outputs."""
     lens = [9000, 3001, 20000]
