@@ -33,9 +33,12 @@
 //  * Every wave then accumulates O[64 heads x its 64 channels] += P V^T with
 //    v_mfma_f32_16x16x32_f16 (heads = M, channels = N, the 32 tokens = K).
 // Two workgroup barriers per tile, both LDS-only; V is double-buffered.
+// A launch of at most 128 (row, split) units runs two workgroups per unit,
+// each with 32 of the heads (the same tile loads, half the MFMA and softmax
+// work), so that it fills the chip.
 // With one split the workgroup normalises and writes the output; otherwise it
-// writes its unnormalised partial (O, reference, sum) and k_mla_combine merges
-// the splits by log-sum-exp weights.
+// writes its normalised partial (O / l in fp16, with the reference and sum in
+// fp32) and k_mla_combine merges the splits by log-sum-exp weights.
 #include <type_traits>
 
 #include "isa_launch.hpp"
