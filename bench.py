@@ -549,6 +549,8 @@ def main():
     ap.add_argument("--traffic-run", action="store_true", help="workload for the rocprofv3 counter passes")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the prefill scoring measurement (for profiling that kernel alone)")
+    ap.add_argument("--decode-workload", type=int, default=None, metavar="N",
+                    help="only the decode steps of workload N (0, 1, 2 or 4), e.g. to profile a secondary line")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_k_indexer_score_*.json from two counter CSVs (no GPU)")
     args = ap.parse_args()
@@ -572,6 +574,18 @@ def main():
     import long_context_sparse_indexpool_amd as m  # noqa: F401  (fails loudly when libisa.so is missing)
     if args.prefill_only:
         print(json.dumps({"prefill_scores": bench_prefill(args)}), flush=True)
+        return
+    if args.decode_workload is not None:
+        w = workload(args.decode_workload)
+        assert w.kind == "decode", "--decode-workload takes a decode workload"
+        d = Decode(w, 2, 4)
+        s = d.time_steps(args.steps, args.warmup)
+        tk, ta = d.time_kernels(10)
+        print(json.dumps({w.name: {"steps_per_s": round(1 / s, 1), "ms_per_step": round(s * 1e3, 4),
+                                   "achieved_hbm_GBps": round(d.bytes_step / s / 1e9, 1),
+                                   "indexer_us": round(tk * 1e6, 2), "sparse_mla_us": round(ta * 1e6, 2)}}),
+              flush=True)
+        d.free()
         return
 
     wl = workload(2)
