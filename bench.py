@@ -30,6 +30,7 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 METRIC = "sparse-attn decode steps/s at 1M ctx (top-2048) + achieved HBM GB/s"
 HBM_PEAK_GBPS = 8000.0
 INT8_PEAK_TOPS = 5000.0
+BF16_PEAK_TFLOPS = 2500.0
 N_POOL_COPIES = 4
 N_QSETS = 16
 KERNEL_SOURCES = {
@@ -387,16 +388,18 @@ def oracle_step_time(dec, min_s=10.0, budget_s=25.0):
 
 
 def bench_prefill(args):
-    """Prefill indexer scores of 2048 queries over 262,144 pooled groups (int8 MFMA)."""
+    """Prefill chunk of 2048 queries at the end of one 2^20-token sequence: indexer
+    scores over 262,144 pooled groups (int8 MFMA), the selection over the score
+    rows, and every row's attention over its selection at its own position."""
     import numpy as np
     import torch
 
     import harness as H
     import long_context_sparse_indexpool_amd as m
-    from synth.configs import workload
+    from synth.configs import SM_SCALE, workload
 
     wl = workload(3)
-    db = H.make_batch(wl, with_keys=True, with_latent=False, keep_host=False)
+    db = H.make_batch(wl, with_keys=True, with_latent=True, keep_host=False)
     H.run_pool(db)
     del db.keys
     Q = wl.rows
@@ -431,10 +434,41 @@ def bench_prefill(args):
     e1.record()
     torch.cuda.synchronize()
     t_sel = e0.elapsed_time(e1) / 3 * 1e-3
+    # attention: every query row over its selection, token-causal at its position
+    qa = torch.from_numpy(wl.q_attn(0, Q).view(np.int16)).cuda()
+    out = torch.empty((Q, 64, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((Q, 64), dtype=torch.float32, device="cuda")
+    rseq = torch.zeros(Q, dtype=torch.int32, device="cuda")
+    rpos = qpos.to(torch.int32)
+    wsa = m.alloc_workspace(m.workspace_size(m.ISA_OP_SPARSE_MLA, db.seqs, Q))
+    run_att = lambda: m.isa_sparse_mla_decode(qa, db.latent, db.seqs, rseq, rpos, Q, idx, cnt, 512, SM_SCALE, out,
+                                              lse, wsa)
+    run_att()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(3):
+        run_att()
+    e1.record()
+    torch.cuda.synchronize()
+    t_att = e0.elapsed_time(e1) / 3 * 1e-3
+    pos = wl.row_pos()
+    cnt_h = cnt.cpu().numpy().astype(np.int64)
+    # tokens attended per row: the selected groups' tokens up to the row's position (selected groups
+    # lie at or before the row's own group, so only that group can be partly visible)
+    idx_h = idx.cpu().numpy()
+    toks = 0
+    for r in range(Q):
+        g = idx_h[r, : cnt_h[r]].astype(np.int64)
+        toks += int(np.minimum(4, pos[r] + 1 - 4 * g).clip(0).sum())
+    att_bytes = toks * 1024 + Q * (64 * 512 * 2 + 64 * 512 * 4 + 64 * 4)
+    att_flops = 4 * 64 * 512 * toks
     res = {"workload": wl.name, "ms": round(t * 1e3, 4), "useful_TOPS": round(useful_ops / t / 1e12, 1),
            "dense_TOPS": round(dense_ops / t / 1e12, 1), "frac_int8_peak": round(dense_ops / t / 1e12 / INT8_PEAK_TOPS, 4),
-           "select_ms": round(t_sel * 1e3, 4), "select_GBps": round(2 * Q * G * 4 / t_sel / 1e9, 1)}
-    del sc, db
+           "select_ms": round(t_sel * 1e3, 4), "select_GBps": round(2 * Q * G * 4 / t_sel / 1e9, 1),
+           "attention_ms": round(t_att * 1e3, 4), "attention_tokens": toks,
+           "attention_GBps": round(att_bytes / t_att / 1e9, 1),
+           "attention_frac_bf16_peak": round(att_flops / t_att / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    del sc, db, out, qa
     torch.cuda.empty_cache()
     return res
 
