@@ -601,8 +601,8 @@ isa_status launch_sparse_mla(const BatchArgs& a, const MlaPlan& p, int32_t n_lay
 #define ISA_MLA_LAUNCH(FP8_, MULTI_)                                                                         \
   (hsplit ? launch_timed(ISA_TIMER_MLA_SPLIT, k_mla_split<FP8_, MULTI_, ATT_HEADS / 2>, grid, block, stream, a, P) \
           : launch_timed(ISA_TIMER_MLA_SPLIT, k_mla_split<FP8_, MULTI_, ATT_HEADS>, grid, block, stream, a, P))
-  if (lat_scale)
-    e = n_layers > 1 ? ISA_MLA_LAUNCH(true, true) : ISA_MLA_LAUNCH(true, false);
+  if (lat_scale)  // the FP8 cache is attended one layer per call
+    e = n_layers == 1 ? ISA_MLA_LAUNCH(true, false) : hipErrorInvalidValue;
   else
     e = n_layers > 1 ? ISA_MLA_LAUNCH(false, true) : ISA_MLA_LAUNCH(false, false);
 #undef ISA_MLA_LAUNCH
