@@ -3,7 +3,7 @@ benchmark times (whole batch per call, scores not requested), against the CPU
 oracle.
 
 Decode workloads (8192 tokens; 64 x 131,072; 8 x 1,048,576; 32 ragged paged
-sequences up to 2^20): pooled keys of every sequence within 1 LSB, every score
+sequences up to 2^20; 256 sequences, one of the maximum 2^22 tokens): pooled keys of every sequence within 1 LSB, every score
 bit-exact (from a second call that also writes the scores), every selected id
 bit-exact, and attention within tolerance for every row.  At 8 x 1,048,576 also
 IndexShare: four layers' attention over the same selection in one call, every
@@ -24,8 +24,7 @@ import harness as H
 pytestmark = pytest.mark.gpu
 
 
-def _decode_full(i: int, share_layers: int = 0):
-    wl = workload(i)
+def _decode_full(wl, share_layers: int = 0):
     B = wl.batch
     H.log(f"{wl.name}: generating inputs")
     db = H.make_batch(wl, keep_host=True)
@@ -149,19 +148,33 @@ def _index_share_full(db, idx, cnt, idx_d, cnt_d, ref0, n):
 
 
 def test_full_decode_b1_L8192():
-    _decode_full(0)
+    _decode_full(workload(0))
 
 
 def test_full_decode_b64_L131072():
-    _decode_full(1)
+    _decode_full(workload(1))
 
 
 def test_full_decode_b8_L1048576():
-    _decode_full(2, share_layers=4)
+    _decode_full(workload(2), share_layers=4)
 
 
 def test_full_ragged_paged_b32():
-    _decode_full(4)
+    _decode_full(workload(4))
+
+
+def test_full_decode_max_batch_and_length():
+    """The largest sizes the library accepts, in one call: ISA_MAX_BATCH = 256
+    sequences, one of them ISA_MAX_SEQ_LEN = 2^22 tokens (128 scoring tiles of
+    8192 groups, the per-sequence maximum) and 255 ragged ones of 1..20,000
+    tokens, pages placed at random; one attention split per row at this batch.
+    Pooled keys, every score and selected id, and every row's attention
+    against the oracle."""
+    m = H.isa()
+    assert m.MAX_BATCH == 256 and m.MAX_SEQ_LEN == 1 << 22
+    rng = np.random.default_rng(31)
+    lens = [m.MAX_SEQ_LEN] + [int(x) for x in rng.integers(1, 20001, m.MAX_BATCH - 1)]
+    _decode_full(custom("max_batch_and_length", 31, lens, paged_random=True))
 
 
 def test_full_prefill_q2048_L1048576():
