@@ -187,20 +187,22 @@ def test_attention_parity_ragged(ragged_batch):
     H.log(f"attention worst max-abs {max(r[0] for r in res):.2e} rel {max(r[1] for r in res):.2e}")
 
 
-@pytest.mark.parametrize("lens", [[9000, 3000, 20000, 700, 131075], [20000]], ids=["b5_64heads", "b1_32heads"])
-def test_index_share_layers(lens):
-    """Four layers attending over one selection in one call: every layer
-    against the oracle with its own query and latent cache; one layer through
-    the shared call is bit-identical to the single-layer call.  Five rows make
-    more than 128 (layer, row, split) units (64 heads per workgroup); one row
-    makes fewer (the heads split over two workgroups)."""
+@pytest.mark.parametrize("lens,n", [([9000, 3000, 20000, 700, 131075], 4), ([20000], 4), ([20000, 5000], 8)],
+                         ids=["b5_64heads", "b1_32heads", "b2_8layers"])
+def test_index_share_layers(lens, n):
+    """n layers attending over one selection in one call: every layer against
+    the oracle with its own query and latent cache; one layer through the
+    shared call is bit-identical to the single-layer call.  Five rows make more
+    than 128 (layer, row, split) units (64 heads per workgroup); one row makes
+    fewer (the heads split over two workgroups); two rows take the most layers
+    a call accepts (ISA_MAX_LAYERS = 8)."""
+    assert n <= H.isa().ISA_MAX_LAYERS
     from synth.configs import layer_flip_view
     wl = custom("index_share", 17, lens, paged_random=True)
     db = H.make_batch(wl)
     H.run_pool(db)
     idx, cnt, _, _ = H.run_topk(db, with_scores=False)
     idx_d, cnt_d = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
-    n = 4
     pools = H.layer_latents(db, n)
     res = H.run_attention_shared(db, idx_d, cnt_d, 512, pools)
     lat, to = db.host["latent"], wl.token_offsets
