@@ -39,8 +39,13 @@
  *    on the host.  Outputs are valid once the stream reaches the call.
  *  - Workspace: `ws` [dev] of at least isa_workspace_size(...) bytes, zero-
  *    filled once before its first use (isa_workspace_init or any zero fill).
- *    Calls keep the parts they use zeroed between calls.  Calls that share a
- *    workspace must be ordered on one stream.
+ *    Layout, the same for every call: the error word in the first 256 bytes,
+ *    then a fixed 2 MiB region (ISA_MAX_BATCH x 2048 words of per-sequence
+ *    candidate histograms) that only isa_indexer_topk uses and leaves zero
+ *    after every call, then the call's own scratch, which it writes before it
+ *    reads.  So one workspace may serve calls of any batch shape and be shared
+ *    by different calls, provided it is as large as each call asks; calls that
+ *    share a workspace must be ordered on one stream.
  *  - Errors: argument errors are reported synchronously by the return code
  *    before anything is enqueued.  Errors that depend on device data (a page
  *    id outside the pool, a head weight outside [0,64], a score above
@@ -72,7 +77,8 @@ typedef enum {
 #define ISA_DERR_PAGE_OOB 0x1u       /* block-table entry outside [0, num_pages) */
 #define ISA_DERR_HEADW_RANGE 0x2u    /* indexer head weight outside [0, 64] */
 #define ISA_DERR_SCORE_OVERFLOW 0x4u /* an indexer score above INT32_MAX */
-#define ISA_DERR_ROW_RANGE 0x8u      /* row sequence / position or a group id outside its sequence */
+#define ISA_DERR_ROW_RANGE 0x8u      /* a row's sequence, position or selection count, a selected group
+                                        id, or a prefill query position outside its sequence */
 #define ISA_DERR_NONFINITE 0x10u     /* non-finite pooled amax (NaN / Inf indexer keys) */
 
 #define ISA_MAX_BATCH 256          /* sequences per call */
@@ -174,6 +180,11 @@ isa_status isa_indexpool(const uint16_t* keys, const float* w4, const isa_seqs* 
  *   out_idx   [dev] int32 [rows, k]: selected group ids in ascending order, then -1
  *   out_count [dev] int32 [rows]: number selected
  * k: 1..512 (512 = 2048 tokens).
+ * Device errors (decode mode): ISA_DERR_HEADW_RANGE for a head weight outside
+ * [0, 64]; ISA_DERR_SCORE_OVERFLOW for a score above INT32_MAX (scores are
+ * accumulated in 32-bit unsigned arithmetic, which holds the largest possible
+ * score, 4,228,120,576, so the selection still ranks it exactly; scores_out
+ * holds it wrapped to a negative int32); ISA_DERR_PAGE_OOB.
  */
 isa_status isa_indexer_topk(const int8_t* q, const int8_t* head_w, const int8_t* pooled, const isa_seqs* s,
                             const int32_t* scores_in, int32_t rows, int32_t ld_scores, int32_t k,
@@ -187,7 +198,7 @@ isa_status isa_indexer_topk(const int8_t* q, const int8_t* head_w, const int8_t*
  * Absorbed form: keys = values = the 512-d latent row; no rotary part.
  *   q        [dev] bf16 bits [rows, 64, 512]
  *   latent   [dev] bf16 bits [num_pages, 256, 512], token-paged; values must be
- *            finite with magnitude below 65504
+ *            finite with magnitude below 65504 (they are converted to fp16)
  *   row_seq  [dev] int32 [rows] sequence of each row, or NULL: row r is sequence r
  *   row_pos  [dev] int32 [rows] last visible token, or NULL: L_seq - 1
  *   idx, count [dev] from isa_indexer_topk ([rows, k], [rows])
@@ -197,10 +208,18 @@ isa_status isa_indexer_topk(const int8_t* q, const int8_t* head_w, const int8_t*
  *   lse      [dev] fp32 [rows, 64] natural log-sum-exp of the scaled scores, or NULL
  * A row with no visible token gets out = 0 and lse = -inf.
  * Arithmetic: bf16 products with fp32 accumulation for q.c; fp32 softmax;
- * probabilities rounded to fp16 and latents converted exactly to fp16 for the
- * weighted sum, fp32 accumulation.  When a row's selection is split over
- * several workgroups, each split's normalised output is held in fp16 (a convex
- * combination of latent rows) and the splits are merged with fp32 weights.
+ * latents converted exactly to fp16 for the weighted sum, each probability
+ * carried as two fp16 terms (p_hi = fp16(p), p_lo = fp16(p - p_hi), about
+ * 2^-22 relative together), fp32 accumulation.  When a row's selection is
+ * split over several workgroups, each split's normalised output (a convex
+ * combination of latent rows) is held in fp16 when all of the workgroup's
+ * values are below 16 in magnitude, else in fp32, and the splits are merged
+ * with fp32 weights.  Accuracy against exact arithmetic: for latent values up
+ * to 1024 in magnitude every output element is within 2e-2 (the rounding of
+ * fp32 accumulation grows with the largest value beyond that) and lse within
+ * 1e-3.  Device errors: ISA_DERR_ROW_RANGE for a bad row sequence, position,
+ * count or group id (the row attends only to valid groups; none: out = 0),
+ * ISA_DERR_PAGE_OOB.
  */
 isa_status isa_sparse_mla_decode(const uint16_t* q, const uint16_t* latent, const isa_seqs* s,
                                  const int32_t* row_seq, const int32_t* row_pos, int32_t rows,
@@ -233,10 +252,15 @@ isa_status isa_sparse_mla_decode_shared(int32_t n_layers, const uint16_t* const*
  * against all its pooled groups -- a dense int8 contraction ([REMIO]: the
  * indexer scores the whole retained history).
  *   q       [dev] int8 [Q, 32, 128]; head_w [dev] int8 [Q, 32] in [0, 64]
- *   q_pos   [dev] int32 [Q] absolute token position of each query, < L
+ *   q_pos   [dev] int32 [Q] absolute token position of each query, in [0, L)
  *   scores  [dev] int32 [Q, ld_scores], ld_scores >= ceil(L/4): the decode score
  *           formula for groups g <= q_pos/4 (the query's own group included) and
- *           -1 for later groups; columns >= ceil(L/4) are left untouched.
+ *           -1 for later groups and for columns ceil(L/4) .. ld_scores-1, so a
+ *           whole row can go to isa_indexer_topk's precomputed mode.
+ * Device errors: ISA_DERR_HEADW_RANGE for a head weight outside [0, 64];
+ * ISA_DERR_ROW_RANGE for a position outside [0, L) (that query's row is all
+ * -1); ISA_DERR_SCORE_OVERFLOW for a score above INT32_MAX (stored as a
+ * negative number, so the row top-k would skip it); ISA_DERR_PAGE_OOB.
  */
 isa_status isa_indexer_prefill_scores(const int8_t* q, const int8_t* head_w, const int32_t* q_pos, int32_t Q,
                                       const int8_t* pooled, const isa_seqs* s, int32_t* scores,
@@ -290,7 +314,7 @@ isa_status isa_append_token(const uint16_t* key_new, const uint16_t* latent_new,
  * latent value of token t is row_scales[t] * decode(codes[t]).  Arithmetic:
  * codes decoded exactly to fp16, the query converted to fp16, fp16 products with
  * fp32 accumulation; the row scale multiplies the fp32 score and is folded into
- * the fp16 probability of the P.V product.  Row scales must be positive, finite
+ * the probability of the P.V product (carried as two fp16 terms, as above).  Row scales must be positive, finite
  * and at most 128.  Arguments, results and errors otherwise as
  * isa_sparse_mla_decode (same workspace size).
  */

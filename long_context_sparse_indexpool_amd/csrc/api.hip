@@ -4,12 +4,23 @@
 // except isa_device_error, which reads the error word on request.
 #include <string.h>
 
+#include <mutex>
+
 #include "isa_launch.hpp"
 
 namespace isa {
 namespace {
 
+// Workspace layout shared by every call: the sticky error word in the first
+// 256 bytes, then the per-sequence candidate histograms of the decode top-k
+// (ISA_MAX_BATCH x NBINS words, zero between calls), then the call's own
+// scratch.  The histograms sit at a fixed offset, so a workspace reused for a
+// different batch shape, or shared with another call, never places them on
+// data an earlier call left behind; no call writes that region except the
+// top-k, which leaves it zero again.
 constexpr size_t HDR = 256;
+constexpr size_t HIST_BYTES = (size_t)ISA_MAX_BATCH * NBINS * 4;
+constexpr size_t SCR0 = HDR + HIST_BYTES;
 
 inline size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -49,7 +60,7 @@ int decode_tiles(int32_t L, int32_t k, int32_t tg) {
 // (every tile holds more than MAX_K groups), so the workspace query and the
 // call agree.
 int32_t decode_tile_g(const isa_seqs* s) {
-  constexpr int N_CU = 256;
+  const int N_CU = device_info().n_cu;
   int32_t tg = TILE_G;
   for (;;) {
     int nt = 0;
@@ -72,25 +83,25 @@ DecodeLayout decode_layout(const isa_seqs* s, int32_t k) {
   const int32_t tg = decode_tile_g(s);
   int nt = 0;
   for (int b = 0; b < s->batch; ++b) nt += decode_tiles(s->seq_lens_host[b], k, tg);
-  d.tile_meta = HDR;
+  d.seq_hist = HDR;
+  d.tile_meta = SCR0;
   d.tile_pairs = d.tile_meta + up256((size_t)nt * 8);
   d.tile_list = d.tile_pairs + up256((size_t)nt * PAIR_CAP * 4);
-  d.seq_hist = d.tile_list + up256((size_t)nt * TILE_G * 8);
-  d.total = d.seq_hist + up256((size_t)s->batch * NBINS * 4);
+  d.total = d.tile_list + up256((size_t)nt * TILE_G * 8);
   return d;
 }
 
 size_t pool_ws(const isa_seqs* s) {
   int nt = 0;
   for (int b = 0; b < s->batch; ++b) nt += pool_tiles(s->seq_lens_host[b]);
-  return HDR + up256((size_t)nt * 4);  // per-tile maxima of the dynamic scale
+  return SCR0 + up256((size_t)nt * 4);  // per-tile maxima of the dynamic scale
 }
 
 size_t mla_ws(int32_t rows, int32_t k, int32_t layers) {
   MlaPlan p = plan_mla(rows, k, layers);
   if (p.splits <= 1) return HDR;
-  return HDR + up256((size_t)layers * rows * p.splits * ATT_HEADS * LAT_DIM * 2) +
-         up256((size_t)layers * rows * p.splits * ATT_HEADS * 2 * 4);
+  return SCR0 + up256((size_t)layers * rows * p.splits * ATT_HEADS * LAT_DIM * 4) +
+         up256((size_t)layers * rows * p.splits * ATT_HEADS * 4 * 4);
 }
 
 __global__ void k_fill_zero(uint4* p, size_t n16) {
@@ -111,6 +122,30 @@ isa_status launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
 }
 
 KernelTimer g_timer[3];
+
+DevInfo device_info() {
+  constexpr int MAX_DEV = 64;
+  static std::mutex mu;
+  static DevInfo cache[MAX_DEV];
+  static bool known[MAX_DEV];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEV) dev = -1;
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= 0 && known[dev]) return cache[dev];
+  // an MI355X as a whole: the values used when a query fails
+  DevInfo d{256, 8};
+  int v = 0;
+  if (dev >= 0 && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+    d.n_cu = v;
+  v = 0;
+  if (dev >= 0 && hipDeviceGetAttribute(&v, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess && v > 0) d.n_xcd = v;
+  if (d.n_xcd > d.n_cu) d.n_xcd = 1;
+  if (dev >= 0) {
+    cache[dev] = d;
+    known[dev] = true;
+  }
+  return d;
+}
 
 }  // namespace isa
 
@@ -196,7 +231,7 @@ isa_status isa_indexpool(const uint16_t* keys, const float* w4, const isa_seqs* 
     t += pool_tiles(s->seq_lens_host[b]);
   }
   a.tile_start[s->batch] = t;
-  float* amax_part = reinterpret_cast<float*>((char*)ws + HDR);
+  float* amax_part = reinterpret_cast<float*>((char*)ws + SCR0);
   return launch_indexpool(a, keys, w4, s->block_table, scales, pooled, flags == ISA_SCALE_DYNAMIC, amax_part,
                           (uint32_t*)ws, (hipStream_t)stream);
 }
@@ -264,8 +299,8 @@ static isa_status sparse_mla(int32_t n_layers, const uint16_t* const* q, const v
   BatchArgs a;
   fill_batch(s, &a, k);
   char* base = (char*)ws;
-  MlaWs w{(uint32_t*)base, (_Float16*)(base + HDR),
-          (float*)(base + HDR + up256((size_t)n_layers * rows * p.splits * ATT_HEADS * LAT_DIM * 2))};
+  MlaWs w{(uint32_t*)base, base + SCR0,
+          (float*)(base + SCR0 + up256((size_t)n_layers * rows * p.splits * ATT_HEADS * LAT_DIM * 4))};
   return launch_sparse_mla(a, p, n_layers, q, latent, lat_scale, s->block_table, row_seq, row_pos, idx, count, k,
                            sm_scale, out, lse, w, (hipStream_t)stream);
 }

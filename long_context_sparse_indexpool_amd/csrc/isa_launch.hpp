@@ -7,6 +7,17 @@
 
 namespace isa {
 
+// Compute units and XCDs (chiplets with their own L2) of the calling thread's
+// current device, queried once per device and cached.  Workgroups are
+// dispatched round-robin over the XCDs, which the attention and prefill
+// launches use to place workgroups that share data on one L2; the decode
+// scoring tile size follows the CU count.
+struct DevInfo {
+  int n_cu;
+  int n_xcd;
+};
+DevInfo device_info();
+
 constexpr int TILE_G = 8192;      // pooled groups of the largest decode work tile (128 pages); list stride
 constexpr int TILE_G_MIN = 2048;  // smallest tile, for batches that would not fill the chip
 constexpr int TILE_MAX_PER_SEQ = (ISA_MAX_SEQ_LEN / GROUP + TILE_G - 1) / TILE_G;
@@ -45,8 +56,9 @@ struct MlaPlan {
 };
 struct MlaWs {
   uint32_t* err;
-  _Float16* o_part;  // [layers][rows][splits][64][512] fp16 O / l
-  float* ml_part;   // [layers][rows][splits][64][2]  (running max in log2 units, sum)
+  char* o_part;     // [layers][rows][splits][64] slots of 2 KiB: a head's normalised partial O / l,
+                    // 512 fp16 values (first KiB) or 512 fp32 values
+  float* ml_part;   // [layers][rows][splits][64][4]: reference (log2 units), sum, format (1 = fp32), 0
 };
 MlaPlan plan_mla(int32_t rows, int32_t k, int32_t layers);
 // n_layers (1..ISA_MAX_LAYERS) attentions that share one selection; q, latent,

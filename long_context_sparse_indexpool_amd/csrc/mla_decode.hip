@@ -28,17 +28,24 @@
 //  * Wave w owns the softmax of heads 8w..8w+7: it sums the four channel
 //    groups' partials for its heads over the 32 tokens, keeps the running
 //    reference and sum (base 2; the reference moves only when a head's scores
-//    exceed it by more than 8, so p <= 256 in fp16 and the output rescale is
-//    rare) and writes P in fp16 to LDS.
+//    exceed it by more than 8, so p <= 256 and the output rescale is rare) and
+//    writes P to LDS as two fp16 terms, p_hi = fp16(p) and p_lo = fp16(p - p_hi),
+//    which together carry p to about 2^-22 relative.
 //  * Every wave then accumulates O[64 heads x its 64 channels] += P V^T with
-//    v_mfma_f32_16x16x32_f16 (heads = M, channels = N, the 32 tokens = K).
+//    v_mfma_f32_16x16x32_f16 (heads = M, channels = N, the 32 tokens = K), once
+//    for p_hi and once for p_lo: the weighted sum stays accurate to fp32
+//    accumulation for large latent values, where fp16 probabilities alone
+//    would be off by 2^-11 of the largest value.
 // Two workgroup barriers per tile, both LDS-only; V is double-buffered.
 // A launch of at most 128 (row, split) units runs two workgroups per unit,
 // each with 32 of the heads (the same tile loads, half the MFMA and softmax
 // work), so that it fills the chip.
 // With one split the workgroup normalises and writes the output; otherwise it
-// writes its normalised partial (O / l in fp16, with the reference and sum in
-// fp32) and k_mla_combine merges the splits by log-sum-exp weights.
+// writes its normalised partial O / l with the reference and sum in fp32, and
+// k_mla_combine merges the splits by log-sum-exp weights.  The partial is held
+// in fp16 when every value of the workgroup's partial is below PART_F16_MAX in
+// magnitude (fp16 rounding then moves a value by at most 2^-8), otherwise in
+// fp32; the format is recorded per (split, head) beside the reference and sum.
 #include <type_traits>
 
 #include "isa_launch.hpp"
@@ -61,6 +68,7 @@ constexpr int MAX_GPS = MAX_K; // groups per split held in LDS
 constexpr int BT_LDS = 1024;   // block-table entries of a row staged in LDS (sequences up to 256K tokens;
                                // for longer rows staging costs more than the round trip it saves)
 constexpr int MAX_SPLITS = 32;
+constexpr float PART_F16_MAX = 16.f;  // partials below this magnitude are held in fp16
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -102,14 +110,16 @@ struct MlaPtrs {
   const int32_t* row_pos;
   const int32_t* idx;
   const int32_t* count;
-  _Float16* o_part;  // [layers][rows][splits][64][512] normalised partials O / l
-  float* ml_part;    // [layers][rows][splits][64][2]
+  char* o_part;      // [layers][rows][splits][64] slots of 2 KiB: normalised partial O / l of one
+                     // head, 512 fp16 (first KiB) or 512 fp32 values
+  float* ml_part;    // [layers][rows][splits][64][4]: reference (log2 units), sum, format (1 = fp32), 0
   uint32_t* err;
   int32_t k;
   float c2;  // sm_scale * log2(e)
   int32_t splits;
   int32_t gps;  // groups per split
   int32_t n_units;  // (layer, row, split) units of the launch
+  int32_t n_xcd;    // XCDs the launch's workgroups are dispatched over, round-robin
 };
 
 // FP8 E4M3 codes of 8 channels to fp16 (exact: every E4M3 value is an fp16
@@ -142,9 +152,11 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
   using QOpT = typename std::conditional<FP8, v8h, v8bf>::type;
   __shared__ __attribute__((aligned(16))) _Float16 vt[2][TILE_TOK * V_STRIDE];  // 2 x 33 KiB: fp16 V of a tile, double-buffered
   __shared__ v4f sp[2][4][HB][SP_LANES];                  // 48 KiB (64 heads): partial S^T [half][group][head block][lane]
-  __shared__ _Float16 pb[NH * P_STRIDE];                  // 5 KiB (64 heads): P of the tile [head][token]
+  __shared__ _Float16 pb[NH * P_STRIDE];                  // 5 KiB (64 heads): p_hi of the tile [head][token]
+  __shared__ _Float16 pbl[NH * P_STRIDE];                 // 5 KiB (64 heads): p_lo of the tile
   __shared__ __attribute__((aligned(16))) float alpha_s[NH];
   __shared__ __attribute__((aligned(16))) uint32_t flag_s[8];
+  __shared__ uint32_t big_s;  // a partial value reached PART_F16_MAX: the split's partial is held in fp32
   __shared__ float fin_s[2][NH];
   __shared__ __attribute__((aligned(16))) uint32_t trow[MAX_GPS * GROUP];  // latent row of each token slot, ~0 if not visible
   __shared__ int32_t bt_s[BT_LDS];                        // 4 KiB: the row's block-table entries
@@ -153,9 +165,10 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
   const int cg = wave & 3, th = wave >> 2;   // channels 128cg.., tokens 16th.. of each tile
   int unit = (int)blockIdx.x, hh = 0;  // (layer, row, split) unit and half of the heads
   if constexpr (NH < ATT_HEADS) {
-    const int slot = (int)blockIdx.x / 8;  // dispatch is round-robin over the 8 XCDs
+    const int nx = P.n_xcd;  // dispatch is round-robin over the XCDs
+    const int slot = (int)blockIdx.x / nx;
     hh = slot & 1;
-    unit = (slot >> 1) * 8 + (int)blockIdx.x % 8;
+    unit = (slot >> 1) * nx + (int)blockIdx.x % nx;
     if (unit >= P.n_units) return;  // the whole workgroup
   }
   const int h0 = hh * NH;  // first head of this workgroup
@@ -240,6 +253,7 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
   const int own_h = OWN_HEADS * wave + (lane & 7);
   const int own_tq = lane >> 3;  // tokens 4 own_tq .. +3 of the tile
   if (tid < 8) flag_s[tid] = 0u;  // waves without softmax heads never set theirs
+  if (tid == 0) big_s = 0u;
   lds_barrier();  // token table complete
 
   const int nslot = ng * GROUP;
@@ -357,18 +371,19 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
       if (tq == 0) alpha_s[own_h] = alpha;
       if (lane == 0) flag_s[wave] = moved ? 1u : 0u;
       float ps = 0.f;
-      v4h ph;
+      v4h ph, pl;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float pr = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[i] - m_ref);
         ps += pr;
-        if constexpr (FP8)
-          ph[i] = (_Float16)(pr * st[i]);  // the row scale enters P.V through P
-        else
-          ph[i] = (_Float16)pr;
+        float pw = pr;
+        if constexpr (FP8) pw = pr * st[i];  // the row scale enters P.V through P
+        ph[i] = (_Float16)pw;
+        pl[i] = (_Float16)(pw - (float)ph[i]);  // exact difference, rounded once
       }
       l_run += ps;
       *reinterpret_cast<v4h*>(&pb[own_h * P_STRIDE + 4 * tq]) = ph;
+      *reinterpret_cast<v4h*>(&pbl[own_h * P_STRIDE + 4 * tq]) = pl;
       if constexpr (FP8) sbuf = *scales_of(t + 2);  // refill with tile t + 2, after the latent rows
     }
     lds_barrier();  // P, reference moves complete
@@ -390,20 +405,46 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
         }
       }
     }
-    v8h pv[HB];
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
-      pv[hb] = __builtin_bit_cast(v8h, *reinterpret_cast<const v4i*>(&pb[(hb * 16 + lq) * P_STRIDE + lg * 8]));
     // V operand: lane (lq, lg) gets channel 16nb + lq of tokens 8lg .. 8lg+7
     const _Float16* vr0 = &vtb[vrow(8 * lg + (lq >> 2)) * V_STRIDE + wave * OUT_DIM + 4 * (lq & 3)];
     const _Float16* vr1 = &vtb[vrow(8 * lg + 4 + (lq >> 2)) * V_STRIDE + wave * OUT_DIM + 4 * (lq & 3)];
-#pragma unroll
-    for (int nb = 0; nb < NBLK; ++nb) {
+    auto v_op = [&](int nb) -> v8h {
       const v4s v0 = lds_read_tr16(vr0 + nb * 16), v1 = lds_read_tr16(vr1 + nb * 16);
-      const v8h vv = __builtin_bit_cast(v8h, v4i{__builtin_bit_cast(v2i, v0).x, __builtin_bit_cast(v2i, v0).y,
-                                                  __builtin_bit_cast(v2i, v1).x, __builtin_bit_cast(v2i, v1).y});
+      return __builtin_bit_cast(v8h, v4i{__builtin_bit_cast(v2i, v0).x, __builtin_bit_cast(v2i, v0).y,
+                                         __builtin_bit_cast(v2i, v1).x, __builtin_bit_cast(v2i, v1).y});
+    };
+    auto p_op = [&](const _Float16* buf, int hb) -> v8h {
+      return __builtin_bit_cast(v8h, *reinterpret_cast<const v4i*>(&buf[(hb * 16 + lq) * P_STRIDE + lg * 8]));
+    };
+    if constexpr (HB <= 2) {
+      // all V operands held; each head block's p_hi and p_lo in turn
+      v8h vv[NBLK];
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) o[hb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pv[hb], vv, o[hb][nb], 0, 0, 0);
+      for (int nb = 0; nb < NBLK; ++nb) vv[nb] = v_op(nb);
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        const v8h ph = p_op(pb, hb), pl = p_op(pbl, hb);
+#pragma unroll
+        for (int nb = 0; nb < NBLK; ++nb) o[hb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vv[nb], o[hb][nb], 0, 0, 0);
+#pragma unroll
+        for (int nb = 0; nb < NBLK; ++nb) o[hb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, vv[nb], o[hb][nb], 0, 0, 0);
+      }
+    } else {
+      // 64 heads: registers are short, so a p_hi pass and a p_lo pass, each
+      // holding one P term per head block and reading V again
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        asm volatile("" ::: "memory");  // V is read again in the second pass, not held in registers
+        v8h pv[HB];
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) pv[hb] = p_op(pass ? pbl : pb, hb);
+#pragma unroll
+        for (int nb = 0; nb < NBLK; ++nb) {
+          const v8h vv = v_op(nb);
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb) o[hb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pv[hb], vv, o[hb][nb], 0, 0, 0);
+        }
+      }
     }
   };
 
@@ -471,12 +512,12 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
     if (P.lse[layer] && own_tq == 0 && wave < NSW)
       P.lse[layer][(size_t)r * ATT_HEADS + h0 + own_h] = l_tot > 0.f ? m_ref * LN2 + logf(l_tot) : -INFINITY;
   } else {
-    // the split's normalised output O / l in fp16 (a convex combination of
-    // latent rows, so within their range), staged in LDS -- the V tiles are
-    // free now -- and written with 16-B stores
+    // the split's normalised output O / l (a convex combination of latent
+    // rows, so within their range), in fp16 when every value is below
+    // PART_F16_MAX in magnitude -- staged in LDS (the V tiles are free now) and
+    // written with 16-B stores -- otherwise in fp32 straight from registers
     const size_t part = unit;  // (layer, row, split)
-    _Float16* stage = &vt[0][0];
-    static_assert(2 * TILE_TOK * V_STRIDE >= NH * LAT_DIM, "staging fits in the V tiles");
+    bool big = false;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       float inv[4];
@@ -488,18 +529,45 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
 #pragma unroll
       for (int nb = 0; nb < NBLK; ++nb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          stage[(hb * 16 + 4 * lg + i) * LAT_DIM + d_base + nb * 16 + lq] = (_Float16)(o[hb][nb][i] * inv[i]);
+        for (int i = 0; i < 4; ++i) {
+          o[hb][nb][i] *= inv[i];
+          big |= !(fabsf(o[hb][nb][i]) < PART_F16_MAX);  // NaN counts as large
+        }
     }
+    if (__any(big) && lane == 0) big_s = 1u;
     __syncthreads();
-    v4i* op = reinterpret_cast<v4i*>(P.o_part + (part * ATT_HEADS + h0) * LAT_DIM);
-    constexpr int N16 = NH * LAT_DIM * 2 / 16;
+    const bool f32 = big_s != 0u;  // uniform
+    char* slot = P.o_part + (part * ATT_HEADS + h0) * (LAT_DIM * 4);  // 2 KiB per head
+    if (!f32) {
+      _Float16* stage = &vt[0][0];
+      static_assert(2 * TILE_TOK * V_STRIDE >= NH * LAT_DIM, "staging fits in the V tiles");
 #pragma unroll
-    for (int k = 0; k < N16 / MLA_THREADS; ++k) op[tid + k * MLA_THREADS] = reinterpret_cast<const v4i*>(stage)[tid + k * MLA_THREADS];
+      for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+        for (int nb = 0; nb < NBLK; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            stage[(hb * 16 + 4 * lg + i) * LAT_DIM + d_base + nb * 16 + lq] = (_Float16)o[hb][nb][i];
+      __syncthreads();
+      constexpr int N16 = NH * LAT_DIM * 2 / 16;  // 16-B chunks, 64 per head
+#pragma unroll
+      for (int k = 0; k < N16 / MLA_THREADS; ++k) {
+        const int c = tid + k * MLA_THREADS;
+        *reinterpret_cast<v4i*>(slot + (size_t)(c >> 6) * (LAT_DIM * 4) + (c & 63) * 16) =
+            reinterpret_cast<const v4i*>(stage)[c];
+      }
+    } else {
+      float* base = reinterpret_cast<float*>(slot) + 4 * lg * LAT_DIM + d_base + lq;  // head 4lg, this lane's channel
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int nb = 0; nb < NBLK; ++nb) base[(hb * 16 + i) * LAT_DIM + nb * 16] = o[hb][nb][i];
+    }
     if (own_tq == 0 && wave < NSW) {
-      float* mp = P.ml_part + (part * ATT_HEADS + h0 + own_h) * 2;
-      mp[0] = l_tot > 0.f ? m_ref : -INFINITY;
-      mp[1] = l_tot;
+      float4* mp = reinterpret_cast<float4*>(P.ml_part) + (part * ATT_HEADS + h0 + own_h);
+      *mp = make_float4(l_tot > 0.f ? m_ref : -INFINITY, l_tot, f32 ? 1.f : 0.f, 0.f);
     }
   }
 }
@@ -509,39 +577,64 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
 template <bool MULTI>
 __global__ __launch_bounds__(128) void k_mla_combine(const MlaPtrs P, int32_t rows) {
   __shared__ float wsh[MAX_SPLITS];
-  __shared__ float stat[2];
+  __shared__ uint32_t fsh[MAX_SPLITS];
+  __shared__ float stat[3];
   const int rl = blockIdx.x / ATT_HEADS, h = blockIdx.x % ATT_HEADS;
   const int layer = MULTI ? rl / rows : 0;
   const int r = MULTI ? rl % rows : rl;
   const int S = P.splits;
   const size_t part0 = ((size_t)layer * rows + r) * S;  // (layer, row, split 0)
-  const float* ml = P.ml_part + (part0 * ATT_HEADS + h) * 2;
+  const float4* ml = reinterpret_cast<const float4*>(P.ml_part) + (part0 * ATT_HEADS + h);
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    float m = lane < S ? ml[(size_t)lane * ATT_HEADS * 2] : -INFINITY;
-    float l = lane < S ? ml[(size_t)lane * ATT_HEADS * 2 + 1] : 0.f;
+    const float4 v = lane < S ? ml[(size_t)lane * ATT_HEADS] : make_float4(-INFINITY, 0.f, 0.f, 0.f);
+    const float m = v.x, l = v.y;
+    const bool f32 = v.z != 0.f;
     float M = m;
     for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
     float w = (M == -INFINITY || m == -INFINITY) ? 0.f : exp2f(m - M);
     float ws = w * l;
     for (int o = 32; o > 0; o >>= 1) ws += __shfl_xor(ws, o, 64);
-    if (lane < S) wsh[lane] = ws > 0.f ? w * l / ws : 0.f;  // weight of the normalised partial
+    if (lane < S) {
+      wsh[lane] = ws > 0.f ? w * l / ws : 0.f;  // weight of the normalised partial
+      fsh[lane] = f32 ? 1u : 0u;
+    }
+    const bool any32 = __any(lane < S && f32);
     if (lane == 0) {
       stat[0] = M;
       stat[1] = ws;
+      stat[2] = any32 ? 1.f : 0.f;
     }
   }
   __syncthreads();
-  const _Float16* op = P.o_part + (part0 * ATT_HEADS + h) * LAT_DIM + threadIdx.x * 4;
+  const char* op = P.o_part + (part0 * ATT_HEADS + h) * (LAT_DIM * 4);
+  constexpr size_t SPLIT_STRIDE = (size_t)ATT_HEADS * LAT_DIM * 4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (stat[2] == 0.f) {  // uniform: every partial in fp16
 #pragma unroll 8
-  for (int s = 0; s < S; ++s) {
-    float f = wsh[s];
-    const v4h v = *reinterpret_cast<const v4h*>(op + (size_t)s * ATT_HEADS * LAT_DIM);
-    acc.x = fmaf(f, (float)v[0], acc.x);
-    acc.y = fmaf(f, (float)v[1], acc.y);
-    acc.z = fmaf(f, (float)v[2], acc.z);
-    acc.w = fmaf(f, (float)v[3], acc.w);
+    for (int s = 0; s < S; ++s) {
+      const float f = wsh[s];
+      const v4h v = *reinterpret_cast<const v4h*>(op + s * SPLIT_STRIDE + threadIdx.x * 8);
+      acc.x = fmaf(f, (float)v[0], acc.x);
+      acc.y = fmaf(f, (float)v[1], acc.y);
+      acc.z = fmaf(f, (float)v[2], acc.z);
+      acc.w = fmaf(f, (float)v[3], acc.w);
+    }
+  } else {
+    for (int s = 0; s < S; ++s) {
+      const float f = wsh[s];
+      float4 x;
+      if (fsh[s]) {  // uniform
+        x = *reinterpret_cast<const float4*>(op + s * SPLIT_STRIDE + threadIdx.x * 16);
+      } else {
+        const v4h v = *reinterpret_cast<const v4h*>(op + s * SPLIT_STRIDE + threadIdx.x * 8);
+        x = make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+      }
+      acc.x = fmaf(f, x.x, acc.x);
+      acc.y = fmaf(f, x.y, acc.y);
+      acc.z = fmaf(f, x.z, acc.z);
+      acc.w = fmaf(f, x.w, acc.w);
+    }
   }
   *reinterpret_cast<float4*>(P.out[layer] + ((size_t)r * ATT_HEADS + h) * LAT_DIM + threadIdx.x * 4) = acc;
   if (P.lse[layer] && threadIdx.x == 0)
@@ -596,7 +689,9 @@ isa_status launch_sparse_mla(const BatchArgs& a, const MlaPlan& p, int32_t n_lay
   P.n_units = units;
   // a launch of at most 128 units would fill half the CUs: split the heads
   const bool hsplit = units <= 128;
-  const dim3 grid(hsplit ? (unsigned)((units + 7) / 8 * 16) : (unsigned)units), block(MLA_THREADS);
+  const int nx = device_info().n_xcd;
+  P.n_xcd = nx;
+  const dim3 grid(hsplit ? (unsigned)((units + nx - 1) / nx * nx * 2) : (unsigned)units), block(MLA_THREADS);
   hipError_t e;
 #define ISA_MLA_LAUNCH(FP8_, MULTI_)                                                                         \
   (hsplit ? launch_timed(ISA_TIMER_MLA_SPLIT, k_mla_split<FP8_, MULTI_, ATT_HEADS / 2>, grid, block, stream, a, P) \

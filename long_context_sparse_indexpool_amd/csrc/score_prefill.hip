@@ -24,7 +24,7 @@
 // The MFMAs of each query are issued before the epilogue of the previous one,
 // across block boundaries, so the matrix core and the VALU work side by side.
 // Workgroups are numbered so that every query block of one group range lands
-// on the same XCD (dispatch is round-robin over the 8 XCDs): the range's
+// on the same XCD (dispatch is round-robin over the XCDs): the range's
 // 512 KiB of keys is then fetched into that XCD's L2 once and reused by all
 // query blocks.
 #include "isa_launch.hpp"
@@ -35,7 +35,6 @@ constexpr int PF_THREADS = 256;
 constexpr int PF_QW = 4;                      // queries per wave
 constexpr int PF_QB = PF_QW * (PF_THREADS / 64);  // queries per workgroup
 constexpr int PF_GT = 4096;                   // groups per workgroup
-constexpr int N_XCD = 8;
 constexpr int PF_NS = 4;                      // key blocks staged in LDS (ring slots)
 constexpr int PF_KB = 32 * IDX_DIM;           // bytes of one key block (32 groups)
 
@@ -45,9 +44,10 @@ constexpr int PF_KB = 32 * IDX_DIM;           // bytes of one key block (32 grou
 // outstanding loads, since it cannot tell ring slots apart.  The instruction
 // has no register result; completion is tracked by vmcnt (waited for
 // explicitly by the caller).  One wait state separates the M0 write from the
-// load that reads it; nothing else in this kernel uses M0.
+// load that reads it; M0 is declared clobbered, so the compiler keeps nothing
+// of its own there across the statement.
 __device__ __forceinline__ void load_to_lds16(const int8_t* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(N), no wait on the other counters
@@ -76,6 +76,7 @@ struct PrefillPtrs {
   int32_t Q;
   int32_t n_qb;
   int32_t n_gr;
+  int32_t n_xcd;  // XCDs the workgroups are dispatched over, round-robin
   uint32_t* err;
 };
 
@@ -83,10 +84,10 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_scores(const BatchArgs a
   __shared__ int32_t pages[PF_GT / PAGE_GRP];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: query indices and bases stay scalar
-  const int xcd = blockIdx.x % N_XCD;
-  const int i = blockIdx.x / N_XCD;
+  const int xcd = blockIdx.x % P.n_xcd;
+  const int i = blockIdx.x / P.n_xcd;
   const int qb = i % P.n_qb;
-  const int gr = (i / P.n_qb) * N_XCD + xcd;
+  const int gr = (i / P.n_qb) * P.n_xcd + xcd;
   if (gr >= P.n_gr) return;
   const int L = a.lens[0];
   const int G = (L + GROUP - 1) / GROUP;
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_scores(const BatchArgs a
   v4i qa[PF_QW][4];
   uint32_t wv[PF_QW][16];  // head weights of the accumulator rows
   int lastg[PF_QW];
-  bool bad = false;
+  bool bad_w = false, bad_p = false;
 #pragma unroll
   for (int qq = 0; qq < PF_QW; ++qq) {
     int qi = qb * PF_QB + wave * PF_QW + qq;
@@ -115,17 +116,18 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_scores(const BatchArgs a
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       int w = hp[(r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)];
-      bad |= (w < 0) | (w > 64);
+      bad_w |= (w < 0) | (w > 64);
       wv[qq][r] = (uint32_t)w;
     }
     int p = P.q_pos[qc];
-    if (live && (p < 0 || p >= L)) {
-      bad = true;
+    if (live && (p < 0 || p >= L)) {  // nothing of this query is visible
+      bad_p = true;
       p = -4;
     }
     lastg[qq] = __builtin_amdgcn_readfirstlane(live ? p / GROUP : -2);  // -2: query beyond Q, nothing stored
   }
-  if (__any(bad) && lane == 0) report(P.err, ISA_DERR_HEADW_RANGE | ISA_DERR_ROW_RANGE);
+  if (__any(bad_w) && lane == 0) report(P.err, ISA_DERR_HEADW_RANGE);
+  if (__any(bad_p) && lane == 0) report(P.err, ISA_DERR_ROW_RANGE);
   __syncthreads();
 
   // Key blocks (32 groups x 128 B) are staged once per workgroup in a ring of
@@ -251,15 +253,26 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_scores(const BatchArgs a
   }
   finish(s2, partial(pend, 3), 1, g0 + (blk - 1) * 32);
   if (__any(smax > 0x7FFFFFFFu) && lane == 0) report(P.err, ISA_DERR_SCORE_OVERFLOW);
+  // columns past the sequence's last group, up to the row stride, are not
+  // candidates: the last group range writes them as -1 for its queries
+  if (gr == P.n_gr - 1) {
+    for (int qq = 0; qq < PF_QW; ++qq) {
+      const int qi = qb * PF_QB + wave * PF_QW + qq;
+      if (qi >= P.Q) break;  // uniform
+      int32_t* row = P.scores + (size_t)qi * P.ld;
+      for (int c = G + lane; c < P.ld; c += 64) row[c] = -1;
+    }
+  }
 }
 
 isa_status launch_prefill_scores(const BatchArgs& a, const int8_t* q, const int8_t* hw, const int32_t* q_pos,
                                  int32_t Q, const int8_t* pooled, const int32_t* bt, int32_t* scores,
                                  int32_t ld, uint32_t* err, hipStream_t stream) {
   const int G = (a.lens[0] + GROUP - 1) / GROUP;
-  PrefillPtrs P{q, hw, q_pos, pooled, bt, scores, ld, Q, (Q + PF_QB - 1) / PF_QB, (G + PF_GT - 1) / PF_GT, err};
-  const int gr_rounds = (P.n_gr + N_XCD - 1) / N_XCD;
-  const long long nwg = (long long)gr_rounds * N_XCD * P.n_qb;
+  const int nx = device_info().n_xcd;
+  PrefillPtrs P{q, hw, q_pos, pooled, bt, scores, ld, Q, (Q + PF_QB - 1) / PF_QB, (G + PF_GT - 1) / PF_GT, nx, err};
+  const int gr_rounds = (P.n_gr + nx - 1) / nx;
+  const long long nwg = (long long)gr_rounds * nx * P.n_qb;
   if (nwg > 0x7FFFFFFF) return ISA_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(k_prefill_scores, dim3((unsigned)nwg), dim3(PF_THREADS), 0, stream, a, P);
   return hipGetLastError() == hipSuccess ? ISA_OK : ISA_ERR_HIP;

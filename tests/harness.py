@@ -117,6 +117,22 @@ def run_topk(db: DeviceBatch, k: int = TOPK_GROUPS, with_scores: bool = True, q=
     return idx.cpu().numpy(), cnt.cpu().numpy(), (sc.cpu().numpy() if sc is not None else None), ws
 
 
+def topk_into(db: DeviceBatch, ws: torch.Tensor, q: np.ndarray, hw: np.ndarray, k: int = TOPK_GROUPS,
+              with_scores: bool = False):
+    """isa_indexer_topk (decode mode) on a caller-provided workspace; host (idx, cnt, scores or None)."""
+    m = isa()
+    B = db.wl.batch
+    Gmax = max(db.wl.groups(b) for b in range(B))
+    ld = (Gmax + 3) // 4 * 4
+    idx = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    sc = torch.full((B, ld), -7, dtype=torch.int32, device="cuda") if with_scores else None
+    m.isa_indexer_topk(torch.from_numpy(q).cuda(), torch.from_numpy(hw).cuda(), db.pooled, db.seqs, None, B, ld, k,
+                       idx, cnt, sc, ws)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), cnt.cpu().numpy(), (sc.cpu().numpy() if sc is not None else None)
+
+
 def run_attention(db: DeviceBatch, idx: torch.Tensor, cnt: torch.Tensor, k: int, q=None, row_seq=None,
                   row_pos=None, rows=None):
     m = isa()
@@ -240,20 +256,15 @@ def check_topk_row(S: np.ndarray, k: int, idx_row: np.ndarray, cnt: int):
     assert np.array_equal(idx_row, ridx), "selected ids differ from the oracle"
 
 
-def attention_tolerance(out: np.ndarray, ref: np.ndarray, lse=None, ref_lse=None, vmax: float = 0.0):
-    """max-abs <= 2e-2 and relative L2 <= 1e-3 (and |d lse| <= 1e-3 where finite).
-
-    vmax: the largest |latent value| among the attended tokens, when a test plants
-    values far outside the N(0,1) workload.  The probabilities of the P.V product
-    are fp16, off by at most 2^-11 relative each, so an output element can be off
-    by about 2^-11 * vmax: the 2e-2 bound covers |v| <= 40 and grows in
-    proportion beyond that (the relative bounds are unchanged)."""
+def attention_tolerance(out: np.ndarray, ref: np.ndarray, lse=None, ref_lse=None):
+    """max-abs <= 2e-2 and relative L2 <= 1e-3 (and |d lse| <= 1e-3 where finite),
+    the same bound for every row whatever its latent values."""
     d = out.astype(np.float64) - ref
     mx = float(np.max(np.abs(d))) if d.size else 0.0
     nrm = float(np.linalg.norm(ref))
     rel = float(np.linalg.norm(d) / nrm) if nrm > 0 else float(np.linalg.norm(d))
     assert np.all(np.isfinite(out)), "non-finite attention output"
-    assert mx <= 2e-2 * max(1.0, vmax / 40.0), f"max-abs error {mx}"
+    assert mx <= 2e-2, f"max-abs error {mx}"
     assert rel <= 1e-3, f"relative L2 error {rel}"
     dl = 0.0
     if lse is not None:

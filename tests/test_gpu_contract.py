@@ -1,0 +1,340 @@
+"""GPU tests of the C ABI's contract beyond the workload shapes, through the
+library: one workspace reused across batch shapes and shared between calls;
+every device error bit the header promises, raised by the kernels' own bounded
+checks (nothing here faults: each bad value is one the kernels test before any
+access it would steer); and attention over latent values far outside N(0,1),
+held to the same bound as every other row.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth.configs import IDX_DIM, IDX_HEADS, LAT_DIM, SM_SCALE, TOPK_GROUPS, custom
+
+import harness as H
+
+pytestmark = pytest.mark.gpu
+
+BF16_P96, BF16_M96 = 0x42C0, 0xC2C0        # +-96
+BF16_P1024, BF16_M1024 = 0x4480, 0xC480    # +-1024
+WORST_SCORE = 32 * 64 * 128 * 127 * 127    # 4,228,120,576 > INT32_MAX
+
+
+def _random_pooled(name, seed, lens):
+    """A batch whose pooled int8 keys are drawn directly (uniform [-127, 127]):
+    the top-k needs no indexer keys, and the oracle scores these same bytes."""
+    m = H.isa()
+    wl = custom(name, seed, lens, paged_random=True)
+    bt = torch.from_numpy(wl.block_table()).cuda()
+    db = H.DeviceBatch(wl, m.Seqs(wl.lens, bt, wl.num_pages), bt)
+    db.pooled = torch.from_numpy(synth.uniform_i8(seed, 40, (wl.num_pages, 64, IDX_DIM), -127, 127)).cuda()
+    return db
+
+
+def _check_ids(db, idx, cnt, q, hw):
+    def one(b):
+        S = oracle.scores(q[b], hw[b], H.pooled_logical(db, b), threads=1)
+        H.check_topk_row(S, TOPK_GROUPS, idx[b], int(cnt[b]))
+        return True
+    assert all(oracle.map_rows(one, range(db.wl.batch)))
+
+
+def _hist_region_zero(ws):
+    # the per-sequence histograms: 2 MiB right after the 256-byte error header
+    return bool((ws[256: 256 + (2 << 20)] == 0).all())
+
+
+def test_workspace_reused_across_shapes_and_shared_with_attention():
+    """One workspace, sized for the largest call, serves top-k calls whose tile
+    counts grow and shrink (64 x 128K tokens, then 1 x 8192; 8, 7 and 8
+    sequences of 2^20) and an attention call in between: every selection is
+    bit-exact against the oracle and the histogram region is zero after every
+    call."""
+    m = H.isa()
+    shapes = [("b64", [131072] * 64), ("b1", [8192]), ("b8", [1 << 20] * 8), ("b7", [1 << 20] * 7),
+              ("b8_again", [1 << 20] * 8)]
+    dbs = [_random_pooled(n, 50 + i, lens) for i, (n, lens) in enumerate(shapes)]
+    small = custom("shared_ws", 57, [3000, 700, 20000], paged_random=True)
+    sdb = H.make_batch(small)
+    H.run_pool(sdb)
+    sizes = [m.workspace_size(m.ISA_OP_INDEXER_TOPK, d.seqs) for d in dbs + [sdb]]
+    sizes.append(m.workspace_size(m.ISA_OP_SPARSE_MLA, sdb.seqs, small.batch))
+    ws = m.alloc_workspace(max(sizes))
+    for i, db in enumerate(dbs):
+        B = db.wl.batch
+        q = synth.uniform_i8(60 + i, 3, (B, IDX_HEADS, IDX_DIM), -127, 127)
+        hw = synth.uniform_i8(60 + i, 4, (B, IDX_HEADS), 0, 64)
+        H.log(f"shared workspace: top-k of {db.wl.name}")
+        idx, cnt, _ = H.topk_into(db, ws, q, hw)
+        assert m.isa_device_error(ws) == 0
+        assert _hist_region_zero(ws), f"histograms not zero after {db.wl.name}"
+        _check_ids(db, idx, cnt, q, hw)
+        if i == 1:
+            # attention on the same workspace leaves its split partials behind;
+            # the next top-k must not read them
+            qs = small.q_idx()
+            hs = small.head_w()
+            sidx, scnt, _ = H.topk_into(sdb, ws, qs, hs)
+            out = torch.empty((small.batch, 64, LAT_DIM), dtype=torch.float32, device="cuda")
+            qa = torch.from_numpy(small.q_attn(0, small.batch).view(np.int16)).cuda()
+            m.isa_sparse_mla_decode(qa, sdb.latent, sdb.seqs, None, None, small.batch, torch.from_numpy(sidx).cuda(),
+                                    torch.from_numpy(scnt).cuda(), TOPK_GROUPS, SM_SCALE, out, None, ws)
+            torch.cuda.synchronize()
+            assert m.isa_device_error(ws) == 0
+            assert _hist_region_zero(ws), "histograms not zero after the attention call"
+            _check_ids(sdb, sidx, scnt, qs, hs)
+            lat, to = sdb.host["latent"], small.token_offsets
+            qah = small.q_attn(0, small.batch)
+            o = out.cpu().numpy()
+            for b in range(small.batch):
+                L = small.lens[b]
+                ref, _ = oracle.attention(qah[b], lat[to[b]: to[b + 1]], L, L - 1, sidx[b], int(scnt[b]), SM_SCALE)
+                H.attention_tolerance(o[b], ref)
+
+
+def _saturated_batch(name, lens):
+    """Pooled keys all +127: with q = 127 and head weights 64 every score is the
+    largest possible one, 4,228,120,576, above INT32_MAX."""
+    m = H.isa()
+    wl = custom(name, 61, lens)
+    bt = torch.from_numpy(wl.block_table()).cuda()
+    db = H.DeviceBatch(wl, m.Seqs(wl.lens, bt, wl.num_pages), bt)
+    db.pooled = torch.full((wl.num_pages, 64, IDX_DIM), 127, dtype=torch.int8, device="cuda")
+    return db
+
+
+def test_score_overflow_is_reported_decode():
+    """Decode scores above INT32_MAX set ISA_DERR_SCORE_OVERFLOW; the selection
+    still ranks them exactly (all equal: the lowest ids), and the optional score
+    output holds them wrapped to int32."""
+    m = H.isa()
+    db = _saturated_batch("overflow_decode", [20000, 9000])
+    B = db.wl.batch
+    q = np.full((B, IDX_HEADS, IDX_DIM), 127, np.int8)
+    hw = np.full((B, IDX_HEADS), 64, np.int8)
+    assert int(oracle.scores(q[0], hw[0], np.full((4, IDX_DIM), 127, np.int8))[0]) == WORST_SCORE
+    ws = m.alloc_workspace(m.workspace_size(m.ISA_OP_INDEXER_TOPK, db.seqs))
+    idx, cnt, sc = H.topk_into(db, ws, q, hw, with_scores=True)
+    err = m.isa_device_error(ws, clear=True)
+    assert err == m.DERR_SCORE_OVERFLOW, f"error word {err:#x}"
+    wrapped = WORST_SCORE - (1 << 32)
+    for b in range(B):
+        G = db.wl.groups(b)
+        assert np.all(sc[b, :G] == wrapped)
+        assert cnt[b] == TOPK_GROUPS and np.array_equal(idx[b], np.arange(TOPK_GROUPS))
+    assert m.isa_device_error(ws) == 0
+
+
+def test_score_overflow_is_reported_prefill():
+    """Prefill scores above INT32_MAX set ISA_DERR_SCORE_OVERFLOW (the stored
+    value is negative, so the row top-k would skip it: the bit is the signal)."""
+    m = H.isa()
+    db = _saturated_batch("overflow_prefill", [5000])
+    G = db.wl.groups(0)
+    pos = np.array([0, 2500, 4999], np.int32)
+    Q = len(pos)
+    q = torch.full((Q, IDX_HEADS, IDX_DIM), 127, dtype=torch.int8, device="cuda")
+    hw = torch.full((Q, IDX_HEADS), 64, dtype=torch.int8, device="cuda")
+    sc = torch.full((Q, G), -7, dtype=torch.int32, device="cuda")
+    ws = m.alloc_workspace(m.workspace_size(m.ISA_OP_PREFILL_SCORES, db.seqs))
+    m.isa_indexer_prefill_scores(q, hw, torch.from_numpy(pos).cuda(), Q, db.pooled, db.seqs, sc, G, ws)
+    torch.cuda.synchronize()
+    err = m.isa_device_error(ws, clear=True)
+    assert err == m.DERR_SCORE_OVERFLOW, f"error word {err:#x}"
+    S = sc.cpu().numpy()
+    for i, p in enumerate(pos):
+        vis = np.arange(G) <= p // 4
+        assert np.all(S[i, vis] == WORST_SCORE - (1 << 32)) and np.all(S[i, ~vis] == -1)
+
+
+def test_prefill_range_errors_are_separate_bits():
+    """A head weight outside [0, 64] sets ISA_DERR_HEADW_RANGE alone; a query
+    position outside [0, L) sets ISA_DERR_ROW_RANGE alone and leaves that
+    query's row all -1, while the other rows are exact."""
+    m = H.isa()
+    L = 3000
+    wl = custom("prefill_errors", 63, [L], kind="prefill", q_pos=[5, 2999, 1200])
+    db = H.make_batch(wl, with_latent=False)
+    H.run_pool(db)
+    G = wl.groups(0)
+    qh, hwh, pos = wl.q_idx(), wl.head_w(), wl.row_pos()
+    k8 = H.pooled_logical(db, 0)
+    ws = m.alloc_workspace(256)
+
+    def run(hw, p):
+        sc = torch.full((3, G + 8), -7, dtype=torch.int32, device="cuda")
+        m.isa_indexer_prefill_scores(torch.from_numpy(qh).cuda(), torch.from_numpy(hw).cuda(),
+                                     torch.from_numpy(p).cuda(), 3, db.pooled, db.seqs, sc, G + 8, ws)
+        torch.cuda.synchronize()
+        return m.isa_device_error(ws, clear=True), sc.cpu().numpy()
+
+    bad_w = hwh.copy()
+    bad_w[1, 7] = 65
+    err, _ = run(bad_w, pos)
+    assert err == m.DERR_HEADW_RANGE, f"error word {err:#x}"
+    bad_p = pos.copy()
+    bad_p[2] = L
+    err, S = run(hwh, bad_p)
+    assert err == m.DERR_ROW_RANGE, f"error word {err:#x}"
+    assert np.all(S[2] == -1)
+    for i in (0, 1):
+        assert np.array_equal(S[i, :G].astype(np.int64), oracle.prefill_scores(qh[i], hwh[i], int(pos[i]), k8))
+        assert np.all(S[i, G:] == -1)
+
+
+def test_nonfinite_inputs_are_reported():
+    """ISA_DERR_NONFINITE from every call that promises it: a NaN indexer key
+    (dynamic pooling scale), an infinite latent value (FP8 quantiser), a scale
+    that is not positive and finite (append), and a KDA state that overflows."""
+    m = H.isa()
+    wl = custom("nonfinite", 65, [3000, 700])
+    db = H.make_batch(wl, with_keys=False, with_latent=False)
+    keys = wl.keys_logical()
+    keys[wl.token_offsets[1] + 17, 3] = 0x7FC0  # NaN
+    db.host["keys"] = keys
+    db.keys = H.pool_from_logical(wl, keys, 256, H.NAN_BF16)
+    pooled = torch.zeros((wl.num_pages, 64, IDX_DIM), dtype=torch.int8, device="cuda")
+    scales = torch.zeros(wl.batch, dtype=torch.float32, device="cuda")
+    ws = m.alloc_workspace(m.workspace_size(m.ISA_OP_INDEXPOOL, db.seqs))
+    m.isa_indexpool(db.keys, wl.pool_weights(), db.seqs, scales, pooled, 0, ws)
+    torch.cuda.synchronize()
+    assert m.isa_device_error(ws, clear=True) == m.DERR_NONFINITE
+
+    lat = wl.latent_logical()
+    lat[9, 100] = 0x7F80  # +inf
+    latd = H.pool_from_logical(wl, lat, 256, H.NAN_BF16)
+    codes = torch.zeros((wl.num_pages, 256, LAT_DIM), dtype=torch.uint8, device="cuda")
+    rs = torch.zeros((wl.num_pages, 256), dtype=torch.float32, device="cuda")
+    ws8 = m.alloc_workspace(m.workspace_size(m.ISA_OP_LATENT_FP8, db.seqs))
+    m.isa_latent_to_fp8(latd, db.seqs, codes, rs, ws8)
+    torch.cuda.synchronize()
+    assert m.isa_device_error(ws8, clear=True) == m.DERR_NONFINITE
+
+    wsa = m.alloc_workspace(m.workspace_size(m.ISA_OP_APPEND_TOKEN, db.seqs))
+    knew = torch.zeros((wl.batch, IDX_DIM), dtype=torch.int16, device="cuda")
+    bad_scale = torch.tensor([1.0, 0.0], dtype=torch.float32, device="cuda")
+    m.isa_append_token(knew, None, wl.pool_weights(), db.seqs, bad_scale, db.keys, None, pooled, wsa)
+    torch.cuda.synchronize()
+    assert m.isa_device_error(wsa, clear=True) == m.DERR_NONFINITE
+
+    n = 4
+    big = np.full((n, 128, 128), 0x7F7F, np.uint16)  # the largest finite bf16, ~3.4e38
+    st = torch.from_numpy(big.view(np.int16)).cuda()
+    one = np.full((n, 128), 0x3F80, np.uint16)  # 1.0
+    q = torch.from_numpy(one.view(np.int16)).cuda()
+    k = torch.from_numpy(one.view(np.int16)).cuda()
+    v = torch.from_numpy(one.view(np.int16)).cuda()
+    alpha = torch.ones((n, 128), dtype=torch.float32, device="cuda")
+    beta = torch.full((n,), 0.5, dtype=torch.float32, device="cuda")
+    out = torch.empty((n, 128), dtype=torch.float32, device="cuda")
+    wsk = m.alloc_workspace(m.workspace_size(m.ISA_OP_KDA_STEP, None))
+    m.isa_kda_decode_step(q, k, v, alpha, beta, st, out, wsk)
+    torch.cuda.synchronize()
+    assert m.isa_device_error(wsk, clear=True) == m.DERR_NONFINITE
+
+
+def test_attention_row_range_errors():
+    """Rows whose sequence, position or count lies outside the batch set
+    ISA_DERR_ROW_RANGE and produce out = 0, lse = -inf; a selected group id past
+    its sequence sets the same bit and is skipped (the row attends to its other
+    groups); the good rows of the same call match the oracle."""
+    m = H.isa()
+    wl = custom("row_range", 67, [3000, 9000])
+    db = H.make_batch(wl)
+    H.run_pool(db)
+    idx, cnt, _, _ = H.run_topk(db, with_scores=False)
+    G1 = wl.groups(1)
+    rows = 6
+    row_seq = np.array([0, 1, 2, 1, 1, 0], np.int32)          # row 2: sequence 2 of a 2-sequence batch
+    row_pos = np.array([2999, 8999, 0, 9000, 4000, 1000], np.int32)  # row 3: position == L
+    ridx = np.stack([idx[0], idx[1], idx[0], idx[1], idx[1], idx[0]]).astype(np.int32)
+    rcnt = np.array([cnt[0], cnt[1], cnt[0], cnt[1], cnt[1], cnt[0]], np.int32)
+    ridx[4, 3] = G1 + 5      # row 4: one group id past its sequence
+    rcnt[5] = TOPK_GROUPS + 1  # row 5: count above k
+    q = synth.normal_bf16(68, 6, (rows, 64, LAT_DIM))
+    qd = torch.from_numpy(q.view(np.int16)).cuda()
+    out = torch.full((rows, 64, LAT_DIM), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((rows, 64), float("nan"), dtype=torch.float32, device="cuda")
+    ws = m.alloc_workspace(m.workspace_size(m.ISA_OP_SPARSE_MLA, db.seqs, rows))
+    m.isa_sparse_mla_decode(qd, db.latent, db.seqs, torch.from_numpy(row_seq).cuda(),
+                            torch.from_numpy(row_pos).cuda(), rows, torch.from_numpy(ridx).cuda(),
+                            torch.from_numpy(rcnt).cuda(), TOPK_GROUPS, SM_SCALE, out, lse, ws)
+    torch.cuda.synchronize()
+    err = m.isa_device_error(ws, clear=True)
+    assert err == m.DERR_ROW_RANGE, f"error word {err:#x}"
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    for r in (2, 3, 5):
+        assert np.all(o[r] == 0) and np.all(np.isneginf(l[r])), f"row {r}"
+    lat, to = db.host["latent"], wl.token_offsets
+    for r in (0, 1, 4):
+        s = row_seq[r]
+        sel = ridx[r].copy()
+        n = int(rcnt[r])
+        if r == 4:  # the bad id is skipped: the oracle attends to the other groups
+            keep = sel[:n][sel[:n] < G1]
+            sel = np.full(TOPK_GROUPS, -1, np.int32)
+            sel[: len(keep)] = keep
+            n = len(keep)
+        ref, ref_lse = oracle.attention(q[r], lat[to[s]: to[s + 1]], wl.lens[s], int(row_pos[r]), sel, n, SM_SCALE)
+        H.attention_tolerance(o[r], ref, l[r], ref_lse)
+
+
+def _plant(lat, wl, idx, cnt, plan):
+    """Write bf16 bits into channels of tokens of selected groups: plan is a list
+    of (sequence, j-th selected group, token in group, channel, bits)."""
+    to = wl.token_offsets
+    for b, j, i, c, bits in plan:
+        g = int(idx[b][j % int(cnt[b])])
+        t = min(4 * g + i, wl.lens[b] - 1)
+        lat[to[b] + t, c] = bits
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("lens", [[9000, 3000, 20003, 700, 131075],
+                                  [3000, 5000, 2500, 4100, 9000, 700, 3333, 6000, 2049, 4096, 8191, 12000]],
+                         ids=["32heads", "64heads"])
+def test_attention_large_latent_values(lens, fmt):
+    """Latent values of +-96 and +-1024 planted in selected tokens (the heads
+    whose query leans on that channel then put almost all their weight on the
+    token, so output elements near +-1024 occur) against the oracle with the
+    unwidened bound: max-abs 2e-2, relative L2 1e-3, lse 1e-3.  Five rows run
+    two workgroups per (row, split) with 32 heads each, twelve rows 64 heads per
+    workgroup; the bf16 cache and the FP8 cache (a planted value sets its row's
+    scale) both."""
+    wl = custom("large_values", 71, lens, paged_random=True)
+    db = H.make_batch(wl, with_latent=False)
+    H.run_pool(db)
+    idx, cnt, _, _ = H.run_topk(db, with_scores=False)
+    lat = wl.latent_logical()
+    plan = []
+    for b in range(wl.batch):
+        plan += [(b, 3, 1, 300, BF16_M96), (b, 40, 2, 17, BF16_P96), (b, 77, 0, 511, BF16_M96)]
+    plan += [(0, 5, 0, 64, BF16_P1024), (0, 200, 3, 65, BF16_M1024), (wl.batch - 1, 9, 1, 400, BF16_M1024)]
+    _plant(lat, wl, idx, cnt, plan)
+    db.host["latent"] = lat
+    db.latent = H.pool_from_logical(wl, lat, 256, H.NAN_BF16)
+    idx_d, cnt_d = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
+    q = wl.q_attn(0, wl.batch)
+    to = wl.token_offsets
+    worst = 0.0
+    if fmt == "bf16":
+        out, lse = H.run_attention(db, idx_d, cnt_d, TOPK_GROUPS, q=q)
+        for b in range(wl.batch):
+            L = wl.lens[b]
+            ref, ref_lse = oracle.attention(q[b], lat[to[b]: to[b + 1]], L, L - 1, idx[b], int(cnt[b]), SM_SCALE)
+            worst = max(worst, float(np.abs(ref).max()))
+            H.attention_tolerance(out[b], ref, lse[b], ref_lse)
+    else:
+        codes, scales = H.latent_fp8(db)
+        ref_c, ref_s = oracle.latent_fp8(lat)
+        out, lse = H.run_attention_fp8(db, codes, scales, idx_d, cnt_d, TOPK_GROUPS, q=q)
+        for b in range(wl.batch):
+            L = wl.lens[b]
+            ref, ref_lse = oracle.attention_fp8(q[b], ref_c[to[b]: to[b + 1]], ref_s[to[b]: to[b + 1]], L, L - 1,
+                                                idx[b], int(cnt[b]), SM_SCALE)
+            worst = max(worst, float(np.abs(ref).max()))
+            H.attention_tolerance(out[b], ref, lse[b], ref_lse)
+    # the planted values dominate some heads: outputs of hundreds occur
+    assert worst > 500.0, f"largest output {worst}: the planted values were not attended"

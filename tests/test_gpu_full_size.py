@@ -7,10 +7,10 @@ sequences up to 2^20; 256 sequences, one of the maximum 2^22 tokens): pooled key
 bit-exact (from a second call that also writes the scores), every selected id
 bit-exact, and attention within tolerance for every row.  At 8 x 1,048,576 also
 IndexShare: four layers' attention over the same selection in one call, every
-row of every layer against the oracle.  The prefill chunk
-(2048 queries at the end of one 2^20-token sequence) checks the mask of all
-2048 score rows at full size and sampled rows one by one: scores, selection and
-attention.
+row of every layer against the oracle.  The prefill chunk (2048 queries at the
+end of one 2^20-token sequence): the mask of every score row, every row's
+scores bit-exact and its selected ids against the oracle's top-k of those
+scores, and attention on one row of every 16-query block.
 """
 import numpy as np
 import pytest
@@ -205,20 +205,31 @@ def test_full_prefill_q2048_L1048576():
     m.isa_indexer_topk(None, None, None, None, sc, Q, G, TOPK_GROUPS, idx, cnt, None, ws)
     torch.cuda.synchronize()
     out, lse = H.run_attention(db, idx, cnt, TOPK_GROUPS, row_seq=np.zeros(Q, np.int32), row_pos=qpos, rows=Q)
+    idxh, cnth = idx.cpu().numpy(), cnt.cpu().numpy()
 
-    rows = [0, 1, 2, 3, 511, 1024, 1537, 2045, 2046, 2047]
-    H.log(f"{wl.name}: oracle on rows {rows}")
+    # every row: scores bit-exact against the oracle, ids against the oracle's
+    # top-k of those scores (rows in chunks, so the host holds one chunk)
     k8 = H.pooled_logical(db, 0)
-    S = sc[rows].cpu().numpy()
-    idxh, cnth = idx[rows].cpu().numpy(), cnt[rows].cpu().numpy()
-    refs = oracle.map_rows(lambda j: oracle.prefill_scores(qh[rows[j]], hwh[rows[j]], int(qpos[rows[j]]), k8),
-                           range(len(rows)))
+    chunk = 128
+    for r0 in range(0, Q, chunk):
+        rows = list(range(r0, min(Q, r0 + chunk)))
+        H.log(f"{wl.name}: oracle scores and selection of rows {rows[0]}..{rows[-1]}")
+        S = sc[rows[0]: rows[-1] + 1].cpu().numpy()
+
+        def one(r):
+            ref = oracle.prefill_scores(qh[r], hwh[r], int(qpos[r]), k8)
+            assert np.array_equal(S[r - r0].astype(np.int64), ref), f"scores of query {r}"
+            H.check_topk_row(ref, TOPK_GROUPS, idxh[r], int(cnth[r]))
+            return True
+
+        assert all(oracle.map_rows(one, rows))
+        del S
+    # attention: one row of every 16-query block, plus the last rows
+    att_rows = sorted(set(range(0, Q, 16)) | {1, 2, 3, Q - 2, Q - 1} | set(range(7, Q, 16 * 8)))
+    H.log(f"{wl.name}: oracle attention on {len(att_rows)} rows")
     qa, lat = db.host["q_attn"], db.host["latent"]
     ref_att = oracle.map_rows(
-        lambda j: oracle.attention(qa[rows[j]], lat, L, int(qpos[rows[j]]), idxh[j], int(cnth[j]), SM_SCALE),
-        range(len(rows)))
-    for j, r in enumerate(rows):
-        assert np.array_equal(S[j].astype(np.int64), refs[j]), f"scores of query {r}"
-        H.check_topk_row(refs[j], TOPK_GROUPS, idxh[j], int(cnth[j]))
+        lambda r: oracle.attention(qa[r], lat, L, int(qpos[r]), idxh[r], int(cnth[r]), SM_SCALE), att_rows)
+    for j, r in enumerate(att_rows):
         H.attention_tolerance(out[r], ref_att[j][0], lse[r], ref_att[j][1])
     H.log(f"{wl.name}: done")

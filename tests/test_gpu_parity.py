@@ -319,8 +319,8 @@ def test_fp8_latent_cache(lens):
         L = wl.lens[b]
         ref, ref_lse = oracle.attention_fp8(q[b], ref_c[to[b]: to[b + 1]], ref_s[to[b]: to[b + 1]], L, L - 1, idx[b],
                                             int(cnt[b]), SM_SCALE)
-        # sequence 2 carries the planted -96: its max-abs bound scales with it
-        H.attention_tolerance(out[b], ref, lse[b], ref_lse, vmax=96.0 if b == 2 else 0.0)
+        # sequence 2 carries the planted -96, held to the same bound as the rest
+        H.attention_tolerance(out[b], ref, lse[b], ref_lse)
 
 
 def test_kda_decode_steps():
@@ -430,8 +430,8 @@ def test_prefill_scores_topk_attention():
     refs = oracle.map_rows(lambda i: oracle.prefill_scores(qh[i], hwh[i], int(qpos[i]), k8), range(Q))
     for i in range(Q):
         assert np.array_equal(S[i, :G].astype(np.int64), refs[i]), f"query {i} (pos {qpos[i]})"
-        assert np.all(S[i, G:] == -7), "columns beyond the sequence were written"
-    # selection from the precomputed rows
+        assert np.all(S[i, G:] == -1), "columns past the sequence must read -1 (not candidates)"
+    # selection from the precomputed rows, over the whole row stride
     idx = torch.full((Q, 512), -7, dtype=torch.int32, device="cuda")
     cnt = torch.zeros(Q, dtype=torch.int32, device="cuda")
     m.isa_indexer_topk(None, None, None, None, sc, Q, ld, 512, idx, cnt, None, ws)
@@ -469,7 +469,7 @@ def test_prefill_scores_short_sequence(L, qpos):
     for i in range(Q):
         ref = oracle.prefill_scores(qh[i], hwh[i], int(qpos[i]), k8)
         assert np.array_equal(S[i, :G].astype(np.int64), ref), f"query {i} (pos {qpos[i]})"
-        assert np.all(S[i, G:] == -7), "columns beyond the sequence were written"
+        assert np.all(S[i, G:] == -1), "columns past the sequence must read -1"
 
 
 def test_paging_is_invisible():
