@@ -192,6 +192,29 @@ isa_status isa_indexer_topk(const int8_t* q, const int8_t* head_w, const int8_t*
                             size_t ws_bytes, isa_stream_t stream);
 
 /*
+ * (2b) isa_indexer_topk in decode mode for callers that cannot allocate device
+ * memory -- code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The scratch the call needs lives in a device array inside
+ * the library, ISA_NOALLOC_TOPK_BYTES bytes on each GPU the library runs on,
+ * held until the process ends; nothing is allocated or freed by the call.
+ * Arguments and results as isa_indexer_topk decode mode (rows = s->batch),
+ * except:
+ *   err_word [dev] one uint32 that receives the call's device error bits
+ *            (ISA_DERR_*, OR-ed in: zero it before the first call)
+ * ISA_ERR_UNSUPPORTED when the batch needs more scratch than the array holds,
+ * i.e. when isa_workspace_size(ISA_OP_INDEXER_TOPK, s, 0, 0) exceeds
+ * ISA_NOALLOC_TOPK_BYTES (at most 384 scoring work tiles: 8 sequences of 2^20
+ * tokens, 64 of 2^17 and the ragged 32-sequence batch fit).  Every call on one
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and give wrong results; order them on one
+ * stream.  Each call clears the histogram part it uses with a fill kernel.
+ */
+#define ISA_NOALLOC_TOPK_BYTES (256u + (2u << 20) + 384u * (8u + 8192u + 65536u))
+isa_status isa_indexer_topk_noalloc(const int8_t* q, const int8_t* head_w, const int8_t* pooled, const isa_seqs* s,
+                                    int32_t k, int32_t* out_idx, int32_t* out_count, int32_t* scores_out,
+                                    int32_t ld_scores, uint32_t* err_word, isa_stream_t stream);
+
+/*
  * (3) Sparse MLA attention over the selected groups ([WIKI] sparse attention
  * section: softmax only over the selected positions; [REMIO]: MLA keeps one
  * compressed latent per token; [TREND] positional encoding section: NoPE).

@@ -36,7 +36,8 @@ ISA_TIMER_INDEXER_SCORE, ISA_TIMER_MLA_SPLIT = 1, 2
 EXPORTS = ("isa_workspace_size", "isa_workspace_init", "isa_device_error", "isa_status_string", "isa_version",
            "isa_set_kernel_timer", "isa_indexpool", "isa_indexer_topk", "isa_sparse_mla_decode",
            "isa_sparse_mla_decode_shared", "isa_indexer_prefill_scores", "isa_append_token", "isa_latent_to_fp8",
-           "isa_sparse_mla_decode_fp8", "isa_kda_decode_step")
+           "isa_sparse_mla_decode_fp8", "isa_kda_decode_step", "isa_indexer_topk_noalloc")
+NOALLOC_TOPK_BYTES = 256 + (2 << 20) + 384 * (8 + 8192 + 65536)
 
 
 class IsaError(RuntimeError):
@@ -67,6 +68,7 @@ def _load() -> ctypes.CDLL:
     lib.isa_set_kernel_timer.argtypes = [i32, vp, vp, i32]
     lib.isa_indexpool.argtypes = [vp, vp, sp, vp, vp, u32, vp, sz, vp]
     lib.isa_indexer_topk.argtypes = [vp, vp, vp, sp, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.isa_indexer_topk_noalloc.argtypes = [vp, vp, vp, sp, i32, vp, vp, vp, i32, vp, vp]
     lib.isa_sparse_mla_decode.argtypes = [vp, vp, sp, vp, vp, i32, vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.isa_sparse_mla_decode_shared.argtypes = [i32, vp, vp, sp, vp, vp, i32, vp, vp, i32, ctypes.c_float, vp, vp,
                                                  vp, sz, vp]
@@ -78,7 +80,8 @@ def _load() -> ctypes.CDLL:
                                               sz, vp]
     for f in ("isa_workspace_init", "isa_device_error", "isa_set_kernel_timer", "isa_indexpool", "isa_indexer_topk",
               "isa_sparse_mla_decode", "isa_sparse_mla_decode_shared", "isa_indexer_prefill_scores",
-              "isa_append_token", "isa_latent_to_fp8", "isa_sparse_mla_decode_fp8", "isa_kda_decode_step"):
+              "isa_append_token", "isa_latent_to_fp8", "isa_sparse_mla_decode_fp8", "isa_kda_decode_step",
+              "isa_indexer_topk_noalloc"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -236,6 +239,18 @@ def isa_indexer_topk(q: Optional[torch.Tensor], head_w: Optional[torch.Tensor], 
         seqs.c if seqs is not None else None, _ptr(scores_in, torch.int32, "scores_in"), rows, ld_scores, k,
         _ptr(out_idx, torch.int32, "out_idx"), _ptr(out_count, torch.int32, "out_count"),
         _ptr(scores_out, torch.int32, "scores_out"), _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
+
+
+def isa_indexer_topk_noalloc(q: torch.Tensor, head_w: torch.Tensor, pooled: torch.Tensor, seqs: Seqs, k: int,
+                             out_idx: torch.Tensor, out_count: torch.Tensor, scores_out: Optional[torch.Tensor],
+                             ld_scores: int, err_word: torch.Tensor, stream=None) -> None:
+    """Decode-mode top-k on the library's own device scratch (no workspace);
+    err_word: int32 [1] device tensor receiving the device error bits."""
+    _check("isa_indexer_topk_noalloc", lib.isa_indexer_topk_noalloc(
+        _ptr(q, torch.int8, "q"), _ptr(head_w, torch.int8, "head_w"), _ptr(pooled, torch.int8, "pooled"), seqs.c, k,
+        _ptr(out_idx, torch.int32, "out_idx"), _ptr(out_count, torch.int32, "out_count"),
+        _ptr(scores_out, torch.int32, "scores_out"), ld_scores, _ptr(err_word, torch.int32, "err_word"),
+        _stream(stream)))
 
 
 def isa_sparse_mla_decode(q: torch.Tensor, latent: torch.Tensor, seqs: Seqs, row_seq: Optional[torch.Tensor],

@@ -147,7 +147,49 @@ DevInfo device_info() {
   return d;
 }
 
+// Argument checks of the decode-mode top-k beyond the batch description.
+isa_status check_decode_topk(const int8_t* q, const int8_t* head_w, const int8_t* pooled, const isa_seqs* s,
+                             const int32_t* scores_out, int32_t ld_scores) {
+  if (!q || !head_w || !pooled || !aligned16(q) || !aligned16(head_w) || !aligned16(pooled))
+    return ISA_ERR_INVALID_ARG;
+  if (scores_out) {
+    if (!aligned16(scores_out)) return ISA_ERR_INVALID_ARG;
+    for (int b = 0; b < s->batch; ++b)
+      if (groups_of(s->seq_lens_host[b]) > ld_scores) return ISA_ERR_INVALID_ARG;
+  }
+  return ISA_OK;
+}
+
+// Decode-mode scoring and selection on scratch laid out as `d` from `base`,
+// device errors into `err`.
+isa_status decode_topk(const int8_t* q, const int8_t* head_w, const int8_t* pooled, const isa_seqs* s, int32_t k,
+                       int32_t* out_idx, int32_t* out_count, int32_t* scores_out, int32_t ld_scores,
+                       const DecodeLayout& d, char* base, uint32_t* err, hipStream_t stream) {
+  BatchArgs a;
+  fill_batch(s, &a, k);
+  a.tile_g = decode_tile_g(s);
+  int t = 0;
+  for (int b = 0; b < s->batch; ++b) {
+    a.tile_start[b] = t;
+    t += decode_tiles(s->seq_lens_host[b], k, a.tile_g);
+  }
+  a.tile_start[s->batch] = t;
+  DecodeWs w{err, (uint2*)(base + d.tile_meta), (uint32_t*)(base + d.tile_pairs), (uint64_t*)(base + d.tile_list),
+             (uint32_t*)(base + d.seq_hist)};
+  return launch_indexer_decode(a, q, head_w, pooled, s->block_table, w, out_idx, out_count, scores_out, ld_scores,
+                               stream);
+}
+
 }  // namespace isa
+
+// The top-k's scratch in a file-scope device array, for callers that cannot
+// allocate (isa_indexer_topk_noalloc): isa_indexer_topk's workspace layout in
+// ISA_NOALLOC_TOPK_BYTES bytes.  Each device holds its own copy, at its own
+// address, looked up once per device with hipGetSymbolAddress; host code uses
+// that address only, never the array's name.
+static __device__ __align__(256) unsigned char scratch[ISA_NOALLOC_TOPK_BYTES];
+static_assert(ISA_NOALLOC_TOPK_BYTES == isa::SCR0 + 384 * (8 + isa::PAIR_CAP * 4 + isa::TILE_G * 8),
+              "the array holds the top-k layout of 384 work tiles");
 
 using namespace isa;
 
@@ -247,31 +289,49 @@ isa_status isa_indexer_topk(const int8_t* q, const int8_t* head_w, const int8_t*
     if (ws_bytes < HDR) return ISA_ERR_WORKSPACE;
     return launch_topk_rows(scores_in, rows, ld_scores, ld_scores, k, out_idx, out_count, (hipStream_t)stream);
   }
-  if (!q || !head_w || !pooled || !aligned16(q) || !aligned16(head_w) || !aligned16(pooled))
-    return ISA_ERR_INVALID_ARG;
   if (!valid_seqs(s) || rows != s->batch) return ISA_ERR_INVALID_ARG;
-  if (scores_out) {
-    if (!aligned16(scores_out)) return ISA_ERR_INVALID_ARG;
-    for (int b = 0; b < s->batch; ++b)
-      if (groups_of(s->seq_lens_host[b]) > ld_scores) return ISA_ERR_INVALID_ARG;
-  }
+  const isa_status st = check_decode_topk(q, head_w, pooled, s, scores_out, ld_scores);
+  if (st != ISA_OK) return st;
   DecodeLayout d = decode_layout(s, k);
   if (ws_bytes < d.total) return ISA_ERR_WORKSPACE;
-  BatchArgs a;
-  fill_batch(s, &a, k);
-  a.tile_g = decode_tile_g(s);
-  int t = 0;
-  for (int b = 0; b < s->batch; ++b) {
-    a.tile_start[b] = t;
-    t += decode_tiles(s->seq_lens_host[b], k, a.tile_g);
-  }
-  a.tile_start[s->batch] = t;
-  char* base = (char*)ws;
-  DecodeWs w{(uint32_t*)base, (uint2*)(base + d.tile_meta), (uint32_t*)(base + d.tile_pairs),
-             (uint64_t*)(base + d.tile_list), (uint32_t*)(base + d.seq_hist)};
-  return launch_indexer_decode(a, q, head_w, pooled, s->block_table, w, out_idx, out_count, scores_out, ld_scores,
-                               (hipStream_t)stream);
+  return decode_topk(q, head_w, pooled, s, k, out_idx, out_count, scores_out, ld_scores, d, (char*)ws, (uint32_t*)ws,
+                     (hipStream_t)stream);
 }
+
+isa_status isa_indexer_topk_noalloc(const int8_t* q, const int8_t* head_w, const int8_t* pooled, const isa_seqs* s,
+                                    int32_t k, int32_t* out_idx, int32_t* out_count, int32_t* scores_out,
+                                    int32_t ld_scores, uint32_t* err_word, isa_stream_t stream) {
+  if (k < 1 || k > MAX_K || !out_idx || !out_count || !err_word) return ISA_ERR_INVALID_ARG;
+  if (!aligned16(out_idx) || !aligned16(out_count) || ((uintptr_t)err_word & 3)) return ISA_ERR_INVALID_ARG;
+  if (!valid_seqs(s)) return ISA_ERR_INVALID_ARG;
+  const isa_status st = check_decode_topk(q, head_w, pooled, s, scores_out, ld_scores);
+  if (st != ISA_OK) return st;
+  DecodeLayout d = decode_layout(s, k);
+  if (d.total > ISA_NOALLOC_TOPK_BYTES) return ISA_ERR_UNSUPPORTED;
+  // the array's device address, once per device, with that device current
+  constexpr int MAX_DEV = 64;
+  static std::mutex mu;
+  static char* addr[MAX_DEV];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEV) return ISA_ERR_HIP;
+  char* base;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+      void* ptr = nullptr;
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return ISA_ERR_HIP;
+      addr[dev] = (char*)ptr;
+    }
+    base = addr[dev];
+  }
+  // the histograms of this batch must start at zero whatever an earlier call
+  // left behind (a fill kernel, which graph capture records as a kernel node)
+  const isa_status z = launch_fill_zero(base + d.seq_hist, (size_t)s->batch * NBINS * 4, (hipStream_t)stream);
+  if (z != ISA_OK) return z;
+  return decode_topk(q, head_w, pooled, s, k, out_idx, out_count, scores_out, ld_scores, d, base, err_word,
+                     (hipStream_t)stream);
+}
+
 
 static isa_status sparse_mla(int32_t n_layers, const uint16_t* const* q, const void* const* latent,
                              const float* const* lat_scale, const isa_seqs* s, const int32_t* row_seq,
