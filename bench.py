@@ -35,6 +35,8 @@ N_POOL_COPIES = 4
 N_QSETS = 16
 KERNEL_SOURCES = {
     "k_indexer_score": ["indexer_decode.hip", "select_device.hpp", "isa_common.hpp", "isa_launch.hpp"],
+    "k_mla_split": ["mla_decode.hip", "isa_common.hpp", "isa_launch.hpp"],
+    "k_mla_combine": ["mla_decode.hip", "isa_common.hpp", "isa_launch.hpp"],
 }
 
 
@@ -358,9 +360,11 @@ def bench_append(batch=8, length=1 << 20, reps=200):
 def oracle_step_time(dec, min_s=10.0, budget_s=25.0):
     """The CPU oracle on whole decode steps of the same workload: scores of every
     group, top-512 selection and 64-head attention for each sequence, from the
-    GPU's pooled keys (rotation set 0).  Sequences are processed, step after step,
-    until at least `min_s` seconds are spent (stopping early once `budget_s` is
-    passed); steps/s is scaled from the sequences done."""
+    GPU's pooled keys (rotation set 0).  Scoring of a sequence is spread over the
+    host threads by group ranges; selection and attention run one sequence per
+    thread.  Whole steps are repeated until at least `min_s` seconds are spent
+    (stopping after the step that passes `budget_s`); per-stage seconds are
+    reported beside steps/s."""
     import oracle
 
     wl, db = dec.wl, dec.db
@@ -373,23 +377,118 @@ def oracle_step_time(dec, min_s=10.0, budget_s=25.0):
         pages = db.bt[b, : wl.pages(b)].long()
         pooled.append(dec.pooled[0][pages].reshape(-1, 128)[: wl.groups(b)].cpu().numpy())
     threads = oracle.n_threads()
+    t_score = t_sel = t_att = 0.0
+    steps = 0
     t0 = time.perf_counter()
-    done = 0
     while True:
-        b = done % B
-        S = oracle.scores(q[b], hw[b], pooled[b], threads=threads)
-        idx, cnt = oracle.topk(S, 512)
-        oracle.attention(qa[b], lat[to[b]: to[b + 1]], wl.lens[b], wl.lens[b] - 1, idx, cnt, 1.0 / math.sqrt(512))
-        done += 1
+        a = time.perf_counter()
+        S = [oracle.scores(q[b], hw[b], pooled[b], threads=threads) for b in range(B)]
+        b_ = time.perf_counter()
+        sel = oracle.map_rows(lambda b: oracle.topk(S[b], 512), range(B), threads=threads)
+        c = time.perf_counter()
+        oracle.map_rows(lambda b: oracle.attention(qa[b], lat[to[b]: to[b + 1]], wl.lens[b], wl.lens[b] - 1,
+                                                   sel[b][0], sel[b][1], 1.0 / math.sqrt(512)),
+                        range(B), threads=threads)
+        d = time.perf_counter()
+        t_score, t_sel, t_att = t_score + b_ - a, t_sel + c - b_, t_att + d - c
+        steps += 1
         spent = time.perf_counter() - t0
-        if (spent >= min_s and done % B == 0) or spent > budget_s:
+        if spent >= min_s or spent > budget_s:
             break
-    step_s = spent * B / done
-    return {"value": round(1.0 / step_s, 4), "unit": "steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} sequence passes ({done / B:g} decode steps of {wl.name}: every pooled group scored, "
-                      f"top-512 selected, 64-head attention over the selection), scaled to steps/s; "
-                      f"scoring spread over {threads} threads, selection and attention on one",
-            "seconds": round(spent, 2)}
+    return {"value": round(steps / spent, 4), "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{steps} whole decode steps of {wl.name} (every pooled group of the {B} sequences scored, "
+                      f"top-512 selected, 64-head attention over the selection); scoring spread over {threads} "
+                      f"threads by group range, selection and attention one sequence per thread",
+            "seconds": round(spent, 2),
+            "stage_seconds_per_step": {"scores": round(t_score / steps, 4), "select": round(t_sel / steps, 4),
+                                       "attention": round(t_att / steps, 4)}}
+
+
+def oracle_single_thread_c0(dec):
+    """One decode step of the 8192-token workload through the oracle on one
+    thread: pooling of its keys, scores, selection and attention, per stage."""
+    import oracle
+
+    wl, db = dec.wl, dec.db
+    keys = wl.keys_logical(0)
+    t0 = time.perf_counter()
+    oracle.pool(keys, wl.pool_weights())
+    t1 = time.perf_counter()
+    pages = db.bt[0, : wl.pages(0)].long()
+    k8 = dec.pooled[0][pages].reshape(-1, 128)[: wl.groups(0)].cpu().numpy()
+    q, hw, qa = wl.q_idx(0, 1), wl.head_w(0, 1), wl.q_attn(0, 1)
+    t2 = time.perf_counter()
+    S = oracle.scores(q[0], hw[0], k8, threads=1)
+    idx, cnt = oracle.topk(S, 512)
+    t3 = time.perf_counter()
+    oracle.attention(qa[0], db.host["latent"], wl.lens[0], wl.lens[0] - 1, idx, cnt, 1.0 / math.sqrt(512))
+    t4 = time.perf_counter()
+    return {"workload": wl.name, "threads": 1, "pool_s": round(t1 - t0, 4), "scores_select_s": round(t3 - t2, 4),
+            "attention_s": round(t4 - t3, 4), "step_s": round(t4 - t2, 4)}
+
+
+def env_info():
+    """Device, software, host CPU and clock facts recorded beside the numbers."""
+    import subprocess
+
+    import torch
+
+    p = torch.cuda.get_device_properties(0)
+    env = {"device": torch.cuda.get_device_name(0), "arch": getattr(p, "gcnArchName", None),
+           "compute_units": p.multi_processor_count, "torch": torch.__version__,
+           "hip": getattr(torch.version, "hip", None)}
+    try:
+        with open("/proc/cpuinfo") as f:
+            models = [ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")]
+        env["cpu_model"] = models[0] if models else None
+        env["cpus_online"] = len(models)
+    except OSError:
+        env["cpu_model"] = None
+    env["cpus_in_affinity"] = len(os.sched_getaffinity(0))
+    env["omp_num_threads"] = os.environ.get("OMP_NUM_THREADS")
+    try:  # current clock levels as the SMI reports them (read-only query)
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30)
+        env["gpu_clocks"] = [ln.strip() for ln in r.stdout.splitlines() if "clk" in ln.lower() and "level" in ln.lower()]
+    except (OSError, subprocess.SubprocessError):
+        env["gpu_clocks"] = None
+    try:
+        r = subprocess.run(["rocm-smi", "--version"], capture_output=True, text=True, timeout=30)
+        env["rocm_smi"] = [ln.strip() for ln in r.stdout.splitlines() if ln.strip()][-1:] or None
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return env
+
+
+def read_ceiling(n_buf=4, buf_bytes=512 << 20, reps=24):
+    """Practical HBM read ceiling: isa_read_probe over buffers rotated so that
+    none is served from the 256 MB Infinity Cache, timed with HIP events."""
+    import torch
+
+    import long_context_sparse_indexpool_amd as m
+    bufs = [torch.empty(buf_bytes, dtype=torch.uint8, device="cuda").fill_(i + 1) for i in range(n_buf)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    clocks = torch.zeros(2, dtype=torch.int64, device="cuda")
+    for i in range(4):
+        m.isa_read_probe(bufs[i % n_buf], sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(reps):
+        m.isa_read_probe(bufs[i % n_buf], sink)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps * 1e-3
+    m.isa_read_probe(bufs[0], sink, clocks)
+    cyc, ticks = [int(x) for x in clocks.cpu()]
+    del bufs
+    torch.cuda.empty_cache()
+    gbps = buf_bytes / t / 1e9
+    ghz = cyc / (ticks / 100e6) / 1e9 if ticks else None
+    log(f"read ceiling: {gbps:.0f} GB/s ({buf_bytes >> 20} MiB per read, {n_buf} buffers rotated); "
+        f"shader clock during the probe {ghz} GHz")
+    return {"GBps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4), "bytes_per_read": buf_bytes,
+            "buffers_rotated": n_buf, "kernel": "isa_read_probe (16-B loads, grid-stride over the device)",
+            "shader_clock_GHz_during_probe": round(ghz, 3) if ghz else None}
 
 
 def bench_prefill(args):
@@ -512,16 +611,17 @@ def bench_pool(dec):
 COPY_BYTES = 1 << 30  # plain device copy used to calibrate the HBM byte counters
 
 
-def traffic_run(steps=5):
-    """Workload for the counter passes: a few decode steps of the 8 x 1M workload,
-    then a plain 1 GiB device-to-device copy three times (known bytes: 1 GiB read
-    and 1 GiB written per copy), which calibrates FETCH_SIZE / WRITE_SIZE."""
+def traffic_run(index=2, steps=5):
+    """Workload for the counter passes: a few decode steps of a decode workload
+    (default the 8 x 1M one), then a plain 1 GiB device-to-device copy three
+    times (known bytes: 1 GiB read and 1 GiB written per copy), which calibrates
+    FETCH_SIZE / WRITE_SIZE."""
     import torch
 
     from synth.configs import workload
 
     torch.cuda.set_device(0)
-    dec = Decode(workload(2), N_POOL_COPIES, N_QSETS)
+    dec = Decode(workload(index), N_POOL_COPIES, N_QSETS)
     for _ in range(3 + steps):
         dec.step()
     torch.cuda.synchronize()
@@ -586,6 +686,10 @@ def main():
     ap.add_argument("--primary-only", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-run", action="store_true", help="workload for the rocprofv3 counter passes")
+    ap.add_argument("--traffic-workload", type=int, default=2, metavar="N",
+                    help="decode workload of --traffic-run / --summarize-traffic (0, 1, 2 or 4)")
+    ap.add_argument("--traffic-kernel", default="k_indexer_score",
+                    help="kernel whose bytes --summarize-traffic extracts")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the prefill scoring measurement (for profiling that kernel alone)")
     ap.add_argument("--decode-workload", type=int, default=None, metavar="N",
@@ -594,10 +698,12 @@ def main():
                     help="write profiles/traffic_k_indexer_score_*.json from two counter CSVs (no GPU)")
     args = ap.parse_args()
     if args.summarize_traffic:
-        summarize_traffic(*args.summarize_traffic)
+        from synth.configs import workload
+        summarize_traffic(*args.summarize_traffic, kernel=args.traffic_kernel,
+                          workload_name=workload(args.traffic_workload).name)
         return
     if args.traffic_run:
-        traffic_run()
+        traffic_run(args.traffic_workload)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (a decode batch would shard by "
@@ -617,7 +723,7 @@ def main():
     if args.decode_workload is not None:
         w = workload(args.decode_workload)
         assert w.kind == "decode", "--decode-workload takes a decode workload"
-        d = Decode(w, 2, 4)
+        d = Decode(w, N_POOL_COPIES, N_QSETS)
         s = d.time_steps(args.steps, args.warmup)
         tk, ta = d.time_kernels(10)
         print(json.dumps({w.name: {"steps_per_s": round(1 / s, 1), "ms_per_step": round(s * 1e3, 4),
@@ -627,14 +733,19 @@ def main():
         d.free()
         return
 
+    env = env_info()
+    ceiling = read_ceiling()
     wl = workload(2)
     dec = Decode(wl, N_POOL_COPIES, N_QSETS, keep_host=not args.no_cpu_baseline)
-    # every 8th timed step carries the dispatch events of the two kernels; a
-    # second pass without them shows what they cost
-    sec_per_step, t_score, t_split = dec.time_steps(args.steps, args.warmup, event_every=min(8, max(1, args.steps)))
-    sec_plain = dec.time_steps(args.steps, 0)
+    # the timed region (value): exactly `steps` steps, no instrumentation;
+    # then the same number of steps again with dispatch events on the scoring
+    # and attention kernels of every step, which give the kernels' durations
+    # (an event pair adds a few microseconds to its step, so those steps are
+    # not the ones the value is taken from)
+    sec_per_step = dec.time_steps(args.steps, args.warmup)
+    sec_events, t_score, t_split = dec.time_steps(args.steps, 0, event_every=1)
     t_topk, t_att = dec.time_kernels(20)
-    log(f"{wl.name}: {1 / sec_per_step:.1f} steps/s ({1 / sec_plain:.1f} without kernel events); scoring kernel "
+    log(f"{wl.name}: {1 / sec_per_step:.1f} steps/s ({1 / sec_events:.1f} with kernel events); scoring kernel "
         f"{t_score * 1e6:.1f} us, attention kernel {t_split * 1e6:.1f} us; indexer call {t_topk * 1e6:.1f} us, "
         f"attention call {t_att * 1e6:.1f} us")
     steps_per_s = 1.0 / sec_per_step
@@ -643,7 +754,9 @@ def main():
     roof = {"kernel": "k_indexer_score", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
             "alg_bytes_per_launch": dec.bytes_score, "groups_per_launch": dec.groups_scored,
-            "alg_bytes_per_group": 128, "avg_launch_us": round(t_score * 1e6, 2)}
+            "alg_bytes_per_group": 128, "avg_launch_us": round(t_score * 1e6, 2),
+            "event_samples": args.steps,
+            "frac_of_read_ceiling": round(achieved / ceiling["GBps"], 4)}
     result = {
         "metric": METRIC, "value": round(steps_per_s, 1), "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(sec_per_step * 1e3, 4), "higher_is_better": True,
@@ -653,8 +766,9 @@ def main():
         "achieved_hbm_GBps": round(dec.bytes_step * steps_per_s / 1e9, 1),
         "hbm_frac": round(dec.bytes_step * steps_per_s / 1e9 / HBM_PEAK_GBPS, 4),
         "alg_bytes_per_step": dec.bytes_step,
-        "steps_per_s_without_kernel_events": round(1.0 / sec_plain, 1),
+        "steps_per_s_with_kernel_events": round(1.0 / sec_events, 1),
         "roofline": roof,
+        "read_ceiling": ceiling,
         "kernels_us": {"k_indexer_score": round(t_score * 1e6, 2), "k_mla_split": round(t_split * 1e6, 2),
                        "isa_indexer_topk_call": round(t_topk * 1e6, 2),
                        "isa_sparse_mla_decode_call": round(t_att * 1e6, 2)},
@@ -672,20 +786,31 @@ def main():
         secondary["kda_decode"] = bench_kda()
     dec.free()
     if not args.primary_only:
-        for i in (1, 4):
+        for i in (0, 1, 4):
             w = workload(i)
-            d = Decode(w, 2, 4)
-            s = d.time_steps(50, 5)
+            d = Decode(w, N_POOL_COPIES, N_QSETS, keep_host=(i == 0 and not args.no_cpu_baseline))
+            s_ = d.time_steps(100, 10)
             tk, ta = d.time_kernels(10)
-            secondary[w.name] = {"steps_per_s": round(1 / s, 1), "ms_per_step": round(s * 1e3, 4),
-                                 "achieved_hbm_GBps": round(d.bytes_step / s / 1e9, 1),
-                                 "indexer_us": round(tk * 1e6, 2), "sparse_mla_us": round(ta * 1e6, 2),
-                                 "alg_bytes_per_step": d.bytes_step}
+            line = {"steps_per_s": round(1 / s_, 1), "ms_per_step": round(s_ * 1e3, 4),
+                    "achieved_hbm_GBps": round(d.bytes_step / s_ / 1e9, 1),
+                    "hbm_frac": round(d.bytes_step / s_ / 1e9 / HBM_PEAK_GBPS, 4),
+                    "indexer_us": round(tk * 1e6, 2), "sparse_mla_us": round(ta * 1e6, 2),
+                    "alg_bytes_per_step": d.bytes_step, "pooled_copies_rotated": N_POOL_COPIES,
+                    "query_sets_rotated": N_QSETS}
+            if i == 0:
+                line["note"] = "2.56 MB per step: launch- and latency-bound, no roofline claim"
+                if not args.no_cpu_baseline:
+                    result["cpu_baseline"]["single_thread_" + w.name] = oracle_single_thread_c0(d)
+            if i == 1:
+                line["fp8_latent"] = bench_fp8(d)
+                line["fp8_latent"]["sparse_mla_us_bf16"] = line["sparse_mla_us"]
+            secondary[w.name] = line
             d.free()
         secondary["prefill_scores"] = bench_prefill(args)
     result["secondary"] = secondary
-    result["env"] = {"device": torch.cuda.get_device_name(0), "torch": torch.__version__,
-                     "hip": getattr(torch.version, "hip", None)}
+    result["env"] = env
+    if "cpu_baseline" in result:
+        result["cpu_baseline"]["cpu_model"] = env.get("cpu_model")
     print(json.dumps(result), flush=True)
 
 

@@ -136,6 +136,16 @@ const char* isa_version(void);
 #define ISA_TIMER_MLA_SPLIT 2     /* main kernel of isa_sparse_mla_decode */
 isa_status isa_set_kernel_timer(int32_t kernel, void* const* starts, void* const* stops, int32_t n);
 
+/* Read-bandwidth probe, for benchmarks: reads every byte of `buf` ([dev],
+ * `bytes` a nonzero multiple of 16) once with 16-byte loads spread over the
+ * whole device.  *sink ([dev] uint32) is written only if the XOR of all words
+ * read equals 0x9E3779B9 (so that no load is dropped).  Its rate over a buffer
+ * larger than the on-package caches is the practical HBM read ceiling the
+ * kernels' rates can be set against.  clocks ([dev] uint64 [2], or NULL)
+ * receives the shader clock cycles (s_memtime) and 100 MHz reference ticks
+ * (s_memrealtime) that one wave spent, whose ratio is the shader clock. */
+isa_status isa_read_probe(const void* buf, size_t bytes, uint32_t* sink, uint64_t* clocks, isa_stream_t stream);
+
 #define ISA_SCALE_DYNAMIC 0u /* scales[b] := max|pooled| / 127 of sequence b (1 if all zero) */
 #define ISA_SCALE_GIVEN 1u   /* use scales[b] as given (> 0), single pass, clamp to +-127 */
 

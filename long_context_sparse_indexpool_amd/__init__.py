@@ -36,7 +36,8 @@ ISA_TIMER_INDEXER_SCORE, ISA_TIMER_MLA_SPLIT = 1, 2
 EXPORTS = ("isa_workspace_size", "isa_workspace_init", "isa_device_error", "isa_status_string", "isa_version",
            "isa_set_kernel_timer", "isa_indexpool", "isa_indexer_topk", "isa_sparse_mla_decode",
            "isa_sparse_mla_decode_shared", "isa_indexer_prefill_scores", "isa_append_token", "isa_latent_to_fp8",
-           "isa_sparse_mla_decode_fp8", "isa_kda_decode_step", "isa_indexer_topk_noalloc")
+           "isa_sparse_mla_decode_fp8", "isa_kda_decode_step", "isa_indexer_topk_noalloc",
+           "isa_read_probe")
 NOALLOC_TOPK_BYTES = 256 + (2 << 20) + 384 * (8 + 8192 + 65536)
 
 
@@ -69,6 +70,7 @@ def _load() -> ctypes.CDLL:
     lib.isa_indexpool.argtypes = [vp, vp, sp, vp, vp, u32, vp, sz, vp]
     lib.isa_indexer_topk.argtypes = [vp, vp, vp, sp, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.isa_indexer_topk_noalloc.argtypes = [vp, vp, vp, sp, i32, vp, vp, vp, i32, vp, vp]
+    lib.isa_read_probe.argtypes = [vp, sz, vp, vp, vp]
     lib.isa_sparse_mla_decode.argtypes = [vp, vp, sp, vp, vp, i32, vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.isa_sparse_mla_decode_shared.argtypes = [i32, vp, vp, sp, vp, vp, i32, vp, vp, i32, ctypes.c_float, vp, vp,
                                                  vp, sz, vp]
@@ -81,7 +83,7 @@ def _load() -> ctypes.CDLL:
     for f in ("isa_workspace_init", "isa_device_error", "isa_set_kernel_timer", "isa_indexpool", "isa_indexer_topk",
               "isa_sparse_mla_decode", "isa_sparse_mla_decode_shared", "isa_indexer_prefill_scores",
               "isa_append_token", "isa_latent_to_fp8", "isa_sparse_mla_decode_fp8", "isa_kda_decode_step",
-              "isa_indexer_topk_noalloc"):
+              "isa_indexer_topk_noalloc", "isa_read_probe"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -158,6 +160,14 @@ def isa_set_kernel_timer(kernel: int, starts: Sequence[torch.cuda.Event], stops:
     a = arr(*[e.cuda_event for e in starts]) if n else None
     b = arr(*[e.cuda_event for e in stops]) if n else None
     _check("isa_set_kernel_timer", lib.isa_set_kernel_timer(kernel, a, b, n))
+
+
+def isa_read_probe(buf: torch.Tensor, sink: torch.Tensor, clocks: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Read every byte of a device buffer once (HBM read-ceiling probe); sink: int32 [1];
+    clocks: int64 [2] (shader cycles, 100 MHz ticks of one wave) or None."""
+    _check("isa_read_probe", lib.isa_read_probe(_ptr(buf, buf.dtype, "buf"), buf.numel() * buf.element_size(),
+                                                _ptr(sink, torch.int32, "sink"), _ptr(clocks, torch.int64, "clocks"),
+                                                _stream(stream)))
 
 
 def isa_workspace_init(ws: torch.Tensor, stream=None) -> None:

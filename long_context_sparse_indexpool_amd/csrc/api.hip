@@ -110,6 +110,40 @@ __global__ void k_fill_zero(uint4* p, size_t n16) {
   for (; i < n16; i += stride) p[i] = make_uint4(0, 0, 0, 0);
 }
 
+// Read-bandwidth probe: every 16-byte chunk read once, grid-stride over the
+// whole device, eight loads in flight per thread.  The words read are XOR-ed
+// and the result stored only when it equals a value no caller supplies, so the
+// loads are kept without a stream of atomics to one address.  The first wave
+// also records the shader clock counter (s_memtime) and the 100 MHz constant
+// clock (s_memrealtime) at its start and end.
+__global__ __launch_bounds__(256) void k_read_probe(const uint4* __restrict__ p, size_t n16, uint32_t* sink,
+                                                    uint64_t* clocks) {
+  uint64_t t0 = 0, r0 = 0;
+  if (blockIdx.x == 0 && threadIdx.x < 64) {
+    t0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+  }
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t x = 0;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = p[i];
+    x ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (x == 0x9E3779B9u) sink[0] = x;
+  if (blockIdx.x == 0 && threadIdx.x == 0 && clocks) {
+    clocks[0] = __builtin_amdgcn_s_memtime() - t0;
+    clocks[1] = __builtin_amdgcn_s_memrealtime() - r0;
+  }
+}
+
 }  // namespace
 
 isa_status launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
@@ -241,6 +275,16 @@ size_t isa_workspace_size(int op, const isa_seqs* s, int32_t rows, int32_t cols)
       return HDR;
   }
   return 0;
+}
+
+isa_status isa_read_probe(const void* buf, size_t bytes, uint32_t* sink, uint64_t* clocks, isa_stream_t stream) {
+  if (!buf || !sink || !aligned16(buf) || ((uintptr_t)sink & 3) || ((uintptr_t)clocks & 7) || bytes == 0 ||
+      (bytes & 15))
+    return ISA_ERR_INVALID_ARG;
+  const unsigned grid = (unsigned)device_info().n_cu * 8;
+  hipLaunchKernelGGL(k_read_probe, dim3(grid), dim3(256), 0, (hipStream_t)stream, (const uint4*)buf, bytes / 16, sink,
+                     clocks);
+  return hipGetLastError() == hipSuccess ? ISA_OK : ISA_ERR_HIP;
 }
 
 isa_status isa_workspace_init(void* ws, size_t ws_bytes, isa_stream_t stream) {

@@ -32,10 +32,14 @@
 //    writes P to LDS as two fp16 terms, p_hi = fp16(p) and p_lo = fp16(p - p_hi),
 //    which together carry p to about 2^-22 relative.
 //  * Every wave then accumulates O[64 heads x its 64 channels] += P V^T with
-//    v_mfma_f32_16x16x32_f16 (heads = M, channels = N, the 32 tokens = K), once
-//    for p_hi and once for p_lo: the weighted sum stays accurate to fp32
-//    accumulation for large latent values, where fp16 probabilities alone
-//    would be off by 2^-11 of the largest value.
+//    v_mfma_f32_16x16x32_f16 (heads = M, channels = N, the 32 tokens = K) for
+//    p_hi, and once more for p_lo when the tile holds a latent value of at
+//    least PV_LO_MIN in magnitude: fp16 probabilities alone would be off by
+//    2^-11 of the largest value (at most 2^-8 below that bound), the pair keeps
+//    the weighted sum accurate to fp32 accumulation.  With bf16 rows each wave
+//    decides for its own 64 channels, from the V operands it has just read,
+//    with integer maxima that issue beside its MFMAs; with FP8 rows the owner
+//    waves decide from the row scales and raise a flag in LDS.
 // Two workgroup barriers per tile, both LDS-only; V is double-buffered.
 // A launch of at most 128 (row, split) units runs two workgroups per unit,
 // each with 32 of the heads (the same tile loads, half the MFMA and softmax
@@ -69,6 +73,7 @@ constexpr int BT_LDS = 1024;   // block-table entries of a row staged in LDS (se
                                // for longer rows staging costs more than the round trip it saves)
 constexpr int MAX_SPLITS = 32;
 constexpr float PART_F16_MAX = 16.f;  // partials below this magnitude are held in fp16
+constexpr float PV_LO_MIN = 8.f;      // a tile with a latent value this large takes the p_lo pass
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -157,6 +162,7 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
   __shared__ __attribute__((aligned(16))) float alpha_s[NH];
   __shared__ __attribute__((aligned(16))) uint32_t flag_s[8];
   __shared__ uint32_t big_s;  // a partial value reached PART_F16_MAX: the split's partial is held in fp32
+  __shared__ uint32_t vflag_s[2];  // FP8: per V buffer, the tile has a row scale of at least PV_LO_MIN / 448
   __shared__ float fin_s[2][NH];
   __shared__ __attribute__((aligned(16))) uint32_t trow[MAX_GPS * GROUP];  // latent row of each token slot, ~0 if not visible
   __shared__ int32_t bt_s[BT_LDS];                        // 4 KiB: the row's block-table entries
@@ -254,6 +260,7 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
   const int own_tq = lane >> 3;  // tokens 4 own_tq .. +3 of the tile
   if (tid < 8) flag_s[tid] = 0u;  // waves without softmax heads never set theirs
   if (tid == 0) big_s = 0u;
+  if (tid < 2) vflag_s[tid] = 0u;
   lds_barrier();  // token table complete
 
   const int nslot = ng * GROUP;
@@ -371,19 +378,38 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
       if (tq == 0) alpha_s[own_h] = alpha;
       if (lane == 0) flag_s[wave] = moved ? 1u : 0u;
       float ps = 0.f;
-      v4h ph, pl;
+      float pw[4];
+      v4h ph;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float pr = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[i] - m_ref);
         ps += pr;
-        float pw = pr;
-        if constexpr (FP8) pw = pr * st[i];  // the row scale enters P.V through P
-        ph[i] = (_Float16)pw;
-        pl[i] = (_Float16)(pw - (float)ph[i]);  // exact difference, rounded once
+        pw[i] = pr;
+        if constexpr (FP8) pw[i] = pr * st[i];  // the row scale enters P.V through P
+        ph[i] = (_Float16)pw[i];
       }
       l_run += ps;
       *reinterpret_cast<v4h*>(&pb[own_h * P_STRIDE + 4 * tq]) = ph;
-      *reinterpret_cast<v4h*>(&pbl[own_h * P_STRIDE + 4 * tq]) = pl;
+      // p_lo: always with bf16 rows (each wave decides in P.V whether it needs
+      // it); with FP8 rows only for a tile with a large row scale, which the
+      // owners flag (the flag of the other V buffer is cleared here: every
+      // wave has finished the tile that used it, and none can reach the next
+      // one before the barrier below)
+      bool lo = true;
+      if constexpr (FP8) {
+        lo = __any(!(st[0] * 448.f < PV_LO_MIN) || !(st[1] * 448.f < PV_LO_MIN) || !(st[2] * 448.f < PV_LO_MIN) ||
+                   !(st[3] * 448.f < PV_LO_MIN));
+        if (lane == 0) {
+          if (lo) vflag_s[vb] = 1u;
+          if (wave == 0) vflag_s[vb ^ 1] = 0u;
+        }
+      }
+      if (lo) {
+        v4h pl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pl[i] = (_Float16)(pw[i] - (float)ph[i]);  // exact difference, rounded once
+        *reinterpret_cast<v4h*>(&pbl[own_h * P_STRIDE + 4 * tq]) = pl;
+      }
       if constexpr (FP8) sbuf = *scales_of(t + 2);  // refill with tile t + 2, after the latent rows
     }
     lds_barrier();  // P, reference moves complete
@@ -416,28 +442,64 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
     auto p_op = [&](const _Float16* buf, int hb) -> v8h {
       return __builtin_bit_cast(v8h, *reinterpret_cast<const v4i*>(&buf[(hb * 16 + lq) * P_STRIDE + lg * 8]));
     };
+    // |v| >= PV_LO_MIN anywhere in this wave's V operands: fp16 magnitudes
+    // (sign cleared) compared as 16-bit integers, packed two per word
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    auto vmag = [&](u16x2 m, const v8h& v) -> u16x2 {
+      const v4i w = __builtin_bit_cast(v4i, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, (uint32_t)w[e] & 0x7FFF7FFFu));
+      return m;
+    };
+    auto large = [&](u16x2 m) -> bool {
+      constexpr unsigned short LIM = 0x4800;  // fp16 bits of PV_LO_MIN = 8
+      static_assert(PV_LO_MIN == 8.f, "LIM holds the fp16 bits of PV_LO_MIN");
+      return __builtin_amdgcn_readfirstlane(__any(m.x >= LIM || m.y >= LIM)) != 0;
+    };
+    bool lo = false;
+    if constexpr (FP8) lo = __builtin_amdgcn_readfirstlane(vflag_s[vb]) != 0u;
+    u16x2 mv = {0, 0};
     if constexpr (HB <= 2) {
-      // all V operands held; each head block's p_hi and p_lo in turn
+      // all V operands held; p_hi of each head block, then p_lo if needed
       v8h vv[NBLK];
 #pragma unroll
       for (int nb = 0; nb < NBLK; ++nb) vv[nb] = v_op(nb);
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
-        const v8h ph = p_op(pb, hb), pl = p_op(pbl, hb);
+        const v8h ph = p_op(pb, hb);
 #pragma unroll
-        for (int nb = 0; nb < NBLK; ++nb) o[hb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vv[nb], o[hb][nb], 0, 0, 0);
+        for (int nb = 0; nb < NBLK; ++nb) {
+          o[hb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vv[nb], o[hb][nb], 0, 0, 0);
+          if (!FP8 && hb == 0) mv = vmag(mv, vv[nb]);
+        }
+      }
+      if (!FP8) lo = large(mv);
+      if (lo) {
 #pragma unroll
-        for (int nb = 0; nb < NBLK; ++nb) o[hb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, vv[nb], o[hb][nb], 0, 0, 0);
+        for (int hb = 0; hb < HB; ++hb) {
+          const v8h pl = p_op(pbl, hb);
+#pragma unroll
+          for (int nb = 0; nb < NBLK; ++nb) o[hb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, vv[nb], o[hb][nb], 0, 0, 0);
+        }
       }
     } else {
-      // 64 heads: registers are short, so a p_hi pass and a p_lo pass, each
-      // holding one P term per head block and reading V again
+      // 64 heads: registers are short, so the p_lo pass reads V again
+      v8h pv[HB];
 #pragma unroll
-      for (int pass = 0; pass < 2; ++pass) {
-        asm volatile("" ::: "memory");  // V is read again in the second pass, not held in registers
-        v8h pv[HB];
+      for (int hb = 0; hb < HB; ++hb) pv[hb] = p_op(pb, hb);
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb) pv[hb] = p_op(pass ? pbl : pb, hb);
+      for (int nb = 0; nb < NBLK; ++nb) {
+        const v8h vv = v_op(nb);
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) o[hb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pv[hb], vv, o[hb][nb], 0, 0, 0);
+        if (!FP8) mv = vmag(mv, vv);
+      }
+      if (!FP8) lo = large(mv);
+      if (lo) {
+        asm volatile("" ::: "memory");  // V is read again, not held in registers
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) pv[hb] = p_op(pbl, hb);
 #pragma unroll
         for (int nb = 0; nb < NBLK; ++nb) {
           const v8h vv = v_op(nb);
@@ -534,21 +596,22 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
           big |= !(fabsf(o[hb][nb][i]) < PART_F16_MAX);  // NaN counts as large
         }
     }
+    // the fp16 copy is staged in any case; the barrier that publishes it also
+    // publishes whether any value was too large for it
     if (__any(big) && lane == 0) big_s = 1u;
+    _Float16* stage = &vt[0][0];
+    static_assert(2 * TILE_TOK * V_STRIDE >= NH * LAT_DIM, "staging fits in the V tiles");
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int nb = 0; nb < NBLK; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          stage[(hb * 16 + 4 * lg + i) * LAT_DIM + d_base + nb * 16 + lq] = (_Float16)o[hb][nb][i];
     __syncthreads();
     const bool f32 = big_s != 0u;  // uniform
     char* slot = P.o_part + (part * ATT_HEADS + h0) * (LAT_DIM * 4);  // 2 KiB per head
     if (!f32) {
-      _Float16* stage = &vt[0][0];
-      static_assert(2 * TILE_TOK * V_STRIDE >= NH * LAT_DIM, "staging fits in the V tiles");
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-        for (int nb = 0; nb < NBLK; ++nb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            stage[(hb * 16 + 4 * lg + i) * LAT_DIM + d_base + nb * 16 + lq] = (_Float16)o[hb][nb][i];
-      __syncthreads();
       constexpr int N16 = NH * LAT_DIM * 2 / 16;  // 16-B chunks, 64 per head
 #pragma unroll
       for (int k = 0; k < N16 / MLA_THREADS; ++k) {
