@@ -40,11 +40,10 @@
  *  - Workspace: `ws` [dev] of at least isa_workspace_size(...) bytes, zero-
  *    filled once before its first use (isa_workspace_init or any zero fill).
  *    Layout, the same for every call: the error word in the first 256 bytes,
- *    then a fixed 2 MiB region (ISA_MAX_BATCH x 2048 words of per-sequence
- *    candidate histograms) that only isa_indexer_topk uses and leaves zero
- *    after every call, then the call's own scratch, which it writes before it
- *    reads.  So one workspace may serve calls of any batch shape and be shared
- *    by different calls, provided it is as large as each call asks; calls that
+ *    then the call's own scratch, which the call writes before it reads it:
+ *    nothing but the error word carries over from one call to the next.  So
+ *    one workspace may serve calls of any batch shape and be shared by
+ *    different calls, provided it is as large as each call asks; calls that
  *    share a workspace must be ordered on one stream.
  *  - Errors: argument errors are reported synchronously by the return code
  *    before anything is enqueued.  Errors that depend on device data (a page
@@ -217,9 +216,10 @@ isa_status isa_indexer_topk(const int8_t* q, const int8_t* head_w, const int8_t*
  * tokens, 64 of 2^17 and the ragged 32-sequence batch fit).  Every call on one
  * GPU shares that GPU's array: calls that overlap in time on one GPU (other
  * streams, other threads) race and give wrong results; order them on one
- * stream.  Each call clears the histogram part it uses with a fill kernel.
+ * stream.  Nothing in the array has to start at zero: a call writes every
+ * part of it that it reads.
  */
-#define ISA_NOALLOC_TOPK_BYTES (256u + (2u << 20) + 384u * (8u + 8192u + 65536u))
+#define ISA_NOALLOC_TOPK_BYTES (256u + 384u * (8u + 8192u + 65536u))
 isa_status isa_indexer_topk_noalloc(const int8_t* q, const int8_t* head_w, const int8_t* pooled, const isa_seqs* s,
                                     int32_t k, int32_t* out_idx, int32_t* out_count, int32_t* scores_out,
                                     int32_t ld_scores, uint32_t* err_word, isa_stream_t stream);

@@ -12,15 +12,11 @@ namespace isa {
 namespace {
 
 // Workspace layout shared by every call: the sticky error word in the first
-// 256 bytes, then the per-sequence candidate histograms of the decode top-k
-// (ISA_MAX_BATCH x NBINS words, zero between calls), then the call's own
-// scratch.  The histograms sit at a fixed offset, so a workspace reused for a
-// different batch shape, or shared with another call, never places them on
-// data an earlier call left behind; no call writes that region except the
-// top-k, which leaves it zero again.
+// 256 bytes, then the call's own scratch, which every kernel writes before it
+// reads it within the same call -- nothing in it has to survive between calls,
+// so a workspace can be reused for any batch shape or shared between calls.
 constexpr size_t HDR = 256;
-constexpr size_t HIST_BYTES = (size_t)ISA_MAX_BATCH * NBINS * 4;
-constexpr size_t SCR0 = HDR + HIST_BYTES;
+constexpr size_t SCR0 = HDR;
 
 inline size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -76,14 +72,13 @@ int32_t decode_tile_g(const isa_seqs* s) {
 int pool_tiles(int32_t L) { return (int)((groups_of(L) + POOL_TILE_G - 1) / POOL_TILE_G); }
 
 struct DecodeLayout {
-  size_t tile_meta, tile_pairs, tile_list, seq_hist, total;
+  size_t tile_meta, tile_pairs, tile_list, total;
 };
 DecodeLayout decode_layout(const isa_seqs* s, int32_t k) {
   DecodeLayout d;
   const int32_t tg = decode_tile_g(s);
   int nt = 0;
   for (int b = 0; b < s->batch; ++b) nt += decode_tiles(s->seq_lens_host[b], k, tg);
-  d.seq_hist = HDR;
   d.tile_meta = SCR0;
   d.tile_pairs = d.tile_meta + up256((size_t)nt * 8);
   d.tile_list = d.tile_pairs + up256((size_t)nt * PAIR_CAP * 4);
@@ -208,8 +203,7 @@ isa_status decode_topk(const int8_t* q, const int8_t* head_w, const int8_t* pool
     t += decode_tiles(s->seq_lens_host[b], k, a.tile_g);
   }
   a.tile_start[s->batch] = t;
-  DecodeWs w{err, (uint2*)(base + d.tile_meta), (uint32_t*)(base + d.tile_pairs), (uint64_t*)(base + d.tile_list),
-             (uint32_t*)(base + d.seq_hist)};
+  DecodeWs w{err, (uint2*)(base + d.tile_meta), (uint32_t*)(base + d.tile_pairs), (uint64_t*)(base + d.tile_list)};
   return launch_indexer_decode(a, q, head_w, pooled, s->block_table, w, out_idx, out_count, scores_out, ld_scores,
                                stream);
 }
@@ -368,10 +362,6 @@ isa_status isa_indexer_topk_noalloc(const int8_t* q, const int8_t* head_w, const
     }
     base = addr[dev];
   }
-  // the histograms of this batch must start at zero whatever an earlier call
-  // left behind (a fill kernel, which graph capture records as a kernel node)
-  const isa_status z = launch_fill_zero(base + d.seq_hist, (size_t)s->batch * NBINS * 4, (hipStream_t)stream);
-  if (z != ISA_OK) return z;
   return decode_topk(q, head_w, pooled, s, k, out_idx, out_count, scores_out, ld_scores, d, base, err_word,
                      (hipStream_t)stream);
 }

@@ -28,10 +28,11 @@
 // k-th best, and writes every candidate from that bin up into a per-tile list
 // ordered by descending bin, plus the (bin, count) pairs of those bins.
 //
-// k_indexer_select: one workgroup per sequence.  It sums the tiles' pairs into
-// an LDS histogram, finds the global boundary bin, takes every candidate above
-// it, resolves the boundary bin exactly by radix select on (score, -id) keys,
-// sorts the k ids ascending and writes them.
+// k_indexer_select: one workgroup per sequence.  It sums the tiles' (bin,
+// count) pairs into an LDS histogram, finds the global boundary bin, takes
+// every candidate above it, resolves the boundary bin exactly on (score, -id)
+// keys, sorts the k ids ascending and writes them.  No state outlives a call:
+// the workspace holds only what the scoring kernel wrote in the same call.
 #include "isa_launch.hpp"
 #include "select_device.hpp"
 
@@ -52,7 +53,6 @@ struct DecodePtrs {
   uint2* tile_meta;     // [ntiles] (candidates, pairs)
   uint32_t* tile_pairs; // [ntiles][PAIR_CAP] (bin << 16 | count), descending bins
   uint64_t* tile_list;  // [ntiles][TILE_G] (score << 32 | group), descending bins
-  uint32_t* seq_hist;   // [B][NBINS] candidates per score bin, summed over the tiles; zero between calls
   int32_t* out_idx;     // [B][k]
   int32_t* out_count;   // [B]
   int32_t* scores_out;  // [B][ld] or null
@@ -185,7 +185,10 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
     }
   }
   if (__any(overflow) && lane == 0) report(P.err, ISA_DERR_SCORE_OVERFLOW);
-  __syncthreads();
+  // The epilogue's barriers order LDS only: waiting for global memory here
+  // (the last chunks' discarded loads, the pair and meta stores) would add its
+  // latency to every tile.
+  lds_barrier();
 
   if (dense) {  // only reached when scores were requested
     for (int i = tid; i < (int)K; i += DEC_THREADS) P.out_idx[(size_t)b * K + i] = i < G ? i : -1;
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
   const uint32_t packed = local | (nzl << 16);
   const uint32_t xin = wave_inclusive_scan(packed);
   if (lane == 63) scr[wave] = xin;
-  __syncthreads();
+  lds_barrier();
   uint32_t above = xin - packed, all = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
@@ -229,26 +232,20 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
     scr[SCR_RES + 1] = in_hi ? run_hi + c_hi : run_hi + local;
     scr[SCR_RES + 2] = in_hi ? pz_hi + 1u : pz_hi + nzl;
   }
-  __syncthreads();
+  lds_barrier();
   const int blo = (int)scr[SCR_RES];
   uint32_t* pairs = P.tile_pairs + (size_t)tile * PAIR_CAP;
-  // kept bins, descending: (bin, count) pairs, the sequence histogram, emission cursors
+  // kept bins, descending: (bin, count) pairs and emission cursors
   if (hb - 1 >= blo) {
-    if (c_hi) {
-      pairs[pz_hi] = ((uint32_t)(hb - 1) << 16) | c_hi;
-      atomicAdd(&P.seq_hist[(size_t)b * NBINS + hb - 1], c_hi);
-    }
+    if (c_hi) pairs[pz_hi] = ((uint32_t)(hb - 1) << 16) | c_hi;
     hist[hb - 1] = run_hi;
   }
   if (hb - 2 >= blo) {
-    if (c_lo) {
-      pairs[pz_hi + (c_hi != 0u)] = ((uint32_t)(hb - 2) << 16) | c_lo;
-      atomicAdd(&P.seq_hist[(size_t)b * NBINS + hb - 2], c_lo);
-    }
+    if (c_lo) pairs[pz_hi + (c_hi != 0u)] = ((uint32_t)(hb - 2) << 16) | c_lo;
     hist[hb - 2] = run_hi + c_hi;
   }
   if (tid == 0) P.tile_meta[tile] = make_uint2(scr[SCR_RES + 1], scr[SCR_RES + 2]);
-  __syncthreads();
+  lds_barrier();
   uint64_t* list = P.tile_list + (size_t)tile * TILE_G;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
@@ -302,6 +299,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
   __shared__ uint32_t bcnt[SEL_BUCKETS];
   __shared__ uint32_t bbase[SEL_BUCKETS];
   __shared__ uint32_t bstage[MAX_K];
+  __shared__ __attribute__((aligned(16))) uint32_t shist[NBINS];  // candidates per score bin over the tiles
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int NWV = SEL_THREADS / 64;
@@ -318,15 +316,13 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
   static_assert(SEL_LDS_HEAD / 32 >= TILE_MAX_PER_SEQ, "list heads of every tile fit");
   const int pu_per_tile = per / 4, hu_per_tile = lh / 2;
 
-  // 1. one batch of loads: the sequence's candidate histogram (summed by the
-  //    scoring tiles), every tile's pair count, the head of its (bin, count)
-  //    list and the head of its candidate list
-  //    (thread t holds bins NBINS - 4t - 4 .. NBINS - 4t - 1: ascending threads
-  //    walk the bins in descending order)
+  // 1. one batch of loads: every tile's pair count, the head of its (bin,
+  //    count) list and the head of its candidate list; the pairs are summed
+  //    into an LDS histogram (thread t then holds bins NBINS - 4t - 4 ..
+  //    NBINS - 4t - 1: ascending threads walk the bins in descending order)
   static_assert(NBINS == 4 * SEL_THREADS, "one uint4 of the histogram per thread");
-  uint4* gh = reinterpret_cast<uint4*>(P.seq_hist + (size_t)b * NBINS);
   const int hq = SEL_THREADS - 1 - tid;
-  const uint4 hcnt = gh[hq];
+  reinterpret_cast<uint4*>(shist)[tid] = uint4{0u, 0u, 0u, 0u};
   constexpr int UP = SEL_LDS_PAIRS / 4 / SEL_THREADS, UH = SEL_LDS_HEAD / 2 / SEL_THREADS;
   uint4 pv[UP], hv[UH];
   uint32_t pnp[UP];
@@ -350,12 +346,12 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
   }
   uint32_t my_np = 0;
   if (tid < nt) my_np = P.tile_meta[t0 + tid].y;
-  gh[hq] = uint4{0u, 0u, 0u, 0u};  // the histogram is zero again for the next call
   for (int i = tid; i < SEL_BUCKETS; i += SEL_THREADS) bcnt[i] = 0;
   if (tid < nt) {
     ngt[tid] = 0;
     nbd[tid] = 0;
   }
+  lds_barrier();  // histogram zero (the loads stay in flight)
 #pragma unroll
   for (int k = 0; k < UP; ++k) {
     const int u = tid + k * SEL_THREADS;
@@ -364,7 +360,10 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
       const uint32_t w[4] = {pv[k].x, pv[k].y, pv[k].z, pv[k].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (part * 4 + e < (int)pnp[k]) lpairs[j * per + part * 4 + e] = w[e];
+        if (part * 4 + e < (int)pnp[k]) {
+          lpairs[j * per + part * 4 + e] = w[e];
+          atomicAdd(&shist[w[e] >> 16], w[e] & 0xFFFFu);
+        }
     }
   }
 #pragma unroll
@@ -376,12 +375,9 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
       lhead[j * lh + part * 2 + 1] = ((uint64_t)hv[k].w << 32) | hv[k].z;
     }
   }
-  // Suffix counts of the histogram by wave, and the offsets of the pairs
-  // beyond a tile's LDS slice (rare: a tile spread over more than `per` bins),
-  // which are read again from global memory as one flat range over tiles.
-  const uint32_t local = hcnt.x + hcnt.y + hcnt.z + hcnt.w;
-  const uint32_t xin = wave_inclusive_scan(local);
-  if (lane == 63) scr[wave] = xin;
+  // The offsets of the pairs beyond a tile's LDS slice (rare: a tile spread
+  // over more than `per` bins), which are read from global memory as one flat
+  // range over tiles.
   const uint32_t o = (tid < nt && my_np > (uint32_t)per) ? my_np - per : 0u;
   if (tid < nt) npr[tid] = my_np;
   if (nt <= 64 && wave == 0) {
@@ -390,7 +386,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
     if (tid < nt) ovf_off[tid] = e;
     if (tid == 0) ovf_off[nt] = tot;
   }
-  __syncthreads();  // pairs, list heads, wave sums and offsets published
+  __syncthreads();  // pairs, list heads and offsets published
   if (nt > 64) {    // uniform: more tiles than one wave scans
     uint32_t tot;
     const uint32_t e = block_exclusive_scan(o, scr + NWV, &tot);
@@ -398,6 +394,21 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
     if (tid == 0) ovf_off[nt] = tot;
     __syncthreads();
   }
+  const uint32_t novf = ovf_off[nt];
+  if (novf) {  // uniform: the pairs past the LDS slices enter the histogram too
+    for (uint32_t i = tid; i < novf; i += SEL_THREADS) {
+      const int j = owner_of(ovf_off, nt, i);
+      const uint32_t w = P.tile_pairs[(size_t)(t0 + j) * PAIR_CAP + per + (i - ovf_off[j])];
+      atomicAdd(&shist[w >> 16], w & 0xFFFFu);
+    }
+    lds_barrier();
+  }
+  // suffix counts of the histogram by wave
+  const uint4 hcnt = reinterpret_cast<const uint4*>(shist)[hq];
+  const uint32_t local = hcnt.x + hcnt.y + hcnt.z + hcnt.w;
+  const uint32_t xin = wave_inclusive_scan(local);
+  if (lane == 63) scr[wave] = xin;
+  lds_barrier();
   // the boundary: the highest bin whose suffix count reaches k
   int bstar;
   uint32_t n_gt, total = 0, above = xin - local;
@@ -429,7 +440,6 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
   n_gt = scr[SCR_RES + 1];
   // bstar >= 0: the tiles together kept at least k candidates.
   const uint32_t m = K - n_gt;
-  const uint32_t novf = ovf_off[nt];
   // 2. per tile: candidates above the boundary bin and in it, one thread per
   //    LDS pair (a tile's pairs cover distinct bins; at most one is the boundary's)
   for (int i = tid; i < nt * per; i += SEL_THREADS) {
@@ -612,7 +622,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
 isa_status launch_indexer_decode(const BatchArgs& a, const int8_t* q, const int8_t* hw, const int8_t* pooled,
                                  const int32_t* bt, const DecodeWs& w, int32_t* out_idx, int32_t* out_count,
                                  int32_t* scores_out, int32_t ld_scores, hipStream_t stream) {
-  DecodePtrs P{q, hw, pooled, bt, w.tile_meta, w.tile_pairs, w.tile_list, w.seq_hist, out_idx, out_count,
+  DecodePtrs P{q, hw, pooled, bt, w.tile_meta, w.tile_pairs, w.tile_list, out_idx, out_count,
                scores_out, ld_scores, w.err};
   const int ntiles = a.tile_start[a.batch];
   if (launch_timed(ISA_TIMER_INDEXER_SCORE, k_indexer_score, dim3(ntiles), dim3(DEC_THREADS), stream, a, P) !=

@@ -30,7 +30,6 @@ struct DecodeWs {
   uint2* tile_meta;      // [ntiles] (candidates kept, pairs)
   uint32_t* tile_pairs;  // [ntiles][PAIR_CAP]
   uint64_t* tile_list;   // [ntiles][TILE_G]
-  uint32_t* seq_hist;    // [B][NBINS], zero between calls
 };
 
 isa_status launch_indexer_decode(const BatchArgs& a, const int8_t* q, const int8_t* hw, const int8_t* pooled,
