@@ -111,7 +111,7 @@ __global__ void k_fill_zero(uint4* p, size_t n16) {
 // loads are kept without a stream of atomics to one address.  The first wave
 // also records the shader clock counter (s_memtime) and the 100 MHz constant
 // clock (s_memrealtime) at its start and end.
-__global__ __launch_bounds__(256) void k_read_probe(const uint4* __restrict__ p, size_t n16, uint32_t* sink,
+__global__ __launch_bounds__(1024) void k_read_probe(const uint4* __restrict__ p, size_t n16, uint32_t* sink,
                                                     uint64_t* clocks) {
   uint64_t t0 = 0, r0 = 0;
   if (blockIdx.x == 0 && threadIdx.x < 64) {
@@ -275,8 +275,10 @@ isa_status isa_read_probe(const void* buf, size_t bytes, uint32_t* sink, uint64_
   if (!buf || !sink || !aligned16(buf) || ((uintptr_t)sink & 3) || ((uintptr_t)clocks & 7) || bytes == 0 ||
       (bytes & 15))
     return ISA_ERR_INVALID_ARG;
-  const unsigned grid = (unsigned)device_info().n_cu * 8;
-  hipLaunchKernelGGL(k_read_probe, dim3(grid), dim3(256), 0, (hipStream_t)stream, (const uint4*)buf, bytes / 16, sink,
+  // one 1024-thread workgroup per CU: of the shapes tried, the fastest for a
+  // plain read (more, smaller workgroups reach less)
+  const unsigned grid = (unsigned)device_info().n_cu;
+  hipLaunchKernelGGL(k_read_probe, dim3(grid), dim3(1024), 0, (hipStream_t)stream, (const uint4*)buf, bytes / 16, sink,
                      clocks);
   return hipGetLastError() == hipSuccess ? ISA_OK : ISA_ERR_HIP;
 }
