@@ -44,6 +44,7 @@ constexpr int SEL_CAND = 2048;           // boundary candidates resolved in LDS
 constexpr int SEL_LDS_PAIRS = 8192;      // (bin, count) pairs fetched into LDS in the first round
 constexpr int SEL_LDS_HEAD = 4096;       // candidate-list entries fetched into LDS in the first round
 constexpr int SEL_BUCKETS = 1024;        // id buckets of the final ascending order
+constexpr int SEL_REFINE = 128;          // boundary lists longer than this take one more histogram level
 
 struct DecodePtrs {
   const int8_t* q;
@@ -284,7 +285,7 @@ __device__ __forceinline__ int owner_of(const uint32_t* off, int n, uint32_t i) 
 //     in LDS, or radix select when there are too many -- and the k ids are
 //     placed in ascending order by counting, straight into the output row.
 __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs a, const DecodePtrs P) {
-  __shared__ uint32_t lpairs[SEL_LDS_PAIRS];
+  __shared__ __attribute__((aligned(16))) uint32_t lpairs[SEL_LDS_PAIRS];  // later: the sub-boundary keys
   __shared__ uint64_t lhead[SEL_LDS_HEAD];
   __shared__ uint32_t npr[TILE_MAX_PER_SEQ];
   __shared__ uint32_t ovf_off[TILE_MAX_PER_SEQ + 1];
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
   __shared__ uint32_t nbd[TILE_MAX_PER_SEQ];
   __shared__ __attribute__((aligned(16))) uint64_t cand[SEL_CAND + 2];
   __shared__ uint32_t sel[MAX_K];
-  __shared__ uint32_t h256[256];
+  __shared__ __attribute__((aligned(16))) uint32_t h256[256];
   __shared__ uint32_t scr[SCR_WORDS];
   __shared__ uint32_t bcnt[SEL_BUCKETS];
   __shared__ uint32_t bbase[SEL_BUCKETS];
@@ -311,9 +312,11 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
   const int nt = a.tile_start[b + 1] - t0;
   constexpr int per = SEL_LDS_PAIRS / TILE_MAX_PER_SEQ;  // pairs of a tile kept in LDS
   static_assert(per == 64, "one pair per lane of a wave");
-  const int lh_sh = nt <= SEL_LDS_HEAD / 64 ? 6 : 5;     // candidates of a tile kept in LDS: 64, or 32
+  // candidates of a tile kept in LDS: the head space shared by the tiles (a
+  // power of two per tile, at most 512)
+  const int lh_sh = min(9, 12 - (nt <= 1 ? 0 : 32 - __clz(nt - 1)));
   const int lh = 1 << lh_sh;
-  static_assert(SEL_LDS_HEAD / 32 >= TILE_MAX_PER_SEQ, "list heads of every tile fit");
+  static_assert(SEL_LDS_HEAD == 1 << 12 && SEL_LDS_HEAD / 32 >= TILE_MAX_PER_SEQ, "list heads of every tile fit");
   const int pu_per_tile = per / 4, hu_per_tile = lh / 2;
 
   // 1. one batch of loads: every tile's pair count, the head of its (bin,
@@ -323,6 +326,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
   static_assert(NBINS == 4 * SEL_THREADS, "one uint4 of the histogram per thread");
   const int hq = SEL_THREADS - 1 - tid;
   reinterpret_cast<uint4*>(shist)[tid] = uint4{0u, 0u, 0u, 0u};
+  if (tid < 64) reinterpret_cast<uint4*>(h256)[tid] = uint4{0u, 0u, 0u, 0u};
   constexpr int UP = SEL_LDS_PAIRS / 4 / SEL_THREADS, UH = SEL_LDS_HEAD / 2 / SEL_THREADS;
   uint4 pv[UP], hv[UH];
   uint32_t pnp[UP];
@@ -347,10 +351,6 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
   uint32_t my_np = 0;
   if (tid < nt) my_np = P.tile_meta[t0 + tid].y;
   for (int i = tid; i < SEL_BUCKETS; i += SEL_THREADS) bcnt[i] = 0;
-  if (tid < nt) {
-    ngt[tid] = 0;
-    nbd[tid] = 0;
-  }
   lds_barrier();  // histogram zero (the loads stay in flight)
 #pragma unroll
   for (int k = 0; k < UP; ++k) {
@@ -440,15 +440,18 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
   n_gt = scr[SCR_RES + 1];
   // bstar >= 0: the tiles together kept at least k candidates.
   const uint32_t m = K - n_gt;
-  // 2. per tile: candidates above the boundary bin and in it, one thread per
-  //    LDS pair (a tile's pairs cover distinct bins; at most one is the boundary's)
-  for (int i = tid; i < nt * per; i += SEL_THREADS) {
-    const int j = i / per, p = i % per;
-    if ((uint32_t)p < npr[j]) {
-      const uint32_t w = lpairs[i];
-      const int bin = (int)(w >> 16);
-      if (bin > bstar) atomicAdd(&ngt[j], w & 0xFFFFu);
-      else if (bin == bstar) nbd[j] = w & 0xFFFFu;
+  // 2. per tile: candidates above the boundary bin and in it, one wave per
+  //    tile, a lane per LDS pair (a tile's pairs cover distinct bins; at most
+  //    one is the boundary's), summed across the wave
+  for (int j = wave; j < nt; j += NWV) {
+    const bool v = (uint32_t)lane < npr[j];
+    const uint32_t w = v ? lpairs[j * per + lane] : 0u;
+    const int bin = (int)(w >> 16);
+    const uint32_t g_ = wave_inclusive_scan(v && bin > bstar ? w & 0xFFFFu : 0u);
+    const uint32_t d_ = wave_inclusive_scan(v && bin == bstar ? w & 0xFFFFu : 0u);
+    if (lane == 63) {
+      ngt[j] = g_;
+      nbd[j] = d_;
     }
   }
   __syncthreads();
@@ -460,10 +463,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
     else if (bin == bstar) nbd[j] = w & 0xFFFFu;
   }
   if (novf) __syncthreads();  // uniform
-  // offsets of each tile's candidates in the selection and the boundary list;
-  // whether a tile has candidates past its LDS head (counted as if every
-  // boundary entry were copied, which covers both resolve paths)
-  if (tid == 0) scr[SCR_RES + 4] = 0;
+  // offsets of each tile's candidates in the selection and the boundary list
   if (nt <= 64) {  // uniform: one wave scans the tiles
     if (wave == 0) {
       const uint32_t g_ = tid < nt ? ngt[tid] : 0u, d_ = tid < nt ? nbd[tid] : 0u;
@@ -478,7 +478,6 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
         sure_off[nt] = tg;
         bnd_off[nt] = tb;
       }
-      if (__any(g_ + d_ > (uint32_t)lh) && tid == 0) scr[SCR_RES + 4] = 1;
     }
   } else {
     const uint32_t g_ = tid < nt ? ngt[tid] : 0u, d_ = tid < nt ? nbd[tid] : 0u;
@@ -493,10 +492,8 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
       sure_off[nt] = tg;
       bnd_off[nt] = tb;
     }
-    if (g_ + d_ > (uint32_t)lh) scr[SCR_RES + 4] = 1;
   }
   __syncthreads();
-  const bool past_head = scr[SCR_RES + 4] != 0;
   // 3. candidates: one wave per tile copies the tile's entries above the
   //    boundary bin to the selection and its boundary-bin entries (as
   //    (score, -id) keys) to the boundary list (both are prefixes of the
@@ -512,22 +509,16 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
     return ((uint64_t)w.y << 32) | w.x;
   };
   const bool in_lds = nbnd <= SEL_CAND;
-  auto put = [&](int j, uint32_t e, uint64_t ent) {
-    const uint32_t gj = ngt[j];
-    if (e < gj) sel[sure_off[j] + e] = (uint32_t)ent;
-    else cand[bnd_off[j] + (e - gj)] = rank_key(key_score(ent), (uint32_t)ent);
-  };
-  // one thread per LDS head entry, then the entries past a head (rare) from
-  // global memory, one wave per tile
-  for (int i = tid; i < nt * lh; i += SEL_THREADS) {
-    const int j = i >> lh_sh;
-    const uint32_t e = (uint32_t)(i & (lh - 1));
-    if (e < ngt[j] + (in_lds ? nbd[j] : 0u)) put(j, e, lhead[i]);
-  }
-  if (past_head) {  // uniform
-    for (int j = wave; j < nt; j += NWV) {
-      const uint32_t nj = ngt[j] + (in_lds ? nbd[j] : 0u);
-      for (uint32_t e = lh + lane; e < nj; e += 64) put(j, e, entry(j, e));
+  // one wave per tile, a lane per entry (entries past the tile's LDS head come
+  // from global memory)
+  for (int j = wave; j < nt; j += NWV) {
+    const uint32_t gj = ngt[j], nj = gj + (in_lds ? nbd[j] : 0u);
+    const uint32_t so = sure_off[j], bo = bnd_off[j];
+#pragma unroll 2
+    for (uint32_t e = lane; e < nj; e += 64) {
+      const uint64_t ent = entry(j, e);
+      if (e < gj) sel[so + e] = (uint32_t)ent;
+      else cand[bo + (e - gj)] = rank_key(key_score(ent), (uint32_t)ent);
     }
   }
   if (tid == 0 && in_lds && (nbnd & 1)) cand[nbnd] = 0;  // pad to an even count for paired reads (ranks below all)
@@ -540,21 +531,75 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
   __syncthreads();
   // 4. the m best boundary candidates
   if (in_lds) {
-    // all-pairs rank: T adjacent lanes per candidate (T = 1 .. 64, the most
-    // that keeps every candidate in one pass when there are few), each
-    // counting over every T-th pair of keys, summed across the T lanes
-    const uint32_t npair = (nbnd + 1) / 2;
-    const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(cand);
+    const uint64_t* rk = cand;  // keys to rank, how many, how many to take, where they go
+    uint32_t nr = nbnd, mr = m, out0 = nsure;
+    if (nbnd > (uint32_t)SEL_REFINE) {  // uniform
+      // one more histogram level on the 8 score bits below the boundary bin's
+      // resolution (inside a bin every score shares the bits above them, so
+      // the level is monotone in the score; a bin below 64 holds one score and
+      // one sub-bin): entries of higher sub-bins are selected outright, the
+      // sub-boundary's go to a short list that is ranked in full
+      const int sh = bstar < 64 ? 0 : max((bstar >> 6) + 5 - 14, 0);
+      for (uint32_t i = tid; i < nbnd; i += SEL_THREADS) atomicAdd(&h256[(key_score(cand[i]) >> sh) & 255u], 1u);
+      lds_barrier();
+      if (wave == 0) {  // lane l holds sub-bins 4(63 - l) .. +3: ascending lanes walk down
+        const uint4 c = reinterpret_cast<const uint4*>(h256)[63 - lane];
+        const uint32_t loc = c.x + c.y + c.z + c.w;
+        const uint32_t above = wave_inclusive_scan(loc) - loc;
+        if (above < m && above + loc >= m) {
+          const uint32_t c4[4] = {c.w, c.z, c.y, c.x};
+          uint32_t run = above;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (run + c4[j] >= m) {
+              scr[SCR_RES + 5] = (uint32_t)(4 * (63 - lane) + 3 - j);
+              scr[SCR_RES + 6] = run;
+              break;
+            }
+            run += c4[j];
+          }
+        }
+        if (lane == 0) {
+          scr[SCR_RES + 7] = 0;  // append cursors: outright, sub-boundary
+          scr[SCR_RES + 8] = 0;
+        }
+      }
+      lds_barrier();
+      const uint32_t sb = scr[SCR_RES + 5], n_above = scr[SCR_RES + 6];
+      uint64_t* sub = reinterpret_cast<uint64_t*>(lpairs);  // the pairs are dead by now
+      static_assert(SEL_LDS_PAIRS * 4 >= (SEL_CAND + 2) * 8, "sub-boundary list fits in the pair space");
+      for (uint32_t i = tid - lane; i < nbnd; i += SEL_THREADS) {  // whole waves (ballots)
+        const bool v = i + lane < nbnd;
+        const uint64_t key = v ? cand[i + lane] : 0ull;
+        const uint32_t sk = (key_score(key) >> sh) & 255u;
+        const uint32_t ph = wave_append(v && sk > sb, &scr[SCR_RES + 7]);
+        const uint32_t pe = wave_append(v && sk == sb, &scr[SCR_RES + 8]);
+        if (v && sk > sb) sel[nsure + ph] = key_id(key);
+        else if (v && sk == sb) sub[pe] = key;
+      }
+      lds_barrier();
+      nr = scr[SCR_RES + 8];
+      if (tid == 0 && (nr & 1)) sub[nr] = 0;  // even count for paired reads (ranks below all)
+      lds_barrier();
+      rk = sub;
+      mr = m - n_above;
+      out0 = nsure + n_above;
+    }
+    // all-pairs rank: T adjacent lanes per key (T = 1 .. 64, the most that
+    // keeps every key in one pass when there are few), each counting over
+    // every T-th pair of keys, summed across the T lanes
+    const uint32_t npair = (nr + 1) / 2;
+    const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(rk);
     int T = 1;
-    while (T < 64 && nbnd * (uint32_t)T * 2 <= (uint32_t)SEL_THREADS) T *= 2;
+    while (T < 64 && nr * (uint32_t)T * 2 <= (uint32_t)SEL_THREADS) T *= 2;
     const int per_pass = SEL_THREADS / T;
-    for (uint32_t base = 0; base < nbnd; base += per_pass) {  // uniform
+    for (uint32_t base = 0; base < nr; base += per_pass) {  // uniform
       const uint32_t i = base + tid / T;
       const int part = tid % T;
       uint32_t rank = 0;
       uint64_t ki = 0;
-      if (i < nbnd) {
-        ki = cand[i];
+      if (i < nr) {
+        ki = rk[i];
 #pragma unroll 4
         for (uint32_t j = part; j < npair; j += T) {
           const ulonglong2 v = c2[j];
@@ -562,7 +607,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
         }
       }
       for (int o = 1; o < T; o <<= 1) rank += __shfl_xor(rank, o, 64);
-      if (i < nbnd && part == 0 && rank < m) sel[nsure + rank] = key_id(ki);
+      if (i < nr && part == 0 && rank < mr) sel[out0 + rank] = key_id(ki);
     }
   } else {
     const uint64_t thr = radix_select_threshold(

@@ -16,6 +16,18 @@ __device__ __forceinline__ uint64_t rank_key(uint32_t score, uint32_t id) {
 __device__ __forceinline__ uint32_t key_id(uint64_t key) { return 0xFFFFFFFFu - (uint32_t)key; }
 __device__ __forceinline__ uint32_t key_score(uint64_t key) { return (uint32_t)(key >> 32); }
 
+// Appends the lanes whose pred holds to a list with one LDS atomic per wave:
+// returns this lane's slot (the wave's base plus its rank among the appending
+// lanes).  Every lane of the wave calls it.
+__device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* counter) {
+  const unsigned long long mask = __ballot(pred);
+  const uint32_t n = (uint32_t)__popcll(mask);
+  uint32_t base = 0;
+  if ((threadIdx.x & 63) == 0 && n) base = atomicAdd(counter, n);
+  base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+  return base + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
 // LDS scratch layout used below: words [0, 17) by block_exclusive_scan, results
 // at RES.. .
 constexpr int SCR_WORDS = 64;

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import synth
-from synth.configs import IDX_DIM, LAT_DIM, SM_SCALE, custom
+from synth.configs import IDX_DIM, LAT_DIM, SM_SCALE, _to_bf16_bits, custom
 
 import harness as H
 
@@ -130,6 +130,49 @@ def test_topk_ties_from_repeated_keys():
             assert len(np.unique(S)) <= 3
             assert np.array_equal(sc[b, : db.wl.groups(b)].astype(np.int64), S)
             H.check_topk_row(S, k, idx[b], int(cnt[b]))
+
+
+def _score_bin(s: int) -> int:
+    """The selection's 11-bit monotone histogram key of a score (exact below 64,
+    then 64 sub-bins per octave), to check that an input reaches a given path."""
+    s = int(s)
+    if s < 64:
+        return s
+    e = s.bit_length() - 1
+    return ((e - 5) << 6) | ((s >> (e - 6)) & 63)
+
+
+def test_topk_boundary_bin_refined():
+    """Several hundred candidates share the boundary histogram bin, with 15
+    distinct scores and dozens of exact ties among them: the boundary bin takes
+    the second histogram level, and its sub-boundary is ranked on (score, id).
+    Groups are copies of one key row with four channels moved by 0.02 per step
+    (0..24 steps), placed at random over the sequence's scoring tiles plus a
+    run of 700 at its end (more candidates in the last tile than its list head
+    in LDS holds); every other key is zero.  Selected ids bit-exact against the oracle at k =
+    512 and k = 100."""
+    L, seed = 40000, 42
+    G = L // 4
+    base = synth.bf16_to_f32(synth.normal_bf16(seed, 1, (IDX_DIM,)))
+    pos = np.unique(np.concatenate([synth.uniform_i64(seed, 2, (700,), 0, G - 1), np.arange(G - 700, G)]))
+    steps = synth.uniform_i64(seed, 3, (len(pos),), 0, 24)
+    rows = np.repeat(base[None, :], len(pos), axis=0)
+    rows[:, :4] += 0.02 * steps[:, None]
+    bits = _to_bf16_bits(rows)
+    keys = np.zeros((L, IDX_DIM), np.uint16)
+    for t in range(4):
+        keys[pos * 4 + t] = bits
+    db = _batch_with_keys("refine", [L], keys, seed=seed)
+    res = {k: H.run_topk(db, k=k) for k in (512, 100)}
+    S = H.oracle_scores_for(db, 0)
+    bins = np.array([_score_bin(x) for x in S])
+    for k in (512, 100):
+        bstar = np.sort(bins)[::-1][k - 1]
+        nb = int((bins == bstar).sum())
+        assert 128 < nb <= 2048 and len(np.unique(S[bins == bstar])) > 2, "input must reach the refined boundary"
+        idx, cnt, sc, _ = res[k]
+        assert np.array_equal(sc[0, :G].astype(np.int64), S)
+        H.check_topk_row(S, k, idx[0], int(cnt[0]))
 
 
 def test_topk_all_scores_equal():
