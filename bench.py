@@ -487,7 +487,8 @@ def read_ceiling(n_buf=4, buf_bytes=512 << 20, reps=24):
     log(f"read ceiling: {gbps:.0f} GB/s ({buf_bytes >> 20} MiB per read, {n_buf} buffers rotated); "
         f"shader clock during the probe {ghz} GHz")
     return {"GBps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4), "bytes_per_read": buf_bytes,
-            "buffers_rotated": n_buf, "kernel": "isa_read_probe (16-B loads, grid-stride over the device)",
+            "buffers_rotated": n_buf,
+            "kernel": "isa_read_probe (one workgroup per CU, contiguous shares, wave-wide non-temporal 16-B loads)",
             "shader_clock_GHz_during_probe": round(ghz, 3) if ghz else None}
 
 

@@ -136,8 +136,9 @@ const char* isa_version(void);
 isa_status isa_set_kernel_timer(int32_t kernel, void* const* starts, void* const* stops, int32_t n);
 
 /* Read-bandwidth probe, for benchmarks: reads every byte of `buf` ([dev],
- * `bytes` a nonzero multiple of 16) once with 16-byte loads spread over the
- * whole device.  *sink ([dev] uint32) is written only if the XOR of all words
+ * `bytes` a nonzero multiple of 16) once, one workgroup per CU streaming a
+ * contiguous share in 4-KiB chunks of wave-wide non-temporal 16-byte loads
+ * (the decode scoring stream's access shape).  *sink ([dev] uint32) is written only if the XOR of all words
  * read equals 0x9E3779B9 (so that no load is dropped).  Its rate over a buffer
  * larger than the on-package caches is the practical HBM read ceiling the
  * kernels' rates can be set against.  clocks ([dev] uint64 [2], or NULL)

@@ -105,12 +105,15 @@ __global__ void k_fill_zero(uint4* p, size_t n16) {
   for (; i < n16; i += stride) p[i] = make_uint4(0, 0, 0, 0);
 }
 
-// Read-bandwidth probe: every 16-byte chunk read once, grid-stride over the
-// whole device, eight loads in flight per thread.  The words read are XOR-ed
-// and the result stored only when it equals a value no caller supplies, so the
-// loads are kept without a stream of atomics to one address.  The first wave
-// also records the shader clock counter (s_memtime) and the 100 MHz constant
-// clock (s_memrealtime) at its start and end.
+// Read-bandwidth probe: every 16-byte unit read once.  Workgroup w streams a
+// contiguous share of the buffer in 4-KiB chunks (the waves taking chunks in
+// turn, two in flight per wave), each chunk as four wave-wide 1-KiB
+// non-temporal loads -- the access shape of the decode scoring stream; a tail
+// shorter than a chunk is read by the first workgroup.  The words read are
+// XOR-ed and the result stored only when it equals a value no caller supplies,
+// so the loads are kept without a stream of atomics to one address.  The first
+// wave also records the shader clock counter (s_memtime) and the 100 MHz
+// constant clock (s_memrealtime) at its start and end.
 __global__ __launch_bounds__(1024) void k_read_probe(const uint4* __restrict__ p, size_t n16, uint32_t* sink,
                                                     uint64_t* clocks) {
   uint64_t t0 = 0, r0 = 0;
@@ -118,20 +121,37 @@ __global__ __launch_bounds__(1024) void k_read_probe(const uint4* __restrict__ p
     t0 = __builtin_amdgcn_s_memtime();
     r0 = __builtin_amdgcn_s_memrealtime();
   }
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int NWV = 16;
+  const size_t nch = n16 / 256;  // whole 4-KiB chunks
+  const size_t per = (nch + gridDim.x - 1) / gridDim.x;
+  const size_t c_beg = (size_t)blockIdx.x * per;
+  const size_t c_end = c_beg + per < nch ? c_beg + per : nch;
   uint32_t x = 0;
-  for (; i + 7 * stride < n16; i += 8 * stride) {
-    uint4 v[8];
+  const v4i* pv = reinterpret_cast<const v4i*>(p);
+  auto ld = [&](size_t c, v4i (&v)[4]) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = p[i + u * stride];
+    for (int q = 0; q < 4; ++q)
+      v[q] = c < c_end ? __builtin_nontemporal_load(pv + c * 256 + q * 64 + lane) : v4i{0, 0, 0, 0};
+  };
+  v4i a[4], b[4];
+  size_t c = c_beg + wave;
+  ld(c, a);
+  ld(c + NWV, b);
+  for (; c < c_end; c += 2 * NWV) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    for (int q = 0; q < 4; ++q) x ^= (uint32_t)(a[q].x ^ a[q].y ^ a[q].z ^ a[q].w);
+    ld(c + 2 * NWV, a);
+    if (c + NWV >= c_end) break;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x ^= (uint32_t)(b[q].x ^ b[q].y ^ b[q].z ^ b[q].w);
+    ld(c + 3 * NWV, b);
   }
-  for (; i < n16; i += stride) {
-    const uint4 a = p[i];
-    x ^= a.x ^ a.y ^ a.z ^ a.w;
-  }
+  if (blockIdx.x == 0)
+    for (size_t i = nch * 256 + threadIdx.x; i < n16; i += blockDim.x) {
+      const uint4 t = p[i];
+      x ^= t.x ^ t.y ^ t.z ^ t.w;
+    }
   if (x == 0x9E3779B9u) sink[0] = x;
   if (blockIdx.x == 0 && threadIdx.x == 0 && clocks) {
     clocks[0] = __builtin_amdgcn_s_memtime() - t0;
@@ -275,8 +295,7 @@ isa_status isa_read_probe(const void* buf, size_t bytes, uint32_t* sink, uint64_
   if (!buf || !sink || !aligned16(buf) || ((uintptr_t)sink & 3) || ((uintptr_t)clocks & 7) || bytes == 0 ||
       (bytes & 15))
     return ISA_ERR_INVALID_ARG;
-  // one 1024-thread workgroup per CU: of the shapes tried, the fastest for a
-  // plain read (more, smaller workgroups reach less)
+  // one 1024-thread workgroup per CU
   const unsigned grid = (unsigned)device_info().n_cu;
   hipLaunchKernelGGL(k_read_probe, dim3(grid), dim3(1024), 0, (hipStream_t)stream, (const uint4*)buf, bytes / 16, sink,
                      clocks);

@@ -67,6 +67,9 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
   __shared__ uint32_t scr[SCR_WORDS];
   __shared__ int32_t pages[TILE_G / PAGE_GRP];
   __shared__ uint32_t chunk_ctr;
+  // per wave, one 32-group chunk on its way from the load layout to the MFMA
+  // layout: piece j (16 B) of row r at 16 (8r + (j ^ ((r >> 1) & 7)))
+  __shared__ __attribute__((aligned(16))) v4i stage[DEC_THREADS / 64][32 * 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile = blockIdx.x;
@@ -120,27 +123,44 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
   // ---- stream the tile: waves take 32-group chunks from an LDS counter ----
   const int nch = tg / 32;  // chunks of the tile (at least 2 per wave)
   constexpr int NW = DEC_THREADS / 64;
-  const int8_t* kbase = P.pooled + (lane >> 5) * 64;
-  // Loads are unconditional (a group past the end, or on a page outside the
-  // pool, reads row 0 and is zeroed by its mask), so the compiler waits for
-  // exactly the chunk it consumes.
+  // A chunk (32 groups, 4 KiB, inside one page) is read as four 1-KiB
+  // stretches, lane l taking 16 B at 16 l of each, with non-temporal loads:
+  // load q brings piece l % 8 of row 8q + l / 8.  Contiguous wave-wide loads
+  // stream faster than the MFMA layout read straight from memory (32 rows per
+  // load).  Loads are unconditional (a chunk past the end, or on a page
+  // outside the pool, reads the pool's first chunk and is zeroed by its mask),
+  // so the compiler waits for exactly the chunk it consumes.
   auto load_chunk = [&](int c, v4i (&kb)[4], int& mask) {
-    const int gl = min(c, nch - 1) * 32 + (lane & 31);
-    const int pg = pages[gl / PAGE_GRP];
-    const bool ok = c < nch && gl < gN && pg >= 0;
-    mask = ok ? -1 : 0;
-    const size_t row = ok ? (size_t)pg * PAGE_GRP + (gl % PAGE_GRP) : 0;
-    const v4i* p = reinterpret_cast<const v4i*>(kbase + row * IDX_DIM);
-    kb[0] = p[0];
-    kb[1] = p[1];
-    kb[2] = p[2];
-    kb[3] = p[3];
+    const int cl = min(c, nch - 1) * 32;
+    const int pg = pages[cl / PAGE_GRP];
+    const int gl = cl + (lane & 31);  // the group this lane holds in the MFMA layout
+    mask = c < nch && gl < gN && pg >= 0 ? -1 : 0;
+    const size_t row0 = c < nch && pg >= 0 ? (size_t)pg * PAGE_GRP + (cl % PAGE_GRP) : 0;
+    const v4i* p = reinterpret_cast<const v4i*>(P.pooled + row0 * IDX_DIM) + lane;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) kb[q] = __builtin_nontemporal_load(p + q * 64);
   };
   bool overflow = false;
   auto compute = [&](int c, v4i (&kb)[4], int mask) {
+    // through the wave's LDS slot into the MFMA layout: lane l takes row l % 32,
+    // pieces 4(l / 32) + q (channels 64(l / 32) + 16q .. +15); the slot's
+    // swizzle keeps both the stores and the loads free of bank conflicts, and
+    // the wave's LDS accesses complete in order, so the slot needs no barrier
+    v4i* st = stage[wave];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 8 * q + (lane >> 3), j = lane & 7;
+      st[8 * r + (j ^ ((r >> 1) & 7))] = kb[q];
+    }
+    v4i kr[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = lane & 31, j = 4 * (lane >> 5) + q;
+      kr[q] = st[8 * r + (j ^ ((r >> 1) & 7))];
+    }
     v16i acc = {0};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[q], kb[q] & mask, acc, 0, 0, 0);
+    for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[q], kr[q] & mask, acc, 0, 0, 0);
     uint32_t s = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s += __umul24((uint32_t)max(acc[i], 0), wv[i]);  // ReLU <= 2,064,512 < 2^24: 24-bit multiply
