@@ -220,7 +220,7 @@ isa_status isa_indexer_topk(const int8_t* q, const int8_t* head_w, const int8_t*
  * stream.  Nothing in the array has to start at zero: a call writes every
  * part of it that it reads.
  */
-#define ISA_NOALLOC_TOPK_BYTES (256u + 384u * (8u + 8192u + 65536u))
+#define ISA_NOALLOC_TOPK_BYTES (256u + 384u * (8u + 8192u + 68096u))
 isa_status isa_indexer_topk_noalloc(const int8_t* q, const int8_t* head_w, const int8_t* pooled, const isa_seqs* s,
                                     int32_t k, int32_t* out_idx, int32_t* out_count, int32_t* scores_out,
                                     int32_t ld_scores, uint32_t* err_word, isa_stream_t stream);

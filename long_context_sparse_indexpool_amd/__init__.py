@@ -38,7 +38,7 @@ EXPORTS = ("isa_workspace_size", "isa_workspace_init", "isa_device_error", "isa_
            "isa_sparse_mla_decode_shared", "isa_indexer_prefill_scores", "isa_append_token", "isa_latent_to_fp8",
            "isa_sparse_mla_decode_fp8", "isa_kda_decode_step", "isa_indexer_topk_noalloc",
            "isa_read_probe")
-NOALLOC_TOPK_BYTES = 256 + 384 * (8 + 8192 + 65536)
+NOALLOC_TOPK_BYTES = 256 + 384 * (8 + 8192 + 68096)
 
 
 class IsaError(RuntimeError):

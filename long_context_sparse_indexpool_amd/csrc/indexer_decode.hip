@@ -53,7 +53,7 @@ struct DecodePtrs {
   const int32_t* bt;
   uint2* tile_meta;     // [ntiles] (candidates, pairs)
   uint32_t* tile_pairs; // [ntiles][PAIR_CAP] (bin << 16 | count), descending bins
-  uint64_t* tile_list;  // [ntiles][TILE_G] (score << 32 | group), descending bins
+  uint64_t* tile_list;  // [ntiles][TILE_CAP] (score << 32 | group), descending bins
   int32_t* out_idx;     // [B][k]
   int32_t* out_count;   // [B]
   int32_t* scores_out;  // [B][ld] or null
@@ -62,10 +62,10 @@ struct DecodePtrs {
 };
 
 __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a, const DecodePtrs P) {
-  __shared__ uint32_t sc[TILE_G];   // tile scores
+  __shared__ uint32_t sc[TILE_CAP];   // tile scores
   __shared__ uint32_t hist[NBINS];  // tile histogram -> emission cursors
   __shared__ uint32_t scr[SCR_WORDS];
-  __shared__ int32_t pages[TILE_G / PAGE_GRP];
+  __shared__ int32_t pages[TILE_CAP / PAGE_GRP];
   __shared__ uint32_t chunk_ctr;
   // per wave, one 32-group chunk on its way from the load layout to the MFMA
   // layout: piece j (16 B) of row r at 16 (8r + (j ^ ((r >> 1) & 7)))
@@ -78,8 +78,16 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
   const int G = (L + GROUP - 1) / GROUP;
   const uint32_t K = (uint32_t)a.k;
   const int tg = a.tile_g;  // groups per tile of this call (2048 .. 8192)
-  const int g0 = (tile - a.tile_start[b]) * tg;
-  const int gN = min(G - g0, tg);
+  // The tiles of a pair (local indices 2i, 2i + 1) that lies wholly inside
+  // the sequence move tile_skew groups from the one on an odd-numbered XCD to
+  // the one on an even-numbered XCD (the grid is one workgroup per tile,
+  // dispatched round-robin over the XCDs, so global tile parity is XCD parity).
+  const int jt = tile - a.tile_start[b];  // tile within the sequence
+  const bool pair_full = ((jt | 1) + 1) * tg <= G;
+  const int sg = pair_full ? (((tile - (jt & 1)) & 1) == 0 ? a.tile_skew : -a.tile_skew) : 0;  // first tile's extra
+  const int g0 = jt * tg + ((jt & 1) ? sg : 0);
+  const int tsz = (jt & 1) ? tg - sg : tg + sg;  // groups of this tile (fewer where the sequence ends)
+  const int gN = min(G - g0, tsz);
   const bool dense = G <= (int)K;
 
   if (dense && P.scores_out == nullptr) {  // at most k groups: select them all
@@ -90,9 +98,9 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
 
   for (int i = tid; i < NBINS; i += DEC_THREADS) hist[i] = 0;
   if (tid == 0) chunk_ctr = 2 * (DEC_THREADS / 64);
-  if (tid < tg / PAGE_GRP) {
-    int j = (g0 / PAGE_GRP) + tid;
-    pages[tid] = (tid * PAGE_GRP < gN) ? phys_page(P.bt, a.max_pages, a.num_pages, b, j, P.err) : -1;
+  if (tid < tsz / PAGE_GRP) {
+    const int jp = (g0 / PAGE_GRP) + tid;
+    pages[tid] = (tid * PAGE_GRP < gN) ? phys_page(P.bt, a.max_pages, a.num_pages, b, jp, P.err) : -1;
   }
 
   // Query as the MFMA A operand: lane -> head lane%32, channels (lane/32)*64 + 16c .. +15.
@@ -121,7 +129,7 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
   __syncthreads();
 
   // ---- stream the tile: waves take 32-group chunks from an LDS counter ----
-  const int nch = tg / 32;  // chunks of the tile (at least 2 per wave)
+  const int nch = tsz / 32;  // chunks of the tile (at least 2 per wave)
   constexpr int NW = DEC_THREADS / 64;
   // A chunk (32 groups, 4 KiB, inside one page) is read as four 1-KiB
   // stretches, lane l taking 16 B at 16 l of each, with non-temporal loads:
@@ -223,9 +231,9 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
   // gives, for every bin, the candidates and the nonzero bins above it; the
   // kept bins (>= the boundary) are a prefix of that order, so these are also
   // their emission offsets and (bin, count) pair positions.
-  constexpr int PER = TILE_G / DEC_THREADS;  // scores per thread of the largest tile
+  constexpr int PER = (TILE_CAP + DEC_THREADS - 1) / DEC_THREADS;  // scores per thread of the largest tile
   static_assert(NBINS == 2 * DEC_THREADS, "two bins per thread");
-  static_assert(TILE_G < 65536 && NBINS < 65536, "counts and nonzero bins share one word");
+  static_assert(TILE_CAP < 65536 && NBINS < 65536, "counts and nonzero bins share one word");
   const int hb = NBINS - 2 * tid;
   const uint32_t c_hi = hist[hb - 1], c_lo = hist[hb - 2];
   const uint32_t local = c_hi + c_lo, nzl = (c_hi != 0u) + (c_lo != 0u);
@@ -267,11 +275,11 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
   }
   if (tid == 0) P.tile_meta[tile] = make_uint2(scr[SCR_RES + 1], scr[SCR_RES + 2]);
   lds_barrier();
-  uint64_t* list = P.tile_list + (size_t)tile * TILE_G;
+  uint64_t* list = P.tile_list + (size_t)tile * TILE_CAP;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     int e = tid + j * DEC_THREADS;
-    if (e >= tg) break;  // uniform
+    if (e >= tsz) break;  // uniform
     uint32_t s = sc[e];
     if (s == INVALID_SCORE) continue;
     int bin = score_bin(s);
@@ -365,7 +373,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
     const int u = tid + k * SEL_THREADS;
     if (u < nt * hu_per_tile) {
       const int j = u / hu_per_tile, part = u % hu_per_tile;
-      hv[k] = *reinterpret_cast<const uint4*>(P.tile_list + (size_t)(t0 + j) * TILE_G + part * 2);
+      hv[k] = *reinterpret_cast<const uint4*>(P.tile_list + (size_t)(t0 + j) * TILE_CAP + part * 2);
     }
   }
   uint32_t my_np = 0;
@@ -521,11 +529,11 @@ __global__ __launch_bounds__(SEL_THREADS) void k_indexer_select(const BatchArgs 
   const uint32_t nbnd = bnd_off[nt];
   // the sequence's candidate lists as a buffer resource: a global load the
   // compiler cannot merge with the LDS read into one flat access
-  const auto lists = __builtin_amdgcn_make_buffer_rsrc(P.tile_list + (size_t)t0 * TILE_G, 0,
-                                                       nt * TILE_G * 8, 0x00020000);
+  const auto lists = __builtin_amdgcn_make_buffer_rsrc(P.tile_list + (size_t)t0 * TILE_CAP, 0,
+                                                       nt * TILE_CAP * 8, 0x00020000);
   auto entry = [&](int j, uint32_t e) -> uint64_t {  // e-th candidate of tile j
     if (e < (uint32_t)lh) return lhead[j * lh + e];
-    const v2u w = __builtin_amdgcn_raw_buffer_load_b64(lists, (j * TILE_G + (int)e) * 8, 0, 0);
+    const v2u w = __builtin_amdgcn_raw_buffer_load_b64(lists, (j * TILE_CAP + (int)e) * 8, 0, 0);
     return ((uint64_t)w.y << 32) | w.x;
   };
   const bool in_lds = nbnd <= SEL_CAND;

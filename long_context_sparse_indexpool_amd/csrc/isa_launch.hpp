@@ -18,7 +18,9 @@ struct DevInfo {
 };
 DevInfo device_info();
 
-constexpr int TILE_G = 8192;      // pooled groups of the largest decode work tile (128 pages); list stride
+constexpr int TILE_G = 8192;      // pooled groups of the largest decode work tile (128 pages)
+constexpr int TILE_SKEW_MAX = 320;  // groups a tile of a pair may take over from its partner (5 pages)
+constexpr int TILE_CAP = TILE_G + TILE_SKEW_MAX;  // candidates one tile can emit: the list stride
 constexpr int TILE_G_MIN = 2048;  // smallest tile, for batches that would not fill the chip
 constexpr int TILE_MAX_PER_SEQ = (ISA_MAX_SEQ_LEN / GROUP + TILE_G - 1) / TILE_G;
 
@@ -29,7 +31,7 @@ struct DecodeWs {
   uint32_t* err;
   uint2* tile_meta;      // [ntiles] (candidates kept, pairs)
   uint32_t* tile_pairs;  // [ntiles][PAIR_CAP]
-  uint64_t* tile_list;   // [ntiles][TILE_G]
+  uint64_t* tile_list;   // [ntiles][TILE_CAP]
 };
 
 isa_status launch_indexer_decode(const BatchArgs& a, const int8_t* q, const int8_t* hw, const int8_t* pooled,
