@@ -205,14 +205,20 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
   }
   // query operand (B = Q^T), fetched in the same round as the group ids:
   // lane -> head 16hb + lq, channels 128cg + 32c + 8lg .. +7 (bf16 bits; the
-  // FP8 path converts it to fp16 once the token table is built)
-  v4i qraw[HB][KSTEPS];
+  // FP8 path converts it to fp16 once the token table is built).  The two
+  // waves of a channel group (token halves th = 0, 1) need the same operand:
+  // each loads the head blocks of its half, 16th .. (HB/2 blocks), and takes
+  // the other half from its partner through LDS, so that every query byte is
+  // read from memory once per workgroup.
+  static_assert(HB % 2 == 0, "head blocks split between the two token halves");
+  constexpr int QH = HB / 2;
+  v4i qmine[QH][KSTEPS];
   {
-    const uint16_t* qp = q + ((size_t)r * ATT_HEADS + h0 + lq) * LAT_DIM + cg * CG_DIM + lg * 8;
+    const uint16_t* qp = q + ((size_t)r * ATT_HEADS + h0 + 16 * QH * th + lq) * LAT_DIM + cg * CG_DIM + lg * 8;
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
+    for (int hh = 0; hh < QH; ++hh)
 #pragma unroll
-      for (int c = 0; c < KSTEPS; ++c) qraw[hb][c] = *reinterpret_cast<const v4i*>(qp + (size_t)hb * 16 * LAT_DIM + c * 32);
+      for (int c = 0; c < KSTEPS; ++c) qmine[hh][c] = *reinterpret_cast<const v4i*>(qp + (size_t)hh * 16 * LAT_DIM + c * 32);
   }
   // the row's block-table entries, fetched in the same round as the group ids
   // (one dependent global round trip less before the first latent load)
@@ -261,7 +267,24 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
   if (tid < 8) flag_s[tid] = 0u;  // waves without softmax heads never set theirs
   if (tid == 0) big_s = 0u;
   if (tid < 2) vflag_s[tid] = 0u;
-  lds_barrier();  // token table complete
+  // this wave's half of the query operand to LDS (the V tiles, free until the
+  // first tile): wave w's entries at 1 KiB (QH KSTEPS w + entry), 16 B per lane
+  v4i* qx = reinterpret_cast<v4i*>(&vt[0][0]);
+  static_assert(MLA_THREADS / 64 * QH * KSTEPS * 1024 <= (int)sizeof(vt), "query exchange fits in the V tiles");
+#pragma unroll
+  for (int hh = 0; hh < QH; ++hh)
+#pragma unroll
+    for (int c = 0; c < KSTEPS; ++c) qx[((wave * QH + hh) * KSTEPS + c) * 64 + lane] = qmine[hh][c];
+  lds_barrier();  // token table complete, query halves published
+  v4i qother[QH][KSTEPS];
+  {
+    const int pw = wave ^ 4;  // the partner: same channel group, other token half
+#pragma unroll
+    for (int hh = 0; hh < QH; ++hh)
+#pragma unroll
+      for (int c = 0; c < KSTEPS; ++c) qother[hh][c] = qx[((pw * QH + hh) * KSTEPS + c) * 64 + lane];
+  }
+  lds_barrier();  // every wave has its operand: the V tiles are free again
 
   const int nslot = ng * GROUP;
   const int ntile = (nslot + TILE_TOK - 1) / TILE_TOK;
@@ -270,7 +293,8 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
   for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
     for (int c = 0; c < KSTEPS; ++c) {
-      const v4i w = qraw[hb][c];
+      // head block hb: this wave's own load when it lies in its half
+      const v4i w = (hb < QH) == (th == 0) ? qmine[hb % QH][c] : qother[hb % QH][c];
       if constexpr (FP8)
         qop[hb][c] = __builtin_bit_cast(v8h, v4i{(int)bf16x2_to_f16x2((uint32_t)w[0]), (int)bf16x2_to_f16x2((uint32_t)w[1]),
                                                  (int)bf16x2_to_f16x2((uint32_t)w[2]), (int)bf16x2_to_f16x2((uint32_t)w[3])});
