@@ -38,16 +38,18 @@ constexpr int PF_GT = 4096;                   // groups per workgroup
 constexpr int PF_NS = 4;                      // key blocks staged in LDS (ring slots)
 constexpr int PF_KB = 32 * IDX_DIM;           // bytes of one key block (32 groups)
 
-// 16 bytes per lane from global memory straight into LDS (lane l's bytes at
-// lds + 16 l; lds is uniform).  Written out rather than through the builtin:
+// 16 bytes per lane from global memory straight into LDS: lane l reads
+// base + voff (base uniform, in scalar registers) and its bytes land at
+// lds + 16 l (lds uniform).  Written out rather than through the builtin:
 // the compiler would otherwise guard every later LDS read with a wait for all
 // outstanding loads, since it cannot tell ring slots apart.  The instruction
 // has no register result; completion is tracked by vmcnt (waited for
 // explicitly by the caller).  One wait state separates the M0 write from the
 // load that reads it; M0 is declared clobbered, so the compiler keeps nothing
 // of its own there across the statement.
-__device__ __forceinline__ void load_to_lds16(const int8_t* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+__device__ __forceinline__ void load_to_lds16(const int8_t* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(N), no wait on the other counters
@@ -65,6 +67,12 @@ __device__ __forceinline__ uint32_t mad_u24(uint32_t a, uint32_t b, uint32_t c) 
   return d;
 }
 
+// compile-time flag passed to the generic lambdas below
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
+
 struct PrefillPtrs {
   const int8_t* q;
   const int8_t* hw;
@@ -80,8 +88,13 @@ struct PrefillPtrs {
   uint32_t* err;
 };
 
-__global__ __launch_bounds__(PF_THREADS) void k_prefill_scores(const BatchArgs a, const PrefillPtrs P) {
-  __shared__ int32_t pages[PF_GT / PAGE_GRP];
+// Two waves per SIMD (two workgroups per CU) is also what the register budget
+// allows; stating it caps a wave at 256 registers, and under that cap the
+// compiler keeps the MFMA accumulators in ordinary VGPRs, where the epilogue
+// reads them directly (with room for 512 it places them in the accumulation
+// registers and copies each element out with an extra VALU move, a quarter of
+// the epilogue's instructions).
+__global__ __launch_bounds__(PF_THREADS, 2) void k_prefill_scores(const BatchArgs a, const PrefillPtrs P) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: query indices and bases stay scalar
   const int xcd = blockIdx.x % P.n_xcd;
@@ -93,10 +106,11 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_scores(const BatchArgs a
   const int G = (L + GROUP - 1) / GROUP;
   const int g0 = gr * PF_GT;
   const int gN = min(G - g0, PF_GT);
-  if (tid < PF_GT / PAGE_GRP) {
-    pages[tid] = tid * PAGE_GRP < gN ? phys_page(P.bt, a.max_pages, a.num_pages, 0, g0 / PAGE_GRP + tid, P.err)
-                                     : -1;
-  }
+  // the range's pages, one per lane (every wave holds the whole table; a
+  // block's page is then one uniform read of a lane)
+  static_assert(PF_GT / PAGE_GRP == 64 && PAGE_GRP % 32 == 0, "one page per lane; a key block within one page");
+  const int pg_lane =
+      lane * PAGE_GRP < gN ? phys_page(P.bt, a.max_pages, a.num_pages, 0, g0 / PAGE_GRP + lane, P.err) : -1;
 
   // this wave's queries: operands, head weights of the accumulator rows, visible range
   v4i qa[PF_QW][4];
@@ -134,18 +148,18 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_scores(const BatchArgs a
   // PF_NS LDS slots by direct-to-LDS loads: wave w fetches K step w of a block
   // (lane l: group l%32, channels 64(l/32) + 16w .. +15), which lands at slot
   // + 1024w + 16l, so every wave's operand read of K step c is one contiguous
-  // KiB.  Loads are unconditional (a group past the range, or on a page
-  // outside the pool, reads row 0); such a group needs no mask: past the range
-  // its score falls outside the row's buffer range and is dropped, and a page
-  // outside the pool has already been reported as an error.
+  // KiB.  A block lies within one page, so its address is a uniform base plus
+  // a fixed per-lane offset.  Loads are unconditional: groups past the range
+  // read the rest of their page (a block past the last page, or a page outside
+  // the pool, reads page 0) -- all inside the pool; their scores are masked
+  // out of the overflow check and fall outside the row's buffer range, and a
+  // page outside the pool has already been reported as an error.
   __shared__ __attribute__((aligned(16))) int8_t ring[PF_NS][PF_KB];
+  const uint32_t key_off = (lane & 31) * IDX_DIM + (lane >> 5) * 64 + wave * 16;
   auto issue = [&](int blk) {
-    const int gi = blk * 32 + (lane & 31);
-    const int gl = min(gi, PF_GT - 1);
-    const int pg = pages[gl / PAGE_GRP];
-    const bool ok = gi < gN && pg >= 0;
-    const size_t row = ok ? (size_t)pg * PAGE_GRP + gl % PAGE_GRP : 0;
-    load_to_lds16(P.pooled + row * IDX_DIM + (lane >> 5) * 64 + wave * 16,
+    const int pg = __builtin_amdgcn_readlane(pg_lane, min(blk, PF_GT / 32 - 1) >> 1);
+    const size_t row0 = pg >= 0 ? (size_t)pg * PAGE_GRP + (blk & 1) * 32 : 0;
+    load_to_lds16(P.pooled + row0 * IDX_DIM, key_off,
                   (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int8_t*)&ring[blk % PF_NS][wave * 1024]);
   };
   auto read_blk = [&](int blk, v4i (&k)[4]) {
@@ -167,10 +181,20 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_scores(const BatchArgs a
   // lanes >= 32 its second (the layout of a pair's finished scores)
   int lgp[PF_QW / 2];
 #pragma unroll
-  for (int pr = 0; pr < PF_QW / 2; ++pr)
-    lgp[pr] = min(lane < 32 ? lastg[2 * pr] : lastg[2 * pr + 1], g0 + gN - 1);  // range clamp: see the loop
+  for (int pr = 0; pr < PF_QW / 2; ++pr) {
+    // (both bounds taken as uniform values first: a per-lane choice between
+    // two array elements would otherwise be folded into a dynamic index, which
+    // moves the array out of registers)
+    const int l0 = __builtin_amdgcn_readfirstlane(lastg[2 * pr]), l1 = __builtin_amdgcn_readfirstlane(lastg[2 * pr + 1]);
+    lgp[pr] = min(lane < 32 ? l0 : l1, g0 + gN - 1);  // range clamp: see the loop
+  }
   const uint32_t oob_lo = lane < 32 ? 0u : 0x80000000u;  // beyond every row's range
   const uint32_t oob_hi = lane < 32 ? 0x80000000u : 0u;
+  const uint32_t voff_lo = (lane & 31) * 4 | oob_lo, voff_hi = (lane & 31) * 4 | oob_hi;
+  // leading blocks whose 32 groups are all inside the range and visible to all
+  // four of this wave's queries: they need no mask (uniform)
+  const int minlast = min(min(lastg[0], lastg[1]), min(lastg[2], lastg[3]));
+  const int nfast = max(0, min(gN / 32, (minlast - g0 + 1) / 32));
   uint32_t smax = 0;  // largest visible score of this lane (overflow check after the loop)
   // this lane's share of query qq's score of group l%32 from its 32 x 32
   // accumulator block: the lane holds 16 of the 32 heads, lane l^32 the others
@@ -182,19 +206,28 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_scores(const BatchArgs a
   };
   // scores of the query pair (2pr, 2pr + 1) for the block's 32 groups (gb
   // uniform): one cross-half swap leaves the first query's sums in lanes < 32
-  // and the second's in lanes >= 32, so every lane finishes one score
-  auto finish = [&](uint32_t s0, uint32_t s1, int pr, int gb) {
+  // and the second's in lanes >= 32, so every lane finishes one score.  Both
+  // stores go out from every lane, each half's offset pushed out of the other
+  // row's range (uniform resources, no per-lane branch).  A block without
+  // masking (fast) adds its first group's offset as the uniform scalar
+  // offset; otherwise each lane's full offset is formed, groups past the
+  // query's position are stored as -1, and groups past the sequence fall
+  // outside the row's range and are dropped.
+  auto finish = [&](uint32_t s0, uint32_t s1, int pr, int gb, auto fast) {
     const auto sw = __builtin_amdgcn_permlane32_swap(s0, s1, false, false);
     const uint32_t s = sw[0] + sw[1];
-    const int g = gb + (lane & 31);
-    const bool vis = g <= lgp[pr];
-    smax = max(smax, vis ? s : 0u);
-    const int32_t v = vis ? (int32_t)s : -1;
-    // both stores from every lane, each half's offset pushed out of the other
-    // row's range (uniform resources, no per-lane branch); groups past the
-    // sequence fall outside the row's range as well and are dropped
-    __builtin_amdgcn_raw_buffer_store_b32(v, rows[2 * pr], (g * 4) | oob_lo, 0, 2 /* nontemporal */);
-    __builtin_amdgcn_raw_buffer_store_b32(v, rows[2 * pr + 1], (g * 4) | oob_hi, 0, 2 /* nontemporal */);
+    if constexpr (decltype(fast)::value) {
+      smax = max(smax, s);
+      __builtin_amdgcn_raw_buffer_store_b32((int32_t)s, rows[2 * pr], voff_lo, gb * 4, 2 /* nontemporal */);
+      __builtin_amdgcn_raw_buffer_store_b32((int32_t)s, rows[2 * pr + 1], voff_hi, gb * 4, 2 /* nontemporal */);
+    } else {
+      const int g = gb + (lane & 31);
+      const bool vis = g <= lgp[pr];
+      smax = max(smax, vis ? s : 0u);
+      const int32_t v = vis ? (int32_t)s : -1;
+      __builtin_amdgcn_raw_buffer_store_b32(v, rows[2 * pr], (g * 4) | oob_lo, 0, 2 /* nontemporal */);
+      __builtin_amdgcn_raw_buffer_store_b32(v, rows[2 * pr + 1], (g * 4) | oob_hi, 0, 2 /* nontemporal */);
+    }
   };
   auto mm = [&](const v4i (&k)[4], int qq) {
     v16i acc = {0};
@@ -209,17 +242,20 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_scores(const BatchArgs a
   static_assert(PF_QW == 4, "the pipeline below is written for four queries per wave");
   v16i pend;       // accumulator of the previous block's last query
   uint32_t s2 = 0;  // partial of the previous block's third query
-  auto do_blk = [&](int blk, const v4i (&k)[4], bool first) {
+  // fprev / fcur: whether the previous / this block is a fast one
+  auto do_blk = [&](int blk, const v4i (&k)[4], bool first, auto fprev, auto fcur) {
     const int g = g0 + blk * 32;
     v16i x = mm(k, 0);
-    if (!first) finish(s2, partial(pend, 3), 1, g - 32);
+    if (!first) finish(s2, partial(pend, 3), 1, g - 32, fprev);
     v16i y = mm(k, 1);
     const uint32_t s0 = partial(x, 0);
     x = mm(k, 2);
-    finish(s0, partial(y, 1), 0, g);
+    finish(s0, partial(y, 1), 0, g, fcur);
     pend = mm(k, 3);
     s2 = partial(x, 2);
   };
+  const Flag<true> FAST;
+  const Flag<false> MASKED;
   // Block b: wait for this wave's load of block b, meet the other waves (their
   // quarters of the block are then in LDS, and every wave is done with the
   // slot of block b - 1), refill that slot with block b + PF_NS - 1, compute.
@@ -238,9 +274,11 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_scores(const BatchArgs a
   asm volatile("" ::: "memory");
   issue(PF_NS - 1);
   read_blk(0, kb);
-  do_blk(0, kb, true);
-  int blk = 1;
-  for (; blk < nblk; ++blk) {
+  if (nfast > 0)
+    do_blk(0, kb, true, MASKED, FAST);
+  else
+    do_blk(0, kb, true, MASKED, MASKED);
+  auto next = [&](int blk) {
     if (blk >= PF_NS)
       wait_vmcnt<(PF_NS - 2) + 4 * (PF_NS - 1)>();
     else
@@ -249,9 +287,27 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_scores(const BatchArgs a
     asm volatile("" ::: "memory");
     issue(blk + PF_NS - 1);
     read_blk(blk, kb);
-    do_blk(blk, kb, false);
+  };
+  // the fast blocks lead; one loop per kind, so no path merges inside a loop
+  // (a merge would copy the pending accumulator every block)
+  int blk = 1;
+  for (; blk < nfast; ++blk) {
+    next(blk);
+    do_blk(blk, kb, false, FAST, FAST);
   }
-  finish(s2, partial(pend, 3), 1, g0 + (blk - 1) * 32);
+  if (blk == nfast && blk < nblk) {
+    next(blk);
+    do_blk(blk, kb, false, FAST, MASKED);
+    ++blk;
+  }
+  for (; blk < nblk; ++blk) {
+    next(blk);
+    do_blk(blk, kb, false, MASKED, MASKED);
+  }
+  if (blk - 1 < nfast)
+    finish(s2, partial(pend, 3), 1, g0 + (blk - 1) * 32, FAST);
+  else
+    finish(s2, partial(pend, 3), 1, g0 + (blk - 1) * 32, MASKED);
   if (__any(smax > 0x7FFFFFFFu) && lane == 0) report(P.err, ISA_DERR_SCORE_OVERFLOW);
   // columns past the sequence's last group, up to the row stride, are not
   // candidates: the last group range writes them as -1 for its queries
