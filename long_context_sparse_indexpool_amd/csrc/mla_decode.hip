@@ -24,7 +24,8 @@
 //  * The same registers, converted to fp16 (exact for bf16 values in the fp16
 //    normal range), are stored token-major in LDS as V; the P.V product reads
 //    them back transposed (ds_read_b64_tr_b16).  The partial scores go to LDS
-//    too.
+//    too.  Operands are not masked: an invisible token's score is discarded
+//    by the softmax and its V row is overwritten with zeros.
 //  * Wave w owns the softmax of heads 8w..8w+7: it sums the four channel
 //    groups' partials for its heads over the 32 tokens, keeps the running
 //    reference and sum (base 2; the reference moves only when a head's scores
@@ -36,10 +37,12 @@
 //    p_hi, and once more for p_lo when the tile holds a latent value of at
 //    least PV_LO_MIN in magnitude: fp16 probabilities alone would be off by
 //    2^-11 of the largest value (at most 2^-8 below that bound), the pair keeps
-//    the weighted sum accurate to fp32 accumulation.  With bf16 rows each wave
-//    decides for its own 64 channels, from the V operands it has just read,
-//    with integer maxima that issue beside its MFMAs; with FP8 rows the owner
-//    waves decide from the row scales and raise a flag in LDS.
+//    the weighted sum accurate to fp32 accumulation.  The decision is one
+//    flag per tile in LDS: with bf16 rows the loading waves raise it from the
+//    magnitudes they see while converting (a three-way maximum per word, on
+//    the conversion's fp32 intermediates), before the first barrier, so the
+//    owners also skip p_lo when it is not needed; with FP8 rows the owners
+//    raise it from the row scales.
 // Two workgroup barriers per tile, both LDS-only; V is double-buffered.
 // A launch of at most 128 (row, split) units runs two workgroups per unit,
 // each with 32 of the heads (the same tile loads, half the MFMA and softmax
@@ -83,6 +86,17 @@ constexpr float LN2 = 0.6931471805599453f;
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
   const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u));
   return __builtin_bit_cast(uint32_t, h);
+}
+// The same conversion, also folding both values' magnitudes into mv: one
+// three-way maximum with absolute-value source modifiers on the fp32
+// intermediates.  Written out, since through fmaxf the compiler would first
+// canonicalise each bit-cast operand (one more instruction per value); NaN
+// handling does not matter here (a NaN in a visible row makes the output NaN
+// whatever is decided).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2_mag(uint32_t w, float& mv) {
+  const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xFFFF0000u);
+  asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(mv) : "v"(mv), "v"(lo), "v"(hi));
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
 // LDS row of token slot t of a tile: slots 8..15 and 24..31 swap their halves,
 // so the two 16-lane groups of a transposed read (tokens 8g + 4h + 0..3,
@@ -162,7 +176,7 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
   __shared__ __attribute__((aligned(16))) float alpha_s[NH];
   __shared__ __attribute__((aligned(16))) uint32_t flag_s[8];
   __shared__ uint32_t big_s;  // a partial value reached PART_F16_MAX: the split's partial is held in fp32
-  __shared__ uint32_t vflag_s[2];  // FP8: per V buffer, the tile has a row scale of at least PV_LO_MIN / 448
+  __shared__ uint32_t vflag_s[2];  // per V buffer: the tile needs the p_lo pass (a large value or row scale)
   __shared__ float fin_s[2][NH];
   __shared__ __attribute__((aligned(16))) uint32_t trow[MAX_GPS * GROUP];  // latent row of each token slot, ~0 if not visible
   __shared__ int32_t bt_s[BT_LDS];                        // 4 KiB: the row's block-table entries
@@ -338,25 +352,40 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
     for (int hb = 0; hb < HB; ++hb) acc[hb] = v4f{0.f, 0.f, 0.f, 0.f};
     int nmask;
     const LoadT* nsrc = row_of(t + 2, nmask);
+    // Operands unmasked: an invisible token's score is discarded by the
+    // softmax (its x is -inf whatever the partials hold), and its V row is
+    // overwritten with zeros below, so that P = 0 meets finite values.
+    float mv = 0.f;  // bf16: largest magnitude of this lane's V values
 #pragma unroll
     for (int c = 0; c < KSTEPS; ++c) {
       v4i vh;  // V in fp16, token-major: this lane's 8 channels of token 16th + lq
       if constexpr (FP8) {
-        const v8h kh = fp8x8_to_f16x8(buf[c] & bmask);
+        const v8h kh = fp8x8_to_f16x8(buf[c]);
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb)
           acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, qop[hb][c], acc[hb], 0, 0, 0);
         vh = __builtin_bit_cast(v4i, kh);
       } else {
-        const v4i kv = buf[c] & bmask;
+        const v4i kv = buf[c];
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb)
           acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kv), qop[hb][c], acc[hb], 0, 0, 0);
-        vh = v4i{(int)bf16x2_to_f16x2((uint32_t)kv[0]), (int)bf16x2_to_f16x2((uint32_t)kv[1]),
-                 (int)bf16x2_to_f16x2((uint32_t)kv[2]), (int)bf16x2_to_f16x2((uint32_t)kv[3])};
+        vh = v4i{(int)bf16x2_to_f16x2_mag((uint32_t)kv[0], mv), (int)bf16x2_to_f16x2_mag((uint32_t)kv[1], mv),
+                 (int)bf16x2_to_f16x2_mag((uint32_t)kv[2], mv), (int)bf16x2_to_f16x2_mag((uint32_t)kv[3], mv)};
       }
       *reinterpret_cast<v4i*>(&vtb[vrow(th * 16 + lq) * V_STRIDE + cg * CG_DIM + c * 32 + lg * 8]) = vh;
       buf[c] = nsrc[c * 4];  // refill with tile t + 2
+    }
+    if (!bmask) {  // invisible token (rare: a split's tail or positions past the query)
+      asm volatile("" ::: "memory");  // keep these stores apart from the ones above
+#pragma unroll
+      for (int c = 0; c < KSTEPS; ++c)
+        *reinterpret_cast<v4i*>(&vtb[vrow(th * 16 + lq) * V_STRIDE + cg * CG_DIM + c * 32 + lg * 8]) = v4i{0, 0, 0, 0};
+    }
+    // bf16: a visible value of at least PV_LO_MIN in magnitude anywhere in the
+    // tile turns on the p_lo pass for the whole workgroup
+    if constexpr (!FP8) {
+      if (__any(bmask && mv >= PV_LO_MIN) && lane == 0) vflag_s[vb] = 1u;
     }
     bmask = nmask;
 #pragma unroll
@@ -414,20 +443,20 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
       }
       l_run += ps;
       *reinterpret_cast<v4h*>(&pb[own_h * P_STRIDE + 4 * tq]) = ph;
-      // p_lo: always with bf16 rows (each wave decides in P.V whether it needs
-      // it); with FP8 rows only for a tile with a large row scale, which the
-      // owners flag (the flag of the other V buffer is cleared here: every
-      // wave has finished the tile that used it, and none can reach the next
-      // one before the barrier below)
-      bool lo = true;
+      // p_lo only for a tile that needs it: with bf16 rows the loading waves
+      // have flagged a large value before the barrier above; with FP8 rows the
+      // owners flag a large row scale here.  The flag of the other V buffer is
+      // cleared here: every wave has finished the tile that used it, and none
+      // can reach the next one before the barrier below.
+      bool lo;
       if constexpr (FP8) {
         lo = __any(!(st[0] * 448.f < PV_LO_MIN) || !(st[1] * 448.f < PV_LO_MIN) || !(st[2] * 448.f < PV_LO_MIN) ||
                    !(st[3] * 448.f < PV_LO_MIN));
-        if (lane == 0) {
-          if (lo) vflag_s[vb] = 1u;
-          if (wave == 0) vflag_s[vb ^ 1] = 0u;
-        }
+        if (lane == 0 && lo) vflag_s[vb] = 1u;
+      } else {
+        lo = __builtin_amdgcn_readfirstlane(vflag_s[vb]) != 0u;
       }
+      if (lane == 0 && wave == 0) vflag_s[vb ^ 1] = 0u;
       if (lo) {
         v4h pl;
 #pragma unroll
@@ -466,24 +495,8 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
     auto p_op = [&](const _Float16* buf, int hb) -> v8h {
       return __builtin_bit_cast(v8h, *reinterpret_cast<const v4i*>(&buf[(hb * 16 + lq) * P_STRIDE + lg * 8]));
     };
-    // |v| >= PV_LO_MIN anywhere in this wave's V operands: fp16 magnitudes
-    // (sign cleared) compared as 16-bit integers, packed two per word
-    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-    auto vmag = [&](u16x2 m, const v8h& v) -> u16x2 {
-      const v4i w = __builtin_bit_cast(v4i, v);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, (uint32_t)w[e] & 0x7FFF7FFFu));
-      return m;
-    };
-    auto large = [&](u16x2 m) -> bool {
-      constexpr unsigned short LIM = 0x4800;  // fp16 bits of PV_LO_MIN = 8
-      static_assert(PV_LO_MIN == 8.f, "LIM holds the fp16 bits of PV_LO_MIN");
-      return __builtin_amdgcn_readfirstlane(__any(m.x >= LIM || m.y >= LIM)) != 0;
-    };
-    bool lo = false;
-    if constexpr (FP8) lo = __builtin_amdgcn_readfirstlane(vflag_s[vb]) != 0u;
-    u16x2 mv = {0, 0};
+    // the tile's p_lo flag (same in every lane; stable until the next tile)
+    const bool lo = __builtin_amdgcn_readfirstlane(vflag_s[vb]) != 0u;
     if constexpr (HB <= 2) {
       // all V operands held; p_hi of each head block, then p_lo if needed
       v8h vv[NBLK];
@@ -495,10 +508,8 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
 #pragma unroll
         for (int nb = 0; nb < NBLK; ++nb) {
           o[hb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vv[nb], o[hb][nb], 0, 0, 0);
-          if (!FP8 && hb == 0) mv = vmag(mv, vv[nb]);
         }
       }
-      if (!FP8) lo = large(mv);
       if (lo) {
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
@@ -517,9 +528,7 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
         const v8h vv = v_op(nb);
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) o[hb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pv[hb], vv, o[hb][nb], 0, 0, 0);
-        if (!FP8) mv = vmag(mv, vv);
       }
-      if (!FP8) lo = large(mv);
       if (lo) {
         asm volatile("" ::: "memory");  // V is read again, not held in registers
 #pragma unroll
