@@ -193,8 +193,12 @@ isa_status isa_indexpool(const uint16_t* keys, const float* w4, const isa_seqs* 
  * Device errors (decode mode): ISA_DERR_HEADW_RANGE for a head weight outside
  * [0, 64]; ISA_DERR_SCORE_OVERFLOW for a score above INT32_MAX (scores are
  * accumulated in 32-bit unsigned arithmetic, which holds the largest possible
- * score, 4,228,120,576, so the selection still ranks it exactly; scores_out
- * holds it wrapped to a negative int32); ISA_DERR_PAGE_OOB.
+ * score -- 32 * 64 * 128 * 128 * 127 = 4,261,412,864 for any int8 query and
+ * pooled entries within +-127, the range isa_indexpool and isa_append write
+ * -- so the selection still ranks it exactly; scores_out holds it wrapped to
+ * a negative int32); ISA_DERR_PAGE_OOB.  Pooled entries of -128 (never written
+ * by this library) can, with a query of -128 on every channel, reach 2^32,
+ * which wraps to 0 unreported.
  */
 isa_status isa_indexer_topk(const int8_t* q, const int8_t* head_w, const int8_t* pooled, const isa_seqs* s,
                             const int32_t* scores_in, int32_t rows, int32_t ld_scores, int32_t k,

@@ -171,7 +171,7 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
     for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[q], kr[q] & mask, acc, 0, 0, 0);
     uint32_t s = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s += __umul24((uint32_t)max(acc[i], 0), wv[i]);  // ReLU <= 2,064,512 < 2^24: 24-bit multiply
+    for (int i = 0; i < 16; ++i) s += __umul24((uint32_t)max(acc[i], 0), wv[i]);  // ReLU <= 128 * 127 * 128 < 2^24: 24-bit multiply
     s += __builtin_amdgcn_permlane32_swap(s, s, false, false)[1];  // lanes < 32: + lane l+32
     const int gl = c * 32 + (lane & 31);
     if (lane < 32) {
