@@ -586,7 +586,9 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
     fin_s[0][own_h] = l_tot > 0.f ? m_ref : -INFINITY;
     fin_s[1][own_h] = l_tot;
   }
-  __syncthreads();
+  // LDS-only barriers from here on: the loop leaves the (unused) loads of two
+  // tiles past the end in flight, and a full barrier would wait for them
+  lds_barrier();
   const int d_base = wave * OUT_DIM;
   if (P.splits == 1) {
     float* orow = P.out[layer] + ((size_t)r * ATT_HEADS + h0) * LAT_DIM;
@@ -641,7 +643,7 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           stage[(hb * 16 + 4 * lg + i) * LAT_DIM + d_base + nb * 16 + lq] = (_Float16)o[hb][nb][i];
-    __syncthreads();
+    lds_barrier();
     const bool f32 = big_s != 0u;  // uniform
     char* slot = P.o_part + (part * ATT_HEADS + h0) * (LAT_DIM * 4);  // 2 KiB per head
     if (!f32) {
@@ -670,7 +672,10 @@ __global__ __launch_bounds__(MLA_THREADS) void k_mla_split(const BatchArgs a, co
 
 // Merge the splits of one (row, head): split s weighs l_s 2^(m_s - M) / sum,
 // applied to its normalised partial (128 threads x 4 channels, loads unrolled).
-template <bool MULTI>
+// NS > 0: exactly NS splits, and the partials' fp16 form (the common case) is
+// loaded in the same round as the splits' statistics, saving one dependent
+// round trip; if any partial turns out to be in fp32 it is read again below.
+template <bool MULTI, int NS>
 __global__ __launch_bounds__(128) void k_mla_combine(const MlaPtrs P, int32_t rows) {
   __shared__ float wsh[MAX_SPLITS];
   __shared__ uint32_t fsh[MAX_SPLITS];
@@ -681,6 +686,13 @@ __global__ __launch_bounds__(128) void k_mla_combine(const MlaPtrs P, int32_t ro
   const int S = P.splits;
   const size_t part0 = ((size_t)layer * rows + r) * S;  // (layer, row, split 0)
   const float4* ml = reinterpret_cast<const float4*>(P.ml_part) + (part0 * ATT_HEADS + h);
+  const char* op = P.o_part + (part0 * ATT_HEADS + h) * (LAT_DIM * 4);
+  constexpr size_t SPLIT_STRIDE = (size_t)ATT_HEADS * LAT_DIM * 4;
+  v4h pre[NS > 0 ? NS : 1];
+  if constexpr (NS > 0) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) pre[s] = *reinterpret_cast<const v4h*>(op + s * SPLIT_STRIDE + threadIdx.x * 8);
+  }
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     const float4 v = lane < S ? ml[(size_t)lane * ATT_HEADS] : make_float4(-INFINITY, 0.f, 0.f, 0.f);
@@ -703,10 +715,17 @@ __global__ __launch_bounds__(128) void k_mla_combine(const MlaPtrs P, int32_t ro
     }
   }
   __syncthreads();
-  const char* op = P.o_part + (part0 * ATT_HEADS + h) * (LAT_DIM * 4);
-  constexpr size_t SPLIT_STRIDE = (size_t)ATT_HEADS * LAT_DIM * 4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (stat[2] == 0.f) {  // uniform: every partial in fp16
+  if (NS > 0 && stat[2] == 0.f) {  // uniform: every partial in fp16, already loaded
+#pragma unroll
+    for (int s = 0; s < (NS > 0 ? NS : 1); ++s) {
+      const float f = wsh[s];
+      acc.x = fmaf(f, (float)pre[s][0], acc.x);
+      acc.y = fmaf(f, (float)pre[s][1], acc.y);
+      acc.z = fmaf(f, (float)pre[s][2], acc.z);
+      acc.w = fmaf(f, (float)pre[s][3], acc.w);
+    }
+  } else if (stat[2] == 0.f) {  // uniform: every partial in fp16
 #pragma unroll 8
     for (int s = 0; s < S; ++s) {
       const float f = wsh[s];
@@ -799,10 +818,21 @@ isa_status launch_sparse_mla(const BatchArgs& a, const MlaPlan& p, int32_t n_lay
 #undef ISA_MLA_LAUNCH
   if (e != hipSuccess) return ISA_ERR_HIP;
   if (p.splits > 1) {
-    if (n_layers > 1)
-      hipLaunchKernelGGL(k_mla_combine<true>, dim3(n_layers * p.rows * ATT_HEADS), dim3(128), 0, stream, P, p.rows);
-    else
-      hipLaunchKernelGGL(k_mla_combine<false>, dim3(p.rows * ATT_HEADS), dim3(128), 0, stream, P, p.rows);
+    const dim3 cgrid((unsigned)(n_layers * p.rows * ATT_HEADS)), cblock(128);
+#define ISA_COMBINE(MULTI_)                                                                                  \
+  switch (p.splits) {                                                                                        \
+    case 2: hipLaunchKernelGGL((k_mla_combine<MULTI_, 2>), cgrid, cblock, 0, stream, P, p.rows); break;     \
+    case 4: hipLaunchKernelGGL((k_mla_combine<MULTI_, 4>), cgrid, cblock, 0, stream, P, p.rows); break;     \
+    case 8: hipLaunchKernelGGL((k_mla_combine<MULTI_, 8>), cgrid, cblock, 0, stream, P, p.rows); break;     \
+    case 16: hipLaunchKernelGGL((k_mla_combine<MULTI_, 16>), cgrid, cblock, 0, stream, P, p.rows); break;   \
+    default: hipLaunchKernelGGL((k_mla_combine<MULTI_, 0>), cgrid, cblock, 0, stream, P, p.rows); break;    \
+  }
+    if (n_layers > 1) {
+      ISA_COMBINE(true)
+    } else {
+      ISA_COMBINE(false)
+    }
+#undef ISA_COMBINE
     if (hipGetLastError() != hipSuccess) return ISA_ERR_HIP;
   }
   return ISA_OK;
