@@ -85,6 +85,7 @@ struct PrefillPtrs {
   int32_t n_qb;
   int32_t n_gr;
   int32_t n_xcd;  // XCDs the workgroups are dispatched over, round-robin
+  int32_t wide_ok;  // a wave's four score rows fit one buffer resource (16 ld < 2^31)
   uint32_t* err;
 };
 
@@ -190,11 +191,27 @@ __global__ __launch_bounds__(PF_THREADS, 2) void k_prefill_scores(const BatchArg
   }
   const uint32_t oob_lo = lane < 32 ? 0u : 0x80000000u;  // beyond every row's range
   const uint32_t oob_hi = lane < 32 ? 0x80000000u : 0u;
-  const uint32_t voff_lo = (lane & 31) * 4 | oob_lo, voff_hi = (lane & 31) * 4 | oob_hi;
+  // Fast blocks store through one resource over this wave's four score rows:
+  // after the cross-half swap lane l holds query 2pr + l / 32's score of group
+  // l % 32, so each lane stores exactly one word (no half pushed out of range).
+  // Rows past Q lie beyond the resource's range and are dropped.
+  const int qw0 = qb * PF_QB + wave * PF_QW;
+  const int nrow_w = min(max(P.Q - qw0, 0), PF_QW);
+  // (base and size passed through readfirstlane: the compiler otherwise keeps
+  // this resource in vector registers and wraps every store in a loop over
+  // its distinct values)
+  const uint64_t wbase = (uint64_t)(uintptr_t)(P.scores + (size_t)(nrow_w > 0 ? qw0 : 0) * P.ld);
+  const __amdgpu_buffer_rsrc_t wrows = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(wbase >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)wbase)),
+      0, __builtin_amdgcn_readfirstlane(P.wide_ok ? nrow_w * P.ld * 4 : 0), 0x00020000);
+  uint32_t voff_w[PF_QW / 2];
+#pragma unroll
+  for (int pr = 0; pr < PF_QW / 2; ++pr) voff_w[pr] = ((2 * pr + (lane >> 5)) * (uint32_t)P.ld + (lane & 31)) * 4u;
   // leading blocks whose 32 groups are all inside the range and visible to all
   // four of this wave's queries: they need no mask (uniform)
   const int minlast = min(min(lastg[0], lastg[1]), min(lastg[2], lastg[3]));
-  const int nfast = max(0, min(gN / 32, (minlast - g0 + 1) / 32));
+  const int nfast = P.wide_ok ? max(0, min(gN / 32, (minlast - g0 + 1) / 32)) : 0;
   uint32_t smax = 0;  // largest visible score of this lane (overflow check after the loop)
   // this lane's share of query qq's score of group l%32 from its 32 x 32
   // accumulator block: the lane holds 16 of the 32 heads, lane l^32 the others
@@ -206,20 +223,19 @@ __global__ __launch_bounds__(PF_THREADS, 2) void k_prefill_scores(const BatchArg
   };
   // scores of the query pair (2pr, 2pr + 1) for the block's 32 groups (gb
   // uniform): one cross-half swap leaves the first query's sums in lanes < 32
-  // and the second's in lanes >= 32, so every lane finishes one score.  Both
-  // stores go out from every lane, each half's offset pushed out of the other
-  // row's range (uniform resources, no per-lane branch).  A block without
-  // masking (fast) adds its first group's offset as the uniform scalar
-  // offset; otherwise each lane's full offset is formed, groups past the
-  // query's position are stored as -1, and groups past the sequence fall
-  // outside the row's range and are dropped.
+  // and the second's in lanes >= 32, so every lane finishes one score.  A
+  // block without masking (fast) stores it once through the wave's four-row
+  // resource, its first group's offset added as the uniform scalar offset.
+  // Otherwise both per-row stores go out from every lane, each half's offset
+  // pushed out of the other row's range (uniform resources, no per-lane
+  // branch), groups past the query's position are stored as -1, and groups
+  // past the sequence fall outside the row's range and are dropped.
   auto finish = [&](uint32_t s0, uint32_t s1, int pr, int gb, auto fast) {
     const auto sw = __builtin_amdgcn_permlane32_swap(s0, s1, false, false);
     const uint32_t s = sw[0] + sw[1];
     if constexpr (decltype(fast)::value) {
       smax = max(smax, s);
-      __builtin_amdgcn_raw_buffer_store_b32((int32_t)s, rows[2 * pr], voff_lo, gb * 4, 2 /* nontemporal */);
-      __builtin_amdgcn_raw_buffer_store_b32((int32_t)s, rows[2 * pr + 1], voff_hi, gb * 4, 2 /* nontemporal */);
+      __builtin_amdgcn_raw_buffer_store_b32((int32_t)s, wrows, voff_w[pr], gb * 4, 2 /* nontemporal */);
     } else {
       const int g = gb + (lane & 31);
       const bool vis = g <= lgp[pr];
@@ -262,8 +278,10 @@ __global__ __launch_bounds__(PF_THREADS, 2) void k_prefill_scores(const BatchArg
   // The compiler does not track direct-to-LDS loads, so the waits are explicit:
   // vmcnt counts loads and stores in issue order, and the load of block b is
   // followed by PF_NS - 2 later loads and the score stores of the blocks in
-  // between (two in block 0, four in every later block); a count below the
-  // true one only waits longer.
+  // between.  The counts take the fewest stores a block can issue (one per
+  // finished pair in a fast block: one in block 0, two in every later block;
+  // a masked block issues twice as many); a count below the true one only
+  // waits longer.
   static_assert(PF_NS == 4, "the wait counts below are written for four slots");
   const int nblk = (gN + 31) / 32;
   v4i kb[4];
@@ -279,10 +297,17 @@ __global__ __launch_bounds__(PF_THREADS, 2) void k_prefill_scores(const BatchArg
   else
     do_blk(0, kb, true, MASKED, MASKED);
   auto next = [&](int blk) {
+    // later loads (PF_NS - 2) + fewest stores of the blocks issued after block
+    // blk's load: blocks 0 .. blk-1 for blk < PF_NS (block 0 one store, the
+    // others two), the PF_NS - 1 blocks before it otherwise
     if (blk >= PF_NS)
-      wait_vmcnt<(PF_NS - 2) + 4 * (PF_NS - 1)>();
+      wait_vmcnt<(PF_NS - 2) + 2 * (PF_NS - 1)>();
+    else if (blk == 1)
+      wait_vmcnt<(PF_NS - 2) + 1>();
+    else if (blk == 2)
+      wait_vmcnt<(PF_NS - 2) + 1 + 2>();
     else
-      wait_vmcnt<PF_NS - 2 + 2>();
+      wait_vmcnt<(PF_NS - 2) + 1 + 2 + 2>();
     lds_barrier();
     asm volatile("" ::: "memory");
     issue(blk + PF_NS - 1);
@@ -326,7 +351,9 @@ isa_status launch_prefill_scores(const BatchArgs& a, const int8_t* q, const int8
                                  int32_t ld, uint32_t* err, hipStream_t stream) {
   const int G = (a.lens[0] + GROUP - 1) / GROUP;
   const int nx = device_info().n_xcd;
-  PrefillPtrs P{q, hw, q_pos, pooled, bt, scores, ld, Q, (Q + PF_QB - 1) / PF_QB, (G + PF_GT - 1) / PF_GT, nx, err};
+  const int wide_ok = (long long)ld * 4 * PF_QW < (1LL << 31) ? 1 : 0;
+  PrefillPtrs P{q,  hw, q_pos, pooled, bt, scores, ld, Q, (Q + PF_QB - 1) / PF_QB, (G + PF_GT - 1) / PF_GT, nx, wide_ok,
+                err};
   const int gr_rounds = (P.n_gr + nx - 1) / nx;
   const long long nwg = (long long)gr_rounds * nx * P.n_qb;
   if (nwg > 0x7FFFFFFF) return ISA_ERR_UNSUPPORTED;
