@@ -53,7 +53,7 @@ void fill_batch(const isa_seqs* s, BatchArgs* a, int32_t k) {
 // pages, 5 of 128 for the largest tiles.  No skew when the XCD count is odd.
 int32_t decode_tile_skew(int32_t tg) {
   if ((device_info().n_xcd & 1) != 0) return 0;
-  return tg * TILE_SKEW_MAX / TILE_G / PAGE_GRP * PAGE_GRP;  // 320, 128, 64 for tiles of 8192, 4096, 2048
+  return tg * TILE_SKEW_MAX / TILE_G / PAGE_GRP * PAGE_GRP;  // 320 for tiles of 8192, 128 at 4096 .. 6528, 64 below
 }
 
 int decode_tiles(int32_t L, int32_t k, int32_t tg) {
@@ -61,23 +61,41 @@ int decode_tiles(int32_t L, int32_t k, int32_t tg) {
   return G <= k ? 1 : (int)((G + tg - 1) / tg);
 }
 
-// Pooled groups per decode scoring tile: the largest of 8192, 4096, 2048 that
-// gives at least one tile per CU, keeping every sequence within the tiles
-// per sequence the selection handles.  The tile count does not depend on k
+// Pooled groups per decode scoring tile.  8192 when that already gives at
+// least one tile per CU.  Otherwise the smallest multiple of PAGE_GRP, at
+// least TILE_G_MIN, whose tiles fit in one round over the CUs: a batch that
+// would make slightly more tiles than CUs runs them all at once, each a little
+// larger, instead of leaving a second round of tiles to a few CUs while the
+// rest wait (halving the tile to reach one tile per CU could double the
+// kernel).  Every sequence stays within the tiles per sequence the selection
+// handles, which 8192 always satisfies.  The tile count does not depend on k
 // (every tile holds more than MAX_K groups), so the workspace query and the
 // call agree.
 int32_t decode_tile_g(const isa_seqs* s) {
   const int N_CU = device_info().n_cu;
-  int32_t tg = TILE_G;
-  for (;;) {
+  auto fits = [&](int32_t tg) {
     int nt = 0;
-    for (int b = 0; b < s->batch; ++b) nt += decode_tiles(s->seq_lens_host[b], MAX_K, tg);
-    if (nt >= N_CU || tg <= TILE_G_MIN) return tg;
-    const int32_t half = tg / 2;
-    for (int b = 0; b < s->batch; ++b)
-      if (decode_tiles(s->seq_lens_host[b], MAX_K, half) > TILE_MAX_PER_SEQ) return tg;
-    tg = half;
+    for (int b = 0; b < s->batch; ++b) {
+      const int t = decode_tiles(s->seq_lens_host[b], MAX_K, tg);
+      if (t > TILE_MAX_PER_SEQ) return false;
+      nt += t;
+    }
+    return nt <= N_CU;
+  };
+  int nt_max = 0;
+  for (int b = 0; b < s->batch; ++b) nt_max += decode_tiles(s->seq_lens_host[b], MAX_K, TILE_G);
+  if (nt_max >= N_CU) return TILE_G;
+  // the tile count only falls as tiles grow: the smallest fitting multiple
+  int32_t lo = TILE_G_MIN / PAGE_GRP, hi = TILE_G / PAGE_GRP;  // in pages; hi fits
+  if (fits(lo * PAGE_GRP)) return TILE_G_MIN;
+  while (hi - lo > 1) {
+    const int32_t mid = (lo + hi) / 2;
+    if (fits(mid * PAGE_GRP))
+      hi = mid;
+    else
+      lo = mid;
   }
+  return hi * PAGE_GRP;
 }
 
 int pool_tiles(int32_t L) { return (int)((groups_of(L) + POOL_TILE_G - 1) / POOL_TILE_G); }

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(DEC_THREADS) void k_indexer_score(const BatchArgs a
   const int L = a.lens[b];
   const int G = (L + GROUP - 1) / GROUP;
   const uint32_t K = (uint32_t)a.k;
-  const int tg = a.tile_g;  // groups per tile of this call (2048 .. 8192)
+  const int tg = a.tile_g;  // groups per tile of this call (a multiple of 64, 2048 .. 8192)
   // The tiles of a pair (local indices 2i, 2i + 1) that lies wholly inside
   // the sequence move tile_skew groups from the one on an odd-numbered XCD to
   // the one on an even-numbered XCD (the grid is one workgroup per tile,

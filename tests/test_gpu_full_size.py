@@ -65,11 +65,12 @@ def _decode_full(wl, share_layers: int = 0):
     H.log(f"{wl.name}: done")
 
 
-def test_decode_tiles_of_4096_groups():
+def test_decode_tiles_between_sizes():
     """A batch that makes fewer scoring tiles than CUs at 8192 groups per tile
-    and enough at 4096 (8 x 600,000 tokens: 152 tiles of 8192, 296 of 4096), so
-    the scoring runs with 4096-group tiles: every score and every selected id
-    bit-exact against the oracle, with and without the score output."""
+    (8 x 600,000 tokens: 152 tiles of 8192, 296 of 4096), so the scoring runs
+    with the smallest tile that fits one round over the CUs (4736 groups, 256
+    tiles, not a power of two): every score and every selected id bit-exact
+    against the oracle, with and without the score output."""
     wl = custom("tile4096", 23, [600000] * 8, paged_random=True)
     B = wl.batch
     db = H.make_batch(wl, with_latent=False)
