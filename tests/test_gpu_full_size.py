@@ -85,6 +85,28 @@ def test_decode_tiles_between_sizes():
         H.check_topk_row(refs[b], TOPK_GROUPS, idx[b], int(cnt[b]))
 
 
+def test_decode_tiles_at_exact_boundaries():
+    """Forty sequences of about six 2560-group tiles each (on 256 CUs the
+    smallest tile that fits one round: 242 tiles), ending exactly on a tile
+    boundary, one group short of it, one group past it (a last tile of a single
+    group) and a little further in, with partial last groups; the full pairs of
+    tiles move groups between their halves.  Every score and every selected id
+    bit-exact against the oracle."""
+    T = 2560
+    groups = [6 * T, 6 * T - 1, 6 * T + 1, 6 * T - 32, 6 * T - 33, 6 * T - 63] + [6 * T - 64 + 2 * i for i in range(34)]
+    lens = [4 * g - (i % 4) for i, g in enumerate(groups)]
+    wl = custom("tile_bounds", 41, lens, paged_random=True)
+    B = wl.batch
+    db = H.make_batch(wl, with_latent=False)
+    H.run_pool(db)
+    idx, cnt, sc, _ = H.run_topk(db, with_scores=True)
+    refs = oracle.map_rows(lambda b: H.oracle_scores_for(db, b), range(B))
+    for b in range(B):
+        G = wl.groups(b)
+        assert np.array_equal(sc[b, :G].astype(np.int64), refs[b]), f"scores of sequence {b} (G = {G})"
+        H.check_topk_row(refs[b], TOPK_GROUPS, idx[b], int(cnt[b]))
+
+
 def _fp8_full(db, idx, cnt, idx_d, cnt_d):
     """FP8 latent cache at full size: the whole pool quantised on the GPU, the
     selected rows' codes and scales bit-exact against the oracle's quantiser, and
